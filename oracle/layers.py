@@ -1,0 +1,234 @@
+"""Weight preparation and reference quantized linears (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+Conventions (readings; the pages define no layouts):
+
+* Linear layers follow the ``nn.Linear`` convention the pages' targets use
+  ("NunchakuLiteQuantizationConfig" section: every target is a linear layer):
+  X [M, K], W [N, K], Y = X W^T + b, Y [M, N].
+* The low-rank branch is two bfloat16 linears in the same convention:
+  ``lora_down`` [r, K] (K -> r) and ``lora_up`` [N, r] (r -> N), so the branch
+  adds (X_hat lora_down^T) lora_up^T.  Rank 32 is the example's ``rank``.
+* bfloat16 tensors are uint16 bit patterns; E4M3 scales are uint8 codes;
+  packed codes are uint8 [rows, K/2] with the low nibble = even column.
+
+SVDQ (the "Supported quantization types" table: 4-bit weights and
+activations "with SVDQ low-rank correction"; the news article's account:
+outliers move into a 16-bit low-rank branch) -- readings, in order:
+
+1. smoothing factor per input channel: lambda_k = sqrt(amax_x[k] / amax_w[k])
+   (1 where that is zero or not finite), stored as bf16 ``smooth``;
+2. the layer divides activations by ``smooth`` and multiplies the weight by it,
+   W_hat[n, k] = W[n, k] * smooth_k, so X_hat W_hat^T = X W^T;
+3. W_hat = U Sigma V^T (fp64 SVD); lora_down = Sigma_r V_r^T, lora_up = U_r,
+   both rounded to bf16;
+4. residual R = W_hat - lora_up lora_down (fp64, from the bf16 factors), cast to
+   fp32 and quantized per row with the activation quantizer of the precision
+   (nvfp4 adds one fp32 tensor scale);
+5. forward: X_hat = fl32(x * fl32(1/smooth)); quantize X_hat per token;
+   Y = sum_g P_g * s_a * s_w * c + (X_hat lora_down^T) lora_up^T + bias,
+   accumulated in fp64, with P_g the integer dot product of the codes in group
+   g (nvfp4 uses doubled E2M1 codes, c = t_w / 4; int4 has c = 1).
+
+AWQ (table row ``awq_w4a16``, int4 weight-only, group 64): y = x W_deq^T + b,
+W_deq = (q - z) * s, fp64 accumulation.
+"""
+
+import numpy as np
+
+from .formats import (F32, bf16_bits, bf16_bits_f64, bf16_to_f32, e4m3_decode,
+                      e2m1_decode, pack_nibbles, nibble_to_int4)
+from .quant import (quantize_int4, quantize_nvfp4_act, quantize_nvfp4_weight,
+                    quantize_awq)
+
+GROUP = {"int4": 64, "nvfp4": 16}
+
+
+# ----------------------------------------------------------------------------
+# weight preparation
+# ----------------------------------------------------------------------------
+def smooth_factors(x_bits, w):
+    """Per-channel smoothing factors sqrt(amax_x / amax_w) as bf16 bits [K]."""
+    x = np.abs(bf16_to_f32(x_bits).astype(np.float64))
+    w = np.abs(np.asarray(w, dtype=np.float64))
+    amax_x = x.max(axis=0)
+    amax_w = w.max(axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lam = np.sqrt(amax_x / amax_w)
+    lam = np.where(np.isfinite(lam) & (lam > 0), lam, 1.0)
+    return bf16_bits_f64(lam)
+
+
+def prepare_svdq_layer(w, smooth_bits, rank, precision, bias_bits=None):
+    """Offline SVDQ preparation of one linear.
+
+    ``w``: float64 [N, K] original weight; ``smooth_bits``: bf16 bits [K].
+    Returns a dict with the library's inputs (packed_w, wscales, wtscale,
+    smooth, lora_down, lora_up, bias) plus the integer codes and the singular
+    values for the oracle's own checks.
+    """
+    if precision not in GROUP:
+        raise ValueError(precision)
+    G = GROUP[precision]
+    w = np.asarray(w, dtype=np.float64)
+    N, K = w.shape
+    smooth = bf16_to_f32(smooth_bits).astype(np.float64)
+    w_hat = w * smooth[None, :]
+    u, sig, vt = np.linalg.svd(w_hat, full_matrices=False)
+    down = sig[:rank, None] * vt[:rank, :]          # [r, K]
+    up = u[:, :rank]                                # [N, r]
+    down_bits = bf16_bits_f64(down).reshape(rank, K)
+    up_bits = bf16_bits_f64(up).reshape(N, rank)
+    low = bf16_to_f32(up_bits).astype(np.float64) @ bf16_to_f32(down_bits).astype(np.float64)
+    resid = w_hat - low
+    r32 = resid.astype(F32)
+    out = dict(precision=precision, group_size=G, rank=rank, N=N, K=K,
+               smooth=np.asarray(smooth_bits, np.uint16), lora_down=down_bits,
+               lora_up=up_bits, sigma=sig, w_hat=w_hat, resid=resid,
+               bias=None if bias_bits is None else np.asarray(bias_bits, np.uint16))
+    if precision == "int4":
+        nib, s, q = quantize_int4(r32, G)
+        out.update(packed_w=pack_nibbles(nib), wscales=bf16_bits(s), wtscale=1.0,
+                   w_codes=nib, w_int=q)
+    else:
+        codes, s8, t = quantize_nvfp4_weight(r32, G)
+        out.update(packed_w=pack_nibbles(codes), wscales=s8, wtscale=t,
+                   w_codes=codes)
+    return out
+
+
+def prepare_awq_layer(w, bias_bits=None, G=64):
+    """AWQ W4A16 preparation: packed uint4 codes, bf16 scales and zero-points."""
+    w32 = np.asarray(w, dtype=np.float64).astype(F32)
+    q, s, z = quantize_awq(w32, G)
+    return dict(packed_w=pack_nibbles(q), wscales=bf16_bits(s), wzeros=bf16_bits(z),
+                q=q, group_size=G, N=w32.shape[0], K=w32.shape[1],
+                bias=None if bias_bits is None else np.asarray(bias_bits, np.uint16))
+
+
+# ----------------------------------------------------------------------------
+# activation side
+# ----------------------------------------------------------------------------
+def smoothed_activations(x_bits, smooth_bits):
+    """X_hat = fl32(x * fl32(1 / smooth)) as float32 [M, K]."""
+    x = bf16_to_f32(x_bits)
+    mu = (F32(1.0) / bf16_to_f32(smooth_bits)).astype(F32)
+    return (x * mu[None, :]).astype(F32)
+
+
+def svdq_quantize_act(x_bits, smooth_bits, lora_down_bits, precision):
+    """Activation quantizer + low-rank down projection.
+
+    Returns dict(codes [M, K] nibbles, packed [M, K/2], scales (bf16 bits
+    [M, K/64] for int4, E4M3 codes [M, K/16] for nvfp4), lora_act float64
+    [M, r], xhat float32 [M, K]).
+    """
+    G = GROUP[precision]
+    xhat = smoothed_activations(x_bits, smooth_bits)
+    if precision == "int4":
+        nib, s, _ = quantize_int4(xhat, G)
+        scales = bf16_bits(s)
+    else:
+        nib, scales = quantize_nvfp4_act(xhat, G)
+    down = bf16_to_f32(lora_down_bits).astype(np.float64)
+    lora_act = xhat.astype(np.float64) @ down.T if down.shape[0] else np.zeros((xhat.shape[0], 0))
+    return dict(codes=nib, packed=pack_nibbles(nib), scales=scales, lora_act=lora_act, xhat=xhat)
+
+
+def _code_values(codes, precision):
+    """Nibble codes -> exact values: int4 integers, or E2M1 values."""
+    if precision == "int4":
+        return nibble_to_int4(codes).astype(np.float64)
+    return e2m1_decode(codes).astype(np.float64)
+
+
+def _scale_values(scales, precision):
+    if precision == "int4":
+        return bf16_to_f32(scales).astype(np.float64)
+    return e4m3_decode(scales).astype(np.float64)
+
+
+def dequant(codes, scales, precision):
+    """Codes [R, K] and group scales [R, K/G] -> exact float64 values."""
+    G = GROUP[precision]
+    v = _code_values(codes, precision)
+    s = _scale_values(scales, precision)
+    R, K = v.shape
+    return (v.reshape(R, K // G, G) * s[..., None]).reshape(R, K)
+
+
+# ----------------------------------------------------------------------------
+# reference forward passes
+# ----------------------------------------------------------------------------
+def svdq_linear_ref(x_bits, layer, act=None):
+    """Reference SVDQ W4A4 forward in fp64: returns Y [M, N] float64."""
+    p = layer["precision"]
+    if act is None:
+        act = svdq_quantize_act(x_bits, layer["smooth"], layer["lora_down"], p)
+    a = dequant(act["codes"], act["scales"], p)
+    w = dequant(layer["w_codes"], layer["wscales"], p)
+    y = (a @ w.T) * float(layer["wtscale"])
+    if layer["rank"]:
+        y = y + act["lora_act"] @ bf16_to_f32(layer["lora_up"]).astype(np.float64).T
+    if layer.get("bias") is not None:
+        y = y + bf16_to_f32(layer["bias"]).astype(np.float64)[None, :]
+    return y
+
+
+def svdq_partials_ref(act_codes, w_codes, precision):
+    """Exact per-group integer dot products P[m, n, g] (int64).
+
+    int4 uses the signed codes; nvfp4 uses doubled E2M1 codes (integers in
+    {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12}).
+    """
+    G = GROUP[precision]
+    if precision == "int4":
+        a = nibble_to_int4(act_codes)
+        w = nibble_to_int4(w_codes)
+    else:
+        a = np.rint(2 * e2m1_decode(act_codes)).astype(np.int64)
+        w = np.rint(2 * e2m1_decode(w_codes)).astype(np.int64)
+    M, K = a.shape
+    N = w.shape[0]
+    return np.einsum("mgk,ngk->mng", a.reshape(M, K // G, G), w.reshape(N, K // G, G))
+
+
+def awq_dequant(layer):
+    G = layer["group_size"]
+    q = layer["q"].astype(np.float64)
+    N, K = q.shape
+    s = bf16_to_f32(layer["wscales"]).astype(np.float64)
+    z = bf16_to_f32(layer["wzeros"]).astype(np.float64)
+    return ((q.reshape(N, K // G, G) - z[..., None]) * s[..., None]).reshape(N, K)
+
+
+def awq_linear_ref(x_bits, layer):
+    """Reference AWQ W4A16 forward in fp64: y = x W_deq^T + bias."""
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    y = x @ awq_dequant(layer).T
+    if layer.get("bias") is not None:
+        y = y + bf16_to_f32(layer["bias"]).astype(np.float64)[None, :]
+    return y
+
+
+# ----------------------------------------------------------------------------
+# error metrics used by the parity tests
+# ----------------------------------------------------------------------------
+def bf16_half_ulp(y):
+    """Half a bfloat16 ulp at |y| (float64), the size of the final rounding."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 2.0 ** -126)))
+    e = np.maximum(e, -126)
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
+def output_errors(y_gpu, y_ref):
+    """(max|err| / RMS(y_ref), max of (|err| - half-ulp) / RMS, mean relative error)."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    err = np.abs(y_gpu - y_ref)
+    rms = np.sqrt(np.mean(y_ref ** 2)) if y_ref.size else 0.0
+    excess = np.max(err - bf16_half_ulp(y_ref)) if y_ref.size else 0.0
+    mre = err.sum() / max(np.abs(y_ref).sum(), 1e-300)
+    return (err.max() / rms if rms else err.max()), (excess / rms if rms else excess), mre

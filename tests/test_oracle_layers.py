@@ -1,0 +1,228 @@
+"""Pins for oracle/layers.py: brute-force integer GEMMs on 8x16x16 inputs,
+Eckart-Young-Mirsky for the low-rank split, exact zero-residual recovery,
+smoothing and reconstruction identities, zero/permutation identities, the AWQ
+reference against a Python loop, and the method's premise (SVDQ beats plain
+W4A4 on outlier-heavy inputs)."""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import formats as F, layers as L
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _ones_smooth(K):
+    return F.bf16_bits(np.ones(K, np.float32))
+
+
+# ------------------------------------------------------------ brute-force GEMM
+def _decode_nibble_int4(b):
+    mag = b & 7
+    return -mag if b & 8 else mag
+
+
+def _decode_nibble_e2m1_doubled(b):
+    mag = [0, 1, 2, 3, 4, 6, 8, 12][b & 7]
+    return -mag if b & 8 else mag
+
+
+def _brute_partials(packed_a, packed_w, G, dec):
+    """Python-int triple loop over bytes of the packed operands."""
+    M, K2 = packed_a.shape
+    N = packed_w.shape[0]
+    K = 2 * K2
+    P = [[[0] * (K // G) for _ in range(N)] for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            for k in range(K):
+                ba = int(packed_a[m, k // 2])
+                bw = int(packed_w[n, k // 2])
+                na = ba & 15 if k % 2 == 0 else ba >> 4
+                nw = bw & 15 if k % 2 == 0 else bw >> 4
+                P[m][n][k // G] += dec(na) * dec(nw)
+    return np.array(P, dtype=np.int64)
+
+
+@pytest.mark.parametrize("precision,K", [("nvfp4", 16), ("int4", 64), ("int4", 128), ("nvfp4", 48)])
+def test_partials_and_output_brute_force(precision, K):
+    M, N = 8, 16
+    rng = np.random.default_rng(K)
+    x = S.to_bf16_bits(rng.standard_normal((M, K)) * 2)
+    w = rng.standard_normal((N, K)) * 0.1
+    b = S.to_bf16_bits(rng.standard_normal(N) * 0.01)
+    lay = L.prepare_svdq_layer(w, _ones_smooth(K), 0, precision, b)
+    act = L.svdq_quantize_act(x, lay["smooth"], lay["lora_down"], precision)
+    G = L.GROUP[precision]
+    dec = _decode_nibble_int4 if precision == "int4" else _decode_nibble_e2m1_doubled
+    Pb = _brute_partials(act["packed"], lay["packed_w"], G, dec)
+    assert np.array_equal(L.svdq_partials_ref(act["codes"], lay["w_codes"], precision), Pb)
+    # output in exact rational arithmetic from the brute-force partials
+    sa = act["scales"]
+    sw = lay["wscales"]
+    sdec = (lambda v: Fraction(float(F.bf16_to_f32(np.uint16(v))))) if precision == "int4" else \
+        (lambda v: Fraction(float(F.e4m3_decode(np.uint8(v)))))
+    c = Fraction(1) if precision == "int4" else Fraction(lay["wtscale"]) / 4
+    y = L.svdq_linear_ref(x, lay)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(float(F.bf16_to_f32(b[n])))
+            for g in range(K // G):
+                acc += int(Pb[m, n, g]) * sdec(sa[m, g]) * sdec(sw[n, g]) * c
+            assert abs(float(acc) - y[m, n]) <= 1e-12 * (1 + abs(float(acc)))
+
+
+def test_awq_reference_brute_force():
+    rng = np.random.default_rng(3)
+    N, K, M = 8, 128, 3
+    w = rng.standard_normal((N, K)) * 0.05
+    lay = L.prepare_awq_layer(w, S.to_bf16_bits(rng.standard_normal(N) * 0.01))
+    x = S.to_bf16_bits(rng.standard_normal((M, K)))
+    y = L.awq_linear_ref(x, lay)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(float(F.bf16_to_f32(lay["bias"][n])))
+            for k in range(K):
+                byte = int(lay["packed_w"][n, k // 2])
+                q = byte & 15 if k % 2 == 0 else byte >> 4
+                s = Fraction(float(F.bf16_to_f32(lay["wscales"][n, k // 64])))
+                z = Fraction(float(F.bf16_to_f32(lay["wzeros"][n, k // 64])))
+                acc += Fraction(float(F.bf16_to_f32(x[m, k]))) * (q - z) * s
+            assert abs(float(acc) - y[m, n]) <= 1e-12 * (1 + abs(float(acc)))
+
+
+# ------------------------------------------------------------ low-rank split
+def _known_spectrum(N, K, sig, rng):
+    u, _ = np.linalg.qr(rng.standard_normal((N, len(sig))))
+    v, _ = np.linalg.qr(rng.standard_normal((K, len(sig))))
+    return (u * sig) @ v.T
+
+
+def test_svd_split_eckart_young():
+    rng = np.random.default_rng(4)
+    N, K, r = 96, 128, 8
+    sig = np.sort(rng.uniform(0.1, 3.0, 40))[::-1]
+    w = _known_spectrum(N, K, sig, rng)
+    lay = L.prepare_svdq_layer(w, _ones_smooth(K), r, "int4")
+    assert np.allclose(lay["sigma"][:40], sig, rtol=1e-10, atol=1e-12)
+    assert np.all(lay["sigma"][40:] < 1e-10)
+    tail = np.sqrt(np.sum(sig[r:] ** 2))
+    head = np.sqrt(np.sum(sig[:r] ** 2))
+    fro = np.linalg.norm(lay["resid"])
+    # the factors are rounded to bf16, which perturbs the split by <= ~2^-8 of the head
+    assert abs(fro - tail) <= 2.0 ** -6 * head
+    assert fro >= tail * (1 - 1e-9)  # no rank-r matrix beats the tail
+    up = F.bf16_to_f32(lay["lora_up"]).astype(np.float64)
+    gram = up.T @ up
+    assert np.allclose(gram, np.eye(r), atol=2.0 ** -6)
+
+
+def test_zero_residual_exact():
+    # W with exactly bf16-representable rank-r factors (scaled permutations):
+    # the split is exact, the residual is 0, all weight codes are 0, and the
+    # output is exactly X_hat lora_down^T lora_up^T + bias.
+    rng = np.random.default_rng(5)
+    N, K, r = 64, 128, 4
+    sig = np.array([8.0, 4.0, 2.0, 1.0])
+    rows = rng.choice(N, r, replace=False)
+    cols = rng.choice(K, r, replace=False)
+    w = np.zeros((N, K))
+    w[rows, cols] = sig
+    x = S.to_bf16_bits(rng.standard_normal((5, K)))
+    for p in ("int4", "nvfp4"):
+        lay = L.prepare_svdq_layer(w, _ones_smooth(K), r, p)
+        assert np.abs(lay["resid"]).max() < 1e-12
+        assert not lay["packed_w"].any()
+        y = L.svdq_linear_ref(x, lay)
+        xf = F.bf16_to_f32(x).astype(np.float64)
+        assert np.allclose(y, xf @ w.T, rtol=0, atol=1e-12)
+
+
+def test_reconstruction_identity():
+    rng = np.random.default_rng(6)
+    N, K = 64, 128
+    w = rng.standard_normal((N, K)) * 0.02
+    sm = S.to_bf16_bits(rng.uniform(0.5, 3, K))
+    lay = L.prepare_svdq_layer(w, sm, 16, "int4")
+    up = F.bf16_to_f32(lay["lora_up"]).astype(np.float64)
+    dn = F.bf16_to_f32(lay["lora_down"]).astype(np.float64)
+    smooth = F.bf16_to_f32(sm).astype(np.float64)
+    assert np.allclose(up @ dn + lay["resid"], w * smooth[None, :], rtol=0, atol=1e-15)
+
+
+def test_smoothing_identity():
+    rng = np.random.default_rng(7)
+    M, N, K = 16, 32, 128
+    x = S.to_bf16_bits(rng.standard_normal((M, K)) * 3)
+    w = rng.standard_normal((N, K)) * 0.02
+    sm = L.smooth_factors(x, w)
+    xf = F.bf16_to_f32(x).astype(np.float64)
+    lam = F.bf16_to_f32(sm).astype(np.float64)
+    # closed form of the calibration, up to the bf16 rounding of lambda
+    ref = np.sqrt(np.abs(xf).max(0) / np.abs(w).max(0))
+    assert np.all(np.abs(lam - ref) <= 2.0 ** -8 * ref)
+    xhat = L.smoothed_activations(x, sm).astype(np.float64)
+    lay = L.prepare_svdq_layer(w, sm, 0, "int4")
+    # (X / lambda)(W lambda)^T = X W^T, up to the fp32 rounding of X_hat
+    assert np.allclose(xhat @ lay["w_hat"].T, xf @ w.T, rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------------ identities
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_zero_weight_and_zero_input(precision):
+    rng = np.random.default_rng(8)
+    M, N, K = 6, 32, 128
+    x = S.to_bf16_bits(rng.standard_normal((M, K)))
+    b = S.to_bf16_bits(rng.standard_normal(N) * 0.01)
+    lay = L.prepare_svdq_layer(np.zeros((N, K)), _ones_smooth(K), 0, precision)
+    assert not L.svdq_linear_ref(x, lay).any()
+    w = rng.standard_normal((N, K)) * 0.02
+    lay = L.prepare_svdq_layer(w, _ones_smooth(K), 16, precision, b)
+    y = L.svdq_linear_ref(np.zeros((M, K), np.uint16), lay)
+    assert np.array_equal(y, np.broadcast_to(F.bf16_to_f32(b).astype(np.float64), (M, N)))
+
+
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_row_permutation_equivariance(precision):
+    rng = np.random.default_rng(9)
+    M, N, K = 12, 32, 128
+    x = S.to_bf16_bits(rng.standard_normal((M, K)) * 2)
+    w = rng.standard_normal((N, K)) * 0.02
+    lay = L.prepare_svdq_layer(w, _ones_smooth(K), 16, precision)
+    perm = rng.permutation(M)
+    a1 = L.svdq_quantize_act(x, lay["smooth"], lay["lora_down"], precision)
+    a2 = L.svdq_quantize_act(x[perm], lay["smooth"], lay["lora_down"], precision)
+    assert np.array_equal(a1["codes"][perm], a2["codes"])
+    assert np.array_equal(a1["scales"][perm], a2["scales"])
+    assert np.array_equal(L.svdq_linear_ref(x, lay)[perm], L.svdq_linear_ref(x[perm], lay))
+
+
+def test_method_premise_svdq_beats_plain_w4a4():
+    # outlier channels + a low-rank spike: smoothing + rank-32 branch must reduce
+    # the error of 4-bit quantization (the news article's account of SVDQuant)
+    c = S.config1(seed=3, M=256, K=512, N=512)
+    xf = F.bf16_to_f32(c["x"]).astype(np.float64)
+    exact = xf @ c["w"].T
+    plain = L.prepare_svdq_layer(c["w"], _ones_smooth(512), 0, "int4")
+    sm = L.smooth_factors(c["x"], c["w"])
+    svdq = L.prepare_svdq_layer(c["w"], sm, 32, "int4")
+    e_plain = np.linalg.norm(L.svdq_linear_ref(c["x"], plain) - exact)
+    e_svdq = np.linalg.norm(L.svdq_linear_ref(c["x"], svdq) - exact)
+    assert e_svdq < 0.6 * e_plain
+
+
+# ------------------------------------------------------------ the pages' table
+def test_group_sizes_match_the_pages_table():
+    tab = json.load(open(os.path.join(GOLDEN, "quantization_types.json")))
+    svdq = {r["precision"]: r["group_size"] for r in tab["rows"] if r["method"] == "svdq_w4a4"}
+    assert svdq == L.GROUP
+    awq = [r for r in tab["rows"] if r["method"] == "awq_w4a16"]
+    assert awq == [{"method": "awq_w4a16", "precision": "int4", "group_size": 64}]
+    ex = json.load(open(os.path.join(GOLDEN, "config_example.json")))
+    assert ex["svdq"]["group_size"] == L.GROUP[ex["svdq"]["precision"]]
+    assert ex["compute_dtype"] == "bfloat16"
