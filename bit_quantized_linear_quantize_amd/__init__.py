@@ -1,0 +1,222 @@
+"""Thin Python binding of the gfx950 SVDQ W4A4 / AWQ W4A16 library.
+
+Argument marshalling only: every step of the quantized linears runs in the HIP
+kernels of ``lib/libsvdq_w4a4.so`` (built by ``build.py``) behind the C ABI of
+``include/svdq_w4a4.h``.  PyTorch provides device memory and the current HIP
+stream.  There is no fallback: if the library is missing or the call fails,
+an exception is raised.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "libsvdq_w4a4.so")
+
+SVDQ_INT4 = 0
+SVDQ_NVFP4 = 1
+PRECISIONS = {"int4": SVDQ_INT4, "nvfp4": SVDQ_NVFP4}
+GROUP_SIZE = {"int4": 64, "nvfp4": 16}
+STATUS = {0: "SVDQ_OK", -1: "SVDQ_EINVAL", -2: "SVDQ_EUNSUPPORTED", -3: "SVDQ_EARCH",
+          -4: "SVDQ_EWORKSPACE", -5: "SVDQ_EDEVICE"}
+
+# entry points declared in include/svdq_w4a4.h
+EXPORTS = ("svdq_w4a4_workspace_bytes", "svdq_w4a4_linear", "awq_w4a16_linear",
+           "svdq_w4a4_quantize_act", "svdq_w4a4_gemm_partials", "svdq_w4a4_check",
+           "awq_w4a16_check", "svdq_last_error")
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+I = ctypes.c_int
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.svdq_w4a4_workspace_bytes.argtypes = [I64, I64, I64, I, I, I]
+        L.svdq_w4a4_workspace_bytes.restype = ctypes.c_size_t
+        L.svdq_w4a4_linear.argtypes = [P, I64, I64, I64, P, P, ctypes.c_float, P, P, P, P, I, I, I,
+                                       P, P, ctypes.c_size_t, P]
+        L.svdq_w4a4_linear.restype = I
+        L.awq_w4a16_linear.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P]
+        L.awq_w4a16_linear.restype = I
+        L.svdq_w4a4_quantize_act.argtypes = [P, I64, I64, P, P, I, I, I, P, P, P, P]
+        L.svdq_w4a4_quantize_act.restype = I
+        L.svdq_w4a4_gemm_partials.argtypes = [P, P, I64, I64, I64, I, I, P, P]
+        L.svdq_w4a4_gemm_partials.restype = I
+        L.svdq_w4a4_check.argtypes = [P, I64, I64, I64, P, P, ctypes.c_float, P, P, P, P, I, I, I,
+                                      P, P, ctypes.c_size_t, ctypes.c_char_p]
+        L.svdq_w4a4_check.restype = I
+        L.awq_w4a16_check.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, ctypes.c_char_p]
+        L.awq_w4a16_check.restype = I
+        L.svdq_last_error.argtypes = []
+        L.svdq_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise SvdqError(rc, lib().svdq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _contig(t, dtype, name):
+    if t is None:
+        return None
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA tensor of dtype {dtype}")
+    return t
+
+
+def workspace_bytes(M, K, N, precision, rank):
+    return lib().svdq_w4a4_workspace_bytes(M, K, N, PRECISIONS[precision], GROUP_SIZE[precision], rank)
+
+
+class SVDQLinear:
+    """Device-resident inputs of one svdq_w4a4 layer (all tensors on the GPU).
+
+    packed_w uint8 [N, K/2]; wscales bf16 [N, K/64] (int4) or uint8 [N, K/16]
+    (nvfp4); smooth bf16 [K]; lora_down bf16 [rank, K]; lora_up bf16 [N, rank];
+    bias bf16 [N] or None; wtscale float (1.0 for int4).
+    """
+
+    def __init__(self, packed_w, wscales, smooth, lora_down, lora_up, bias, precision, wtscale=1.0):
+        self.precision = precision
+        self.N, k2 = packed_w.shape
+        self.K = 2 * k2
+        self.rank = 0 if lora_down is None else lora_down.shape[0]
+        self.packed_w = _contig(packed_w, torch.uint8, "packed_w")
+        sdt = torch.bfloat16 if precision == "int4" else torch.uint8
+        self.wscales = _contig(wscales, sdt, "wscales")
+        self.smooth = _contig(smooth, torch.bfloat16, "smooth")
+        self.lora_down = _contig(lora_down, torch.bfloat16, "lora_down")
+        self.lora_up = _contig(lora_up, torch.bfloat16, "lora_up")
+        self.bias = _contig(bias, torch.bfloat16, "bias")
+        self.wtscale = float(wtscale)
+
+    @classmethod
+    def from_numpy(cls, d, device="cuda"):
+        """From a dict of numpy arrays (bf16 tensors as uint16 bit patterns)."""
+        def bf(a):
+            if a is None:
+                return None
+            return torch.from_numpy(a.view("int16").copy()).view(torch.bfloat16).to(device)
+
+        def u8(a):
+            return torch.from_numpy(a.copy()).to(device)
+
+        p = d["precision"]
+        ws = bf(d["wscales"]) if p == "int4" else u8(d["wscales"])
+        rank = d["rank"]
+        return cls(u8(d["packed_w"]), ws, bf(d["smooth"]),
+                   bf(d["lora_down"]) if rank else None, bf(d["lora_up"]) if rank else None,
+                   bf(d.get("bias")), p, d.get("wtscale", 1.0))
+
+    def workspace_bytes(self, M):
+        return workspace_bytes(M, self.K, self.N, self.precision, self.rank)
+
+    def __call__(self, x, out=None, workspace=None, stream=None):
+        return svdq_w4a4_linear(x, self, out=out, workspace=workspace, stream=stream)
+
+
+def svdq_w4a4_linear(x, layer, out=None, workspace=None, stream=None):
+    """Y = svdq_w4a4(x) for a bf16 [M, K] CUDA tensor; returns bf16 [M, N]."""
+    x = _contig(x, torch.bfloat16, "x")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(layer.workspace_bytes(M), 1), dtype=torch.uint8, device=x.device)
+    _check(lib().svdq_w4a4_linear(
+        _ptr(x), M, K, layer.N, _ptr(layer.packed_w), _ptr(layer.wscales), layer.wtscale,
+        _ptr(layer.smooth), _ptr(layer.lora_down), _ptr(layer.lora_up), _ptr(layer.bias),
+        PRECISIONS[layer.precision], GROUP_SIZE[layer.precision], layer.rank, _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+class AWQLinear:
+    """Device-resident inputs of one awq_w4a16 layer: packed_w uint8 [N, K/2],
+    wscales / wzeros bf16 [N, K/64], bias bf16 [N] or None."""
+
+    def __init__(self, packed_w, wscales, wzeros, bias=None):
+        self.N, k2 = packed_w.shape
+        self.K = 2 * k2
+        self.packed_w = _contig(packed_w, torch.uint8, "packed_w")
+        self.wscales = _contig(wscales, torch.bfloat16, "wscales")
+        self.wzeros = _contig(wzeros, torch.bfloat16, "wzeros")
+        self.bias = _contig(bias, torch.bfloat16, "bias")
+
+    @classmethod
+    def from_numpy(cls, d, device="cuda"):
+        def bf(a):
+            if a is None:
+                return None
+            return torch.from_numpy(a.view("int16").copy()).view(torch.bfloat16).to(device)
+        return cls(torch.from_numpy(d["packed_w"].copy()).to(device), bf(d["wscales"]),
+                   bf(d["wzeros"]), bf(d.get("bias")))
+
+    def __call__(self, x, out=None, stream=None):
+        return awq_w4a16_linear(x, self, out=out, stream=stream)
+
+
+def awq_w4a16_linear(x, layer, out=None, stream=None):
+    x = _contig(x, torch.bfloat16, "x")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=torch.bfloat16, device=x.device)
+    _check(lib().awq_w4a16_linear(
+        _ptr(x), M, K, layer.N, _ptr(layer.packed_w), _ptr(layer.wscales), _ptr(layer.wzeros),
+        _ptr(layer.bias), 64, _ptr(out), _stream(stream)))
+    return out
+
+
+def svdq_w4a4_quantize_act(x, smooth, lora_down, precision, stream=None):
+    """Parity export of kernel 1: returns (codes uint8 [M, K/2], scales, lora_act fp32 [M, rank])."""
+    x = _contig(x, torch.bfloat16, "x")
+    M, K = x.shape
+    rank = 0 if lora_down is None else lora_down.shape[0]
+    G = GROUP_SIZE[precision]
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    sdt = torch.bfloat16 if precision == "int4" else torch.uint8
+    scales = torch.empty((M, K // G), dtype=sdt, device=x.device)
+    lora_act = torch.empty((M, rank), dtype=torch.float32, device=x.device) if rank else None
+    _check(lib().svdq_w4a4_quantize_act(
+        _ptr(x), M, K, _ptr(smooth), _ptr(lora_down), PRECISIONS[precision], G, rank,
+        _ptr(codes), _ptr(scales), _ptr(lora_act), _stream(stream)))
+    return codes, scales, lora_act
+
+
+def svdq_w4a4_gemm_partials(act_codes, w_codes, precision, stream=None):
+    """Parity export of kernel 2's 4-bit product: int32 [M, N, K/G]."""
+    M, k2 = act_codes.shape
+    N = w_codes.shape[0]
+    K = 2 * k2
+    G = GROUP_SIZE[precision]
+    out = torch.empty((M, N, K // G), dtype=torch.int32, device=act_codes.device)
+    _check(lib().svdq_w4a4_gemm_partials(
+        _ptr(act_codes), _ptr(w_codes), M, K, N, PRECISIONS[precision], G, _ptr(out), _stream(stream)))
+    return out

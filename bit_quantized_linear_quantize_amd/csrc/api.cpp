@@ -1,0 +1,288 @@
+// C-ABI host layer: argument validation, workspace carve-up, launches and
+// error reporting for the entry points declared in include/svdq_w4a4.h.
+//
+// Validation rules (the pages: only the (precision, group size) pairs of the
+// "Supported quantization types" table exist; a quantized checkpoint must
+// match its model exactly, "Load a quantized pipeline" note; unsupported GPUs
+// are rejected at load time, news article's hardware section):
+//   (int4, 64) and (nvfp4, 16) only; AWQ group 64      -> SVDQ_EUNSUPPORTED
+//   rank in 0..128, multiple of 16                      -> SVDQ_EUNSUPPORTED
+//   M >= 1, K % 128 == 0, 128 <= K <= 16384, N % 64 == 0 -> SVDQ_EINVAL
+//   null / non-16-byte-aligned pointers, out overlapping an input or the
+//   workspace, wtscale != 1 for int4                      -> SVDQ_EINVAL
+//   workspace too small                                 -> SVDQ_EWORKSPACE
+//   device not gfx950                                   -> SVDQ_EARCH
+// Everything is checked before the first launch, so on error nothing is
+// written.  The library is stateless apart from a per-device architecture
+// cache and a thread-local error message.
+
+#include "../../include/svdq_w4a4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+constexpr int64_t kMaxM = int64_t(1) << 24;
+constexpr int64_t kMaxK = 16384;
+constexpr size_t kAlign = 16;
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+size_t round_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+  if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool arch_is_gfx950(const char* arch) { return arch && std::strncmp(arch, "gfx950", 6) == 0; }
+
+// Lazy, per-device architecture check (first call on a device queries it).
+int check_device_arch() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SVDQ_EDEVICE, std::string("hipGetDevice failed: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(SVDQ_EDEVICE, "device index out of range");
+  int c = cache[dev].load(std::memory_order_acquire);
+  if (c == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(SVDQ_EDEVICE, std::string("hipGetDeviceProperties failed: ") + hipGetErrorString(e));
+    c = arch_is_gfx950(prop.gcnArchName) ? 1 : -1;
+    cache[dev].store(c, std::memory_order_release);
+    if (c < 0) g_last_error = std::string("device architecture is ") + prop.gcnArchName + ", not gfx950";
+  }
+  if (c < 0) return fail(SVDQ_EARCH, "device architecture is not gfx950");
+  return SVDQ_OK;
+}
+
+int check_shape(int64_t M, int64_t K, int64_t N) {
+  if (M < 1 || M > kMaxM) return fail(SVDQ_EINVAL, "M must be in [1, 2^24]");
+  if (K < 128 || K > kMaxK || K % 128) return fail(SVDQ_EINVAL, "K must be a multiple of 128 in [128, 16384]");
+  if (N < 64 || N % 64 || N > (int64_t(1) << 24)) return fail(SVDQ_EINVAL, "N must be a positive multiple of 64");
+  return SVDQ_OK;
+}
+
+int check_svdq_kind(int precision, int group_size, int rank) {
+  if (precision == SVDQ_INT4) {
+    if (group_size != 64) return fail(SVDQ_EUNSUPPORTED, "int4 requires group_size 64");
+  } else if (precision == SVDQ_NVFP4) {
+    if (group_size != 16) return fail(SVDQ_EUNSUPPORTED, "nvfp4 requires group_size 16");
+  } else {
+    return fail(SVDQ_EUNSUPPORTED, "precision must be SVDQ_INT4 or SVDQ_NVFP4");
+  }
+  if (rank < 0 || rank > 128 || rank % 16) return fail(SVDQ_EUNSUPPORTED, "rank must be a multiple of 16 in [0, 128]");
+  return SVDQ_OK;
+}
+
+size_t act_scale_bytes(int64_t M, int64_t K, int precision) {
+  return precision == SVDQ_INT4 ? size_t(M) * size_t(K / 64) * 2 : size_t(M) * size_t(K / 16);
+}
+size_t w_scale_bytes(int64_t N, int64_t K, int precision) {
+  return precision == SVDQ_INT4 ? size_t(N) * size_t(K / 64) * 2 : size_t(N) * size_t(K / 16);
+}
+
+size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
+  return round_up(size_t(M) * size_t(K / 2)) + round_up(act_scale_bytes(M, K, precision)) +
+         round_up(size_t(M) * size_t(rank) * 4);
+}
+
+int validate_svdq(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                  const void* wscales, float wtscale, const void* smooth, const void* lora_down,
+                  const void* lora_up, const void* bias, int precision, int group_size, int rank,
+                  const void* out, const void* workspace, size_t workspace_bytes_given) {
+  int rc = check_svdq_kind(precision, group_size, rank);
+  if (rc) return rc;
+  rc = check_shape(M, K, N);
+  if (rc) return rc;
+  if (!x || !packed_w || !wscales || !smooth || !out || !workspace)
+    return fail(SVDQ_EINVAL, "null pointer argument");
+  if ((rank > 0) != (lora_down != nullptr) || (rank > 0) != (lora_up != nullptr))
+    return fail(SVDQ_EINVAL, "lora_down / lora_up must be non-null exactly when rank > 0");
+  const void* ptrs[] = {x, packed_w, wscales, smooth, lora_down, lora_up, bias, out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  if (precision == SVDQ_INT4 && wtscale != 1.0f) return fail(SVDQ_EINVAL, "wtscale must be 1.0 for int4");
+  if (precision == SVDQ_NVFP4 && !(std::isfinite(wtscale) && wtscale > 0.f))
+    return fail(SVDQ_EINVAL, "wtscale must be finite and positive");
+  const size_t need = workspace_bytes(M, K, precision, rank);
+  const Range o{out, size_t(M) * size_t(N) * 2};
+  const Range ins[] = {{x, size_t(M) * size_t(K) * 2},
+                       {packed_w, size_t(N) * size_t(K / 2)},
+                       {wscales, w_scale_bytes(N, K, precision)},
+                       {smooth, size_t(K) * 2},
+                       {lora_down, size_t(rank) * size_t(K) * 2},
+                       {lora_up, size_t(N) * size_t(rank) * 2},
+                       {bias, size_t(N) * 2},
+                       {workspace, need}};
+  for (const Range& r : ins)
+    if (overlaps(o, r)) return fail(SVDQ_EINVAL, "out overlaps an input or the workspace");
+  if (overlaps(Range{x, size_t(M) * size_t(K) * 2}, Range{workspace, need}))
+    return fail(SVDQ_EINVAL, "workspace overlaps x");
+  if (workspace_bytes_given < need) return fail(SVDQ_EWORKSPACE, "workspace too small");
+  return SVDQ_OK;
+}
+
+int validate_awq(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                 const void* wscales, const void* wzeros, const void* bias, int group_size,
+                 const void* out) {
+  if (group_size != 64) return fail(SVDQ_EUNSUPPORTED, "awq_w4a16 requires group_size 64");
+  int rc = check_shape(M, K, N);
+  if (rc) return rc;
+  if (!x || !packed_w || !wscales || !wzeros || !out) return fail(SVDQ_EINVAL, "null pointer argument");
+  const void* ptrs[] = {x, packed_w, wscales, wzeros, bias, out};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  const Range o{out, size_t(M) * size_t(N) * 2};
+  const Range ins[] = {{x, size_t(M) * size_t(K) * 2},
+                       {packed_w, size_t(N) * size_t(K / 2)},
+                       {wscales, size_t(N) * size_t(K / 64) * 2},
+                       {wzeros, size_t(N) * size_t(K / 64) * 2},
+                       {bias, size_t(N) * 2}};
+  for (const Range& r : ins)
+    if (overlaps(o, r)) return fail(SVDQ_EINVAL, "out overlaps an input");
+  return SVDQ_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SVDQ_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+  return SVDQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* svdq_last_error(void) { return g_last_error.c_str(); }
+
+size_t svdq_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision, int group_size,
+                                 int rank) {
+  const std::string saved = g_last_error;
+  const bool ok = check_svdq_kind(precision, group_size, rank) == SVDQ_OK && check_shape(M, K, N) == SVDQ_OK;
+  g_last_error = saved;
+  return ok ? workspace_bytes(M, K, precision, rank) : 0;
+}
+
+int svdq_w4a4_check(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                    const void* wscales, float wtscale, const void* smooth, const void* lora_down,
+                    const void* lora_up, const void* bias, int precision, int group_size, int rank,
+                    const void* out, const void* workspace, size_t ws_bytes, const char* arch) {
+  g_last_error.clear();
+  int rc = validate_svdq(x, M, K, N, packed_w, wscales, wtscale, smooth, lora_down, lora_up, bias,
+                         precision, group_size, rank, out, workspace, ws_bytes);
+  if (rc) return rc;
+  if (!arch_is_gfx950(arch)) return fail(SVDQ_EARCH, "device architecture is not gfx950");
+  return SVDQ_OK;
+}
+
+int awq_w4a16_check(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                    const void* wscales, const void* wzeros, const void* bias, int group_size,
+                    const void* out, const char* arch) {
+  g_last_error.clear();
+  int rc = validate_awq(x, M, K, N, packed_w, wscales, wzeros, bias, group_size, out);
+  if (rc) return rc;
+  if (!arch_is_gfx950(arch)) return fail(SVDQ_EARCH, "device architecture is not gfx950");
+  return SVDQ_OK;
+}
+
+int svdq_w4a4_linear(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                     const void* wscales, float wtscale, const void* smooth, const void* lora_down,
+                     const void* lora_up, const void* bias, int precision, int group_size, int rank,
+                     void* out, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = validate_svdq(x, M, K, N, packed_w, wscales, wtscale, smooth, lora_down, lora_up, bias,
+                         precision, group_size, rank, out, workspace, ws_bytes);
+  if (rc) return rc;
+  rc = check_device_arch();
+  if (rc) return rc;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* codes = ws;
+  uint8_t* scales = codes + round_up(size_t(M) * size_t(K / 2));
+  float* lora_act = reinterpret_cast<float*>(scales + round_up(act_scale_bytes(M, K, precision)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  svdq::QuantActArgs qa{x, smooth, lora_down, codes, scales, lora_act, M, K, precision, rank};
+  rc = launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
+  if (rc) return rc;
+  svdq::GemmArgs ga{codes, scales, lora_act, packed_w, wscales, lora_up, bias, out, nullptr,
+                    wtscale, M, K, N, precision, rank};
+  return launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up launch");
+}
+
+int awq_w4a16_linear(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                     const void* wscales, const void* wzeros, const void* bias, int group_size,
+                     void* out, void* stream) {
+  g_last_error.clear();
+  int rc = validate_awq(x, M, K, N, packed_w, wscales, wzeros, bias, group_size, out);
+  if (rc) return rc;
+  rc = check_device_arch();
+  if (rc) return rc;
+  svdq::AwqArgs a{x, packed_w, wscales, wzeros, bias, out, M, K, N};
+  return launch_status(svdq::launch_awq_gemv(a, static_cast<hipStream_t>(stream)), "awq_w4a16 launch");
+}
+
+int svdq_w4a4_quantize_act(const void* x, int64_t M, int64_t K, const void* smooth,
+                           const void* lora_down, int precision, int group_size, int rank,
+                           void* codes_out, void* scales_out, float* lora_act_out, void* stream) {
+  g_last_error.clear();
+  int rc = check_svdq_kind(precision, group_size, rank);
+  if (rc) return rc;
+  rc = check_shape(M, K, 64);
+  if (rc) return rc;
+  if (!x || !smooth || !codes_out || !scales_out) return fail(SVDQ_EINVAL, "null pointer argument");
+  if ((rank > 0) != (lora_down != nullptr) || (rank > 0) != (lora_act_out != nullptr))
+    return fail(SVDQ_EINVAL, "lora_down / lora_act_out must be non-null exactly when rank > 0");
+  const void* ptrs[] = {x, smooth, lora_down, codes_out, scales_out, lora_act_out};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  rc = check_device_arch();
+  if (rc) return rc;
+  svdq::QuantActArgs qa{x, smooth, lora_down, codes_out, scales_out, lora_act_out, M, K, precision, rank};
+  return launch_status(svdq::launch_quantize_act(qa, static_cast<hipStream_t>(stream)),
+                       "quantize_act_lora_down launch");
+}
+
+int svdq_w4a4_gemm_partials(const void* act_codes, const void* w_codes, int64_t M, int64_t K,
+                            int64_t N, int precision, int group_size, int32_t* partials_out,
+                            void* stream) {
+  g_last_error.clear();
+  int rc = check_svdq_kind(precision, group_size, 0);
+  if (rc) return rc;
+  rc = check_shape(M, K, N);
+  if (rc) return rc;
+  if (!act_codes || !w_codes || !partials_out) return fail(SVDQ_EINVAL, "null pointer argument");
+  const void* ptrs[] = {act_codes, w_codes, partials_out};
+  for (const void* p : ptrs)
+    if (!aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  rc = check_device_arch();
+  if (rc) return rc;
+  svdq::GemmArgs ga{act_codes, nullptr, nullptr, w_codes, nullptr, nullptr, nullptr, nullptr,
+                    partials_out, 1.0f, M, K, N, precision, 0};
+  return launch_status(svdq::launch_gemm_w4a4(ga, static_cast<hipStream_t>(stream)),
+                       "gemm_w4a4 partials launch");
+}
+
+}  // extern "C"

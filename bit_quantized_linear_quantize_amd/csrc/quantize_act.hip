@@ -1,0 +1,228 @@
+// Kernel 1 of the SVDQ W4A4 linear: smoothing, per-token group quantization
+// of the activations to 4 bits, and the low-rank down projection
+// lora_act = X_hat lora_down^T, fused in one pass over X.
+//
+// Method: Nunchaku Lite pages, "Supported quantization types" table (int4 with
+// group 64, nvfp4 with group 16, each with an SVDQ low-rank correction) and
+// the news article's description of the low-rank branch as a 16-bit path.
+// Numeric readings (the pages name the formats only):
+//   X_hat = fl32(x * fl32(1/smooth));
+//   int4 : s = bf16(fl32(amax/7)), q = rne(fl32(X_hat * fl32(1/s))), |q| <= 7,
+//          sign-magnitude nibble (bit 3 = sign bit of the product);
+//   nvfp4: s8 = E4M3(fl32(amax/6)) (round-nearest-even, saturating),
+//          code = E2M1(fl32(X_hat * fl32(1/dec(s8)))), tensor scale 1;
+//   groups with amax < 2^-100 (or a zero E4M3 scale) get scale 0 and codes 0.
+//
+// Work layout (gfx950, wave64): a workgroup of 8 waves owns 16 token rows and
+// all K; wave w handles the 64-column chunks w, w+8, w+16, ...  Inside a wave,
+// lane (r = lane%16, q = lane/16) holds 16 consecutive columns 64c+16q..+15 of
+// row r.  That is exactly one nvfp4 group per lane, a quarter of an int4 group
+// (amax then needs two cross-lane max steps), and the A-operand slot group q
+// of the 16x16x32 bf16 matrix instruction used for the low-rank product.  X_hat
+// is split into bf16 hi + lo parts so the low-rank product keeps ~16 bits.
+// The per-wave low-rank partials are summed in LDS in a fixed order
+// (deterministic).  Loads of X are 16 bytes per lane, four chunks in flight.
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace svdq {
+
+constexpr int kK1Waves = 8;
+constexpr int kK1Rows = 16;
+
+template <int RB>
+struct K1Prefetch {
+  static constexpr int value = RB <= 2 ? 4 : 2;
+};
+
+template <int PREC, int RB>
+__global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint16_t* __restrict__ smooth,
+    const uint16_t* __restrict__ lora_down, uint8_t* __restrict__ codes,
+    void* __restrict__ scales, float* __restrict__ lora_act) {
+  extern __shared__ float lds[];
+  constexpr int PF = K1Prefetch<RB>::value;
+  constexpr int NB = RB > 0 ? RB : 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // 1 / smooth for every input channel (IEEE division, one per channel).
+  for (int k = tid; k < K; k += 512) lds[k] = __fdiv_rn(1.0f, bf16_bits_to_f32(smooth[k]));
+  __syncthreads();
+
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int row = blockIdx.x * kK1Rows + r;
+  const bool row_ok = row < M;
+  const uint16_t* xr = x + (size_t)(row_ok ? row : M - 1) * K;
+  const int nchunks = K >> 6;
+  const int K2 = K >> 1;
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 xbuf[PF][2];
+  u32x4 lbuf[PF][NB][2];
+
+  auto issue = [&](int slot, int c) {
+    if (c < nchunks) {
+      const int k0 = c * 64 + q * 16;
+      xbuf[slot][0] = *(const u32x4*)(xr + k0);
+      xbuf[slot][1] = *(const u32x4*)(xr + k0 + 8);
+      if constexpr (RB > 0) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          const uint16_t* lr = lora_down + (size_t)(b * 16 + r) * K + k0;
+          lbuf[slot][b][0] = *(const u32x4*)(lr);
+          lbuf[slot][b][1] = *(const u32x4*)(lr + 8);
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int p = 0; p < PF; ++p) issue(p, wave + p * kK1Waves);
+
+  for (int base = wave; base < nchunks; base += PF * kK1Waves) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int c = base + p * kK1Waves;
+      if (c >= nchunks) break;
+      const int k0 = c * 64 + q * 16;
+      // ---- unpack + smooth ------------------------------------------------
+      float xh[16];
+      const f32x4* mu4 = (const f32x4*)(lds + k0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = xbuf[p][h][i];
+          const f32x4 mu = mu4[h * 2 + (i >> 1)];
+          xh[h * 8 + 2 * i] = __fmul_rn(bf16_lo(w), mu[(2 * i) & 3]);
+          xh[h * 8 + 2 * i + 1] = __fmul_rn(bf16_hi(w), mu[(2 * i + 1) & 3]);
+        }
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+
+      // ---- quantize -------------------------------------------------------
+      uint32_t cw0 = 0, cw1 = 0;
+      if constexpr (PREC == kInt4) {
+        amax = wave_max_xor(amax, 16);
+        amax = wave_max_xor(amax, 32);
+        const bool zero = !(amax >= kTiny);
+        const uint32_t sbits = zero ? 0u : f32_to_bf16_bits(__fdiv_rn(amax, 7.0f));
+        const float s = __uint_as_float(sbits << 16);
+        const float inv = zero ? 0.f : __fdiv_rn(1.0f, s);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float t = __fmul_rn(xh[i], inv);
+          const uint32_t mag = (uint32_t)fminf(rintf(fabsf(t)), 7.0f);
+          const uint32_t nib = zero ? 0u : (mag | ((__float_as_uint(t) >> 28) & 8u));
+          if (i < 8) cw0 |= nib << (4 * i);
+          else cw1 |= nib << (4 * (i - 8));
+        }
+        if (row_ok && q == 0) ((uint16_t*)scales)[(size_t)row * (K >> 6) + c] = (uint16_t)sbits;
+      } else {
+        const float sf = __fdiv_rn(amax, 6.0f);
+        const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sf, 448.0f), 0.0f, 0, false) & 0xffu;
+        const float S = __builtin_amdgcn_cvt_f32_fp8((int)s8, 0);
+        const bool zero = !(amax >= kTiny) || S == 0.0f;
+        const float inv = zero ? 0.f : __fdiv_rn(1.0f, S);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float t0 = __fmul_rn(xh[2 * j], inv);
+          const float t1 = __fmul_rn(xh[2 * j + 1], inv);
+          const uint32_t byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t0, t1, 1.0f, 0) & 0xffu;
+          const uint32_t b = zero ? 0u : byte;
+          if (j < 4) cw0 |= b << (8 * j);
+          else cw1 |= b << (8 * (j - 4));
+        }
+        if (row_ok) ((uint8_t*)scales)[(size_t)row * (K >> 4) + 4 * c + q] = (uint8_t)(zero ? 0u : s8);
+      }
+      if (row_ok) *(u32x2*)(codes + (size_t)row * K2 + (k0 >> 1)) = u32x2{cw0, cw1};
+
+      // ---- low-rank down projection (bf16 hi + lo, fp32 accumulate) --------
+      if constexpr (RB > 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          bf16x8 ahi, alo;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float v = xh[8 * j + i];
+            const __bf16 h = (__bf16)v;
+            ahi[i] = h;
+            alo[i] = (__bf16)(v - (float)h);
+          }
+#pragma unroll
+          for (int b = 0; b < RB; ++b) {
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, lbuf[p][b][j]);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bop, acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bop, acc[b], 0, 0, 0);
+          }
+        }
+      }
+      issue(p, c + PF * kK1Waves);
+    }
+  }
+
+  // ---- reduce the low-rank partials of the 8 waves (fixed order) ----------
+  if constexpr (RB > 0) {
+    constexpr int rank = RB * 16;
+    __syncthreads();  // everyone is done with the 1/smooth table
+    float* red = lds;  // [wave][16 rows][rank]
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[(wave * kK1Rows + q * 4 + j) * rank + b * 16 + r] = acc[b][j];
+    __syncthreads();
+    for (int o = tid; o < kK1Rows * rank; o += 512) {
+      const int rr = o / rank;
+      const int cc = o - rr * rank;
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kK1Waves; ++w) s += red[(w * kK1Rows + rr) * rank + cc];
+      const int grow = blockIdx.x * kK1Rows + rr;
+      if (grow < M) lora_act[(size_t)grow * rank + cc] = s;
+    }
+  }
+}
+
+template <int PREC, int RB>
+static hipError_t launch_k1(const QuantActArgs& a, hipStream_t stream) {
+  const int rank = RB * 16;
+  size_t lds = (size_t)a.K * sizeof(float);
+  const size_t red = (size_t)kK1Waves * kK1Rows * rank * sizeof(float);
+  if (red > lds) lds = red;
+  dim3 grid((unsigned)((a.M + kK1Rows - 1) / kK1Rows));
+  hipLaunchKernelGGL((quantize_act_lora_down_kernel<PREC, RB>), grid, dim3(512), lds, stream,
+                     (const uint16_t*)a.x, (int)a.M, (int)a.K, (const uint16_t*)a.smooth,
+                     (const uint16_t*)a.lora_down, (uint8_t*)a.codes, a.scales, a.lora_act);
+  return hipGetLastError();
+}
+
+template <int PREC>
+static hipError_t dispatch_rank(const QuantActArgs& a, hipStream_t s) {
+  switch (a.rank / 16) {
+    case 0: return launch_k1<PREC, 0>(a, s);
+    case 1: return launch_k1<PREC, 1>(a, s);
+    case 2: return launch_k1<PREC, 2>(a, s);
+    case 3: return launch_k1<PREC, 3>(a, s);
+    case 4: return launch_k1<PREC, 4>(a, s);
+    case 5: return launch_k1<PREC, 5>(a, s);
+    case 6: return launch_k1<PREC, 6>(a, s);
+    case 7: return launch_k1<PREC, 7>(a, s);
+    case 8: return launch_k1<PREC, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream) {
+  return a.precision == kInt4 ? dispatch_rank<kInt4>(a, stream) : dispatch_rank<kNvfp4>(a, stream);
+}
+
+}  // namespace svdq

@@ -1,0 +1,148 @@
+/*
+ * svdq_w4a4.h -- C ABI of the gfx950 (MI355X) quantized-linear library.
+ *
+ * Two layer types, as listed in the "Supported quantization types" table of
+ * the Nunchaku Lite pages (Hugging Face Diffusers quantization docs):
+ *
+ *   svdq_w4a4  4-bit weights and 4-bit activations with an SVDQ low-rank
+ *              correction; precision int4 (group 64) or nvfp4 (group 16).
+ *   awq_w4a16  int4 weight-only (AWQ style), group 64, bf16 activations.
+ *
+ * "NunchakuLiteQuantizationConfig" section of the same pages: every floating
+ * point buffer is bfloat16 (compute_dtype), the example uses rank 32, and
+ * every quantized target is a linear layer.  The news article on Nunchaku
+ * Lite describes the low-rank branch as a 16-bit side path that absorbs the
+ * outliers while the rest runs in 4 bits.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Layer convention is nn.Linear: X [M, K], W [N, K], Y = X W^T + b, Y [M, N].
+ * - All tensors are dense, row-major, in device memory, 16-byte aligned.
+ *   bf16 = IEEE bfloat16.  The caller owns every buffer; the library never
+ *   allocates, frees or synchronizes on the hot path.
+ * - Packed 4-bit codes are uint8 [rows, K/2]; the low nibble of byte j holds
+ *   column 2j, the high nibble column 2j+1.
+ *     int4  codes: sign-magnitude, bit 3 = sign, bits 0..2 = |q| in 0..7.
+ *     nvfp4 codes: OCP E2M1 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 = sign).
+ *     AWQ   codes: unsigned 0..15.
+ * - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work on
+ *   it and return without waiting.
+ * - Return value: SVDQ_OK or a negative status.  Validation happens before any
+ *   launch; on error nothing is written and svdq_last_error() describes the
+ *   failure.  The library never aborts the process.
+ */
+#ifndef SVDQ_W4A4_H
+#define SVDQ_W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum svdq_precision { SVDQ_INT4 = 0, SVDQ_NVFP4 = 1 };
+
+enum svdq_status {
+  SVDQ_OK = 0,
+  SVDQ_EINVAL = -1,       /* null/misaligned pointer, bad dimension, aliasing  */
+  SVDQ_EUNSUPPORTED = -2, /* (precision, group_size) or rank not in the table  */
+  SVDQ_EARCH = -3,        /* current device is not gfx950                       */
+  SVDQ_EWORKSPACE = -4,   /* workspace smaller than svdq_w4a4_workspace_bytes  */
+  SVDQ_EDEVICE = -5       /* HIP runtime error (no device, launch failure)     */
+};
+
+/* Bytes of scratch svdq_w4a4_linear needs: activation codes [M, K/2],
+ * activation scales [M, K/G] (bf16 for int4, E4M3 bytes for nvfp4) and the
+ * low-rank activations [M, rank] fp32, each 256-byte aligned.  Returns 0 for
+ * arguments svdq_w4a4_linear would reject. */
+size_t svdq_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision,
+                                 int group_size, int rank);
+
+/* SVDQ W4A4 linear ("Supported quantization types": svdq_w4a4 rows).
+ *
+ *   X_hat = X * (1 / smooth)                       per input channel, fp32
+ *   per token and group: int4  s = bf16(amax / 7),  q = rne(X_hat / s)
+ *                        nvfp4 s = E4M3(amax / 6),  q = E2M1(X_hat / s)
+ *   Y = sum_g (q_x . q_w)_g * s_x * s_w * wtscale
+ *       + (X_hat lora_down^T) lora_up^T + bias     -> bf16
+ *
+ * x         bf16 [M, K]
+ * packed_w  uint8 [N, K/2] weight codes (residual after the low-rank split)
+ * wscales   int4: bf16 [N, K/64]; nvfp4: uint8 E4M3 [N, K/16]
+ * wtscale   nvfp4 fp32 weight tensor scale; must be 1.0f for int4
+ * smooth    bf16 [K], per-channel smoothing divisors (> 0, finite)
+ * lora_down bf16 [rank, K] (the K -> rank linear); NULL iff rank == 0
+ * lora_up   bf16 [N, rank] (the rank -> N linear); NULL iff rank == 0
+ * bias      bf16 [N] or NULL
+ * precision SVDQ_INT4 with group_size 64, or SVDQ_NVFP4 with group_size 16
+ * rank      0..128, multiple of 16
+ * out       bf16 [M, N]; must not overlap x, the weights or the workspace
+ * workspace device scratch of at least svdq_w4a4_workspace_bytes(...) bytes,
+ *           owned by the caller; its contents on entry do not matter
+ * Shapes: M >= 1, K % 128 == 0, 128 <= K <= 16384, N % 64 == 0, N >= 64.
+ */
+int svdq_w4a4_linear(const void* x, int64_t M, int64_t K, int64_t N,
+                     const void* packed_w, const void* wscales, float wtscale,
+                     const void* smooth, const void* lora_down, const void* lora_up,
+                     const void* bias, int precision, int group_size, int rank,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* AWQ W4A16 linear ("Supported quantization types": awq_w4a16, int4, group 64).
+ *
+ *   Y = X ((q - z) * s)^T + bias, fp32 accumulation, bf16 output.
+ *
+ * x        bf16 [M, K]
+ * packed_w uint8 [N, K/2] unsigned codes 0..15
+ * wscales  bf16 [N, K/64]
+ * wzeros   bf16 [N, K/64] zero-points, integer values 0..15
+ * bias     bf16 [N] or NULL
+ * out      bf16 [M, N]; must not overlap x or the weights
+ * Shapes: M >= 1, K % 128 == 0, 128 <= K <= 16384, N % 64 == 0, N >= 64.
+ * group_size must be 64.  Bandwidth-bound for M <= 32 (one weight pass per
+ * 32 rows of X).
+ */
+int awq_w4a16_linear(const void* x, int64_t M, int64_t K, int64_t N,
+                     const void* packed_w, const void* wscales, const void* wzeros,
+                     const void* bias, int group_size, void* out, void* stream);
+
+/* Parity export of the first svdq_w4a4 kernel (same kernel as the linear):
+ * smoothing, activation quantization and the low-rank down projection.
+ * codes_out  uint8 [M, K/2]; scales_out bf16 [M, K/64] (int4) or uint8 E4M3
+ * [M, K/16] (nvfp4); lora_act_out fp32 [M, rank] (may be NULL iff rank == 0).
+ * Arguments as for svdq_w4a4_linear. */
+int svdq_w4a4_quantize_act(const void* x, int64_t M, int64_t K, const void* smooth,
+                           const void* lora_down, int precision, int group_size, int rank,
+                           void* codes_out, void* scales_out, float* lora_act_out,
+                           void* stream);
+
+/* Parity export of the 4-bit product of the second svdq_w4a4 kernel (same
+ * operand unpacking and matrix instructions): exact per-group integer dot
+ * products P[m, n, g] = sum over group g of q_x * q_w, int32 [M, N, K/G].
+ * nvfp4 reports doubled E2M1 codes (integers), i.e. 4 * sum(e2m1_x * e2m1_w).
+ * act_codes uint8 [M, K/2], w_codes uint8 [N, K/2]. */
+int svdq_w4a4_gemm_partials(const void* act_codes, const void* w_codes, int64_t M,
+                            int64_t K, int64_t N, int precision, int group_size,
+                            int32_t* partials_out, void* stream);
+
+/* Host-only argument validation, without touching the GPU: the checks
+ * svdq_w4a4_linear / awq_w4a16_linear perform, with the device architecture
+ * given as a string (for example "gfx950:sramecc+:xnack-").  Returns the
+ * status the call would return before launching. */
+int svdq_w4a4_check(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                    const void* wscales, float wtscale, const void* smooth,
+                    const void* lora_down, const void* lora_up, const void* bias,
+                    int precision, int group_size, int rank, const void* out,
+                    const void* workspace, size_t workspace_bytes, const char* arch);
+int awq_w4a16_check(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                    const void* wscales, const void* wzeros, const void* bias,
+                    int group_size, const void* out, const char* arch);
+
+/* Message for the last failure on the calling thread ("" if none). */
+const char* svdq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_W4A4_H */

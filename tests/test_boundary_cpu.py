@@ -1,0 +1,182 @@
+"""C-ABI boundary on the CPU: the library loads without a GPU, exports every
+entry point of include/svdq_w4a4.h, and its host-side validation returns the
+documented status for every class of bad argument (no device memory is ever
+touched: the pointers below are fake, aligned addresses)."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import bit_quantized_linear_quantize_amd as bq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq_w4a4.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+OK, EINVAL, EUNSUP, EARCH, EWS, EDEV = 0, -1, -2, -3, -4, -5
+GFX950 = b"gfx950:sramecc+:xnack-"
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bq.LIB_PATH):
+        from bit_quantized_linear_quantize_amd import build
+        build.build()
+    return bq.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s+([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported(L):
+    names = header_functions()
+    assert set(names) == set(bq.EXPORTS), names
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def _fake(base):
+    return ctypes.c_void_p(base)
+
+
+class Args:
+    """A valid svdq_w4a4 call (fake, disjoint, aligned pointers)."""
+
+    def __init__(self, M=256, K=512, N=256, precision=0, group=64, rank=32):
+        self.M, self.K, self.N = M, K, N
+        self.precision, self.group, self.rank = precision, group, rank
+        self.x = 0x1000_0000
+        self.w = 0x2000_0000
+        self.ws = 0x3000_0000
+        self.sm = 0x4000_0000
+        self.ld = 0x5000_0000
+        self.lu = 0x6000_0000
+        self.b = 0x7000_0000
+        self.out = 0x8000_0000
+        self.work = 0x9000_0000
+        self.wt = 1.0 if precision == 0 else 0.01
+        self.wsb = None
+
+    def call(self, L, arch=GFX950, **kw):
+        d = dict(vars(self))
+        d.update(kw)
+        wsb = d["wsb"]
+        if wsb is None:
+            wsb = L.svdq_w4a4_workspace_bytes(d["M"], d["K"], d["N"], d["precision"], d["group"], d["rank"])
+        p = lambda v: None if v is None else _fake(v)
+        return L.svdq_w4a4_check(p(d["x"]), d["M"], d["K"], d["N"], p(d["w"]), p(d["ws"]), d["wt"],
+                                 p(d["sm"]), p(d["ld"]), p(d["lu"]), p(d["b"]), d["precision"],
+                                 d["group"], d["rank"], p(d["out"]), p(d["work"]), wsb, arch)
+
+
+def test_valid_calls_pass(L):
+    assert Args().call(L) == OK
+    assert Args(precision=1, group=16).call(L) == OK
+    assert Args(rank=0).call(L, ld=None, lu=None) == OK
+    assert Args().call(L, b=None) == OK
+    assert Args(M=1, K=128, N=64).call(L) == OK
+
+
+def test_only_the_tabled_precision_group_pairs(L):
+    tab = json.load(open(os.path.join(GOLDEN, "quantization_types.json")))
+    legal = {(bq.PRECISIONS[r["precision"]], r["group_size"]) for r in tab["rows"] if r["method"] == "svdq_w4a4"}
+    for prec in (0, 1, 2, -1):
+        for g in (8, 16, 32, 64, 128):
+            rc = Args(precision=prec if prec in (0, 1) else 0, group=g).call(L, precision=prec, group=g,
+                                                                               wt=1.0 if prec != 1 else 0.01)
+            assert (rc == OK) == ((prec, g) in legal), (prec, g, rc)
+            if (prec, g) not in legal:
+                assert rc == EUNSUP
+
+
+def test_rank_bounds(L):
+    for r, want in ((0, OK), (16, OK), (32, OK), (128, OK), (8, EUNSUP), (144, EUNSUP), (-16, EUNSUP)):
+        kw = {} if r else dict(ld=None, lu=None)
+        assert Args(rank=r).call(L, rank=r, **kw) == want, r
+
+
+def test_shape_rules(L):
+    assert Args().call(L, M=0) == EINVAL
+    assert Args().call(L, K=192) == EINVAL
+    assert Args().call(L, K=64) == EINVAL
+    assert Args().call(L, N=96) == EINVAL
+    assert Args().call(L, K=32768) == EINVAL
+
+
+def test_null_and_alignment(L):
+    for f in ("x", "w", "ws", "sm", "out", "work"):
+        assert Args().call(L, **{f: None}) == EINVAL, f
+    assert Args().call(L, ld=None) == EINVAL
+    assert Args(rank=0).call(L, rank=0) == EINVAL  # lora given with rank 0
+    for f in ("x", "w", "ws", "sm", "ld", "lu", "b", "out", "work"):
+        a = Args()
+        assert a.call(L, **{f: getattr(a, f) + 8}) == EINVAL, f
+
+
+def test_aliasing(L):
+    a = Args()
+    assert a.call(L, out=a.x) == EINVAL
+    assert a.call(L, out=a.x + 1024) == EINVAL
+    assert a.call(L, out=a.work) == EINVAL
+    assert a.call(L, out=a.w + 64) == EINVAL
+
+
+def test_wtscale_rules(L):
+    assert Args().call(L, wt=0.5) == EINVAL
+    assert Args(precision=1, group=16).call(L, wt=0.0) == EINVAL
+    assert Args(precision=1, group=16).call(L, wt=float("inf")) == EINVAL
+
+
+def test_workspace_size(L):
+    M, K, N = 300, 512, 320
+    for prec, g, sb in ((0, 64, 2 * 8), (1, 16, 32)):
+        need = L.svdq_w4a4_workspace_bytes(M, K, N, prec, g, 32)
+        rnd = lambda v: (v + 255) // 256 * 256
+        assert need == rnd(M * K // 2) + rnd(M * sb) + rnd(M * 32 * 4)
+        a = Args(M=M, K=K, N=N, precision=prec, group=g)
+        assert a.call(L, wsb=need - 1) == EWS
+        assert a.call(L, wsb=need) == OK
+    assert L.svdq_w4a4_workspace_bytes(M, K, N, 0, 16, 32) == 0
+
+
+def test_arch_rule(L):
+    assert Args().call(L, arch=b"gfx942:sramecc+:xnack-") == EARCH
+    assert Args().call(L, arch=b"gfx1100") == EARCH
+    assert Args().call(L, arch=GFX950) == OK
+
+
+def test_error_message(L):
+    Args().call(L, K=192)
+    assert b"K must be" in L.svdq_last_error()
+    Args().call(L)
+    assert L.svdq_last_error() == b""
+
+
+def test_awq_rules(L):
+    p = _fake
+    def call(M=16, K=3072, N=18432, x=0x1000_0000, w=0x2000_0000, s=0x3000_0000, z=0x4000_0000,
+             b=0x5000_0000, g=64, out=0x8000_0000, arch=GFX950):
+        q = lambda v: None if v is None else p(v)
+        return L.awq_w4a16_check(q(x), M, K, N, q(w), q(s), q(z), q(b), g, q(out), arch)
+    assert call() == OK
+    assert call(b=None) == OK
+    assert call(g=128) == EUNSUP
+    assert call(K=100) == EINVAL
+    assert call(z=None) == EINVAL
+    assert call(out=0x1000_0000 + 64) == EINVAL
+    assert call(arch=b"gfx90a") == EARCH
+    assert call(x=0x1000_0004) == EINVAL
+
+
+def test_linear_rejects_before_touching_the_device(L):
+    # validation runs first: an unsupported pair never reaches the HIP runtime
+    rc = L.svdq_w4a4_linear(_fake(0x1000_0000), 256, 512, 256, _fake(0x2000_0000), _fake(0x3000_0000),
+                            1.0, _fake(0x4000_0000), None, None, None, 0, 32, 0, _fake(0x8000_0000),
+                            _fake(0x9000_0000), 1 << 20, None)
+    assert rc == EUNSUP

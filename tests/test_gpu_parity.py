@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (the bf16 output reading is derived in the design doc):
+* activation codes, activation scales and per-group integer partials: bit-exact;
+* low-rank activations (fp32): max |err| <= 1e-4 * max |ref|;
+* bf16 output Y against the fp64 oracle:
+    max(|err| - half a bf16 ulp of Y_ref) <= 1e-2 * RMS(Y_ref)   (the final
+    rounding to the bf16 output dtype is not charged to the kernel), and
+    mean relative error sum|err| / sum|Y_ref| <= 2e-3 (rounding included).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from oracle import formats as F, layers as L
+
+pytestmark = pytest.mark.gpu
+
+bq = pytest.importorskip("bit_quantized_linear_quantize_amd")
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a).copy()).cuda()
+
+
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def ones_smooth(K):
+    return F.bf16_bits(np.ones(K, np.float32))
+
+
+def assert_output(y_dev, y_ref, label):
+    y = F.bf16_to_f32(host_bits(y_dev)).astype(np.float64)
+    maxrel, excess, mre = L.output_errors(y, y_ref)
+    print(f"[{label}] max|err|/RMS={maxrel:.3e} (beyond half-ulp {excess:.3e}) MRE={mre:.3e}", flush=True)
+    assert np.all(np.isfinite(y))
+    assert excess <= 1e-2, label
+    assert mre <= 2e-3, label
+
+
+def prepared(x, w, bias, precision, rank, smooth="ones"):
+    K = w.shape[1]
+    sm = ones_smooth(K) if smooth == "ones" else L.smooth_factors(x, w)
+    return L.prepare_svdq_layer(w, sm, rank, precision, bias)
+
+
+def run_linear(x_bits, lay, poison=None):
+    layer = bq.SVDQLinear.from_numpy(lay)
+    x = dev_bf16(x_bits)
+    ws = torch.empty(max(layer.workspace_bytes(x.shape[0]), 1), dtype=torch.uint8, device="cuda")
+    if poison is not None:
+        ws.fill_(poison)
+    y = layer(x, workspace=ws)
+    torch.cuda.synchronize()
+    return y
+
+
+# ------------------------------------------------------------------ fixtures
+@pytest.fixture(scope="module")
+def cfg0():
+    c = S.config0()
+    return c
+
+
+@pytest.fixture(scope="module")
+def ragged():
+    rng = np.random.default_rng(11)
+    M, K, N = 300, 512, 320
+    x = S.activations(M, K, 5, rng)
+    w = S.weight(N, K, 0.02, rng, spike_rank=4)
+    b = S.bias(N, rng)
+    return x, w, b
+
+
+@pytest.fixture(scope="module")
+def cfg1_layers():
+    c = S.config1()
+    sm = L.smooth_factors(c["x"], c["w"])
+    lay4 = L.prepare_svdq_layer(c["w"], sm, 32, "int4", c["bias"])
+    lay_fp4 = L.prepare_svdq_layer(c["w"], sm, 32, "nvfp4", c["bias"])
+    return c, lay4, lay_fp4
+
+
+# ------------------------------------------------------------------ kernel 1
+def check_quantize_act(x_bits, lay, label):
+    p = lay["precision"]
+    ref = L.svdq_quantize_act(x_bits, lay["smooth"], lay["lora_down"], p)
+    x = dev_bf16(x_bits)
+    ld = dev_bf16(lay["lora_down"]) if lay["rank"] else None
+    codes, scales, lora = bq.svdq_w4a4_quantize_act(x, dev_bf16(lay["smooth"]), ld, p)
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy()
+    sc = host_bits(scales) if p == "int4" else scales.cpu().numpy()
+    bad = np.argwhere(codes != ref["packed"])
+    assert bad.size == 0, f"{label}: {len(bad)} code bytes differ, first {bad[:4].tolist()}"
+    assert np.array_equal(sc, ref["scales"]), f"{label}: scales differ"
+    if lay["rank"]:
+        la = lora.cpu().numpy().astype(np.float64)
+        err = np.abs(la - ref["lora_act"]).max()
+        tol = 1e-4 * np.abs(ref["lora_act"]).max() + 1e-6
+        print(f"[{label}] lora_act max err {err:.3e} (tol {tol:.3e})", flush=True)
+        assert err <= tol, label
+
+
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_quantize_act_config0(cfg0, precision):
+    lay = prepared(cfg0["x"], cfg0["w"], cfg0["bias"], precision, 32)
+    check_quantize_act(cfg0["x"], lay, f"k1 cfg0 {precision}")
+
+
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+@pytest.mark.parametrize("rank", [0, 16, 128])
+def test_quantize_act_ragged(ragged, precision, rank):
+    x, w, b = ragged
+    lay = prepared(x, w, b, precision, rank, smooth="calibrated")
+    check_quantize_act(x, lay, f"k1 ragged {precision} r{rank}")
+
+
+@pytest.mark.parametrize("which", ["int4", "nvfp4"])
+def test_quantize_act_full_size(cfg1_layers, which):
+    c, lay4, layfp4 = cfg1_layers
+    check_quantize_act(c["x"], lay4 if which == "int4" else layfp4, f"k1 cfg1 {which}")
+
+
+def test_quantize_act_edge_values():
+    # zero rows, a denormal-only group, huge and tiny magnitudes, exact ties
+    rng = np.random.default_rng(5)
+    M, K = 40, 256
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    xf[0] = 0
+    xf[1, :64] = 1e-39
+    xf[2] *= 1e30
+    xf[3] *= 1e-30
+    xf[4, :64] = np.arange(64) * 0.5
+    xf[5, :16] = [6, 5, 3.5, 2.5, 1.75, 1.25, .75, .25, -6, -5, -3.5, -2.5, -1.75, -1.25, -.75, -.25]
+    xf[6, :] = -0.0
+    x = S.to_bf16_bits(xf)
+    w = rng.standard_normal((64, K)) * 0.02
+    for p in ("int4", "nvfp4"):
+        lay = prepared(x, w, None, p, 16)
+        check_quantize_act(x, lay, f"k1 edge {p}")
+
+
+# ------------------------------------------------------------------ kernel 2 partials
+def check_partials(act_codes, w_codes, p, label):
+    ref = L.svdq_partials_ref(act_codes, w_codes, p)
+    got = bq.svdq_w4a4_gemm_partials(dev_u8(F.pack_nibbles(act_codes)), dev_u8(F.pack_nibbles(w_codes)), p)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.int64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{label}: {len(bad)} partials differ, first {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_partials_config0(cfg0, precision):
+    lay = prepared(cfg0["x"], cfg0["w"], None, precision, 32)
+    act = L.svdq_quantize_act(cfg0["x"], lay["smooth"], lay["lora_down"], precision)
+    check_partials(act["codes"], lay["w_codes"], precision, f"partials cfg0 {precision}")
+
+
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_partials_all_codes(precision):
+    # every nibble value on both sides (int4 includes the 0x8 "-0" code)
+    rng = np.random.default_rng(7)
+    a = rng.integers(0, 16, size=(200, 256)).astype(np.uint8)
+    w = rng.integers(0, 16, size=(192, 256)).astype(np.uint8)
+    check_partials(a, w, precision, f"partials random {precision}")
+
+
+@pytest.mark.parametrize("which", ["int4", "nvfp4"])
+def test_partials_full_size_sampled(cfg1_layers, which):
+    c, lay4, layfp4 = cfg1_layers
+    lay = lay4 if which == "int4" else layfp4
+    act = L.svdq_quantize_act(c["x"][:130], lay["smooth"], lay["lora_down"], which)
+    check_partials(act["codes"], lay["w_codes"][1024:1024 + 192], which, f"partials cfg1 {which}")
+
+
+# ------------------------------------------------------------------ full linear
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_linear_config0(cfg0, precision):
+    lay = prepared(cfg0["x"], cfg0["w"], cfg0["bias"], precision, 32)
+    y = run_linear(cfg0["x"], lay)
+    assert_output(y, L.svdq_linear_ref(cfg0["x"], lay), f"linear cfg0 {precision}")
+
+
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+@pytest.mark.parametrize("rank", [0, 16, 32, 128])
+def test_linear_ragged(ragged, precision, rank):
+    x, w, b = ragged
+    lay = prepared(x, w, b, precision, rank, smooth="calibrated")
+    y = run_linear(x, lay)
+    assert_output(y, L.svdq_linear_ref(x, lay), f"linear ragged {precision} r{rank}")
+
+
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_linear_single_row_and_no_bias(ragged, precision):
+    x, w, _ = ragged
+    lay = prepared(x[:1], w, None, precision, 32, smooth="calibrated")
+    y = run_linear(x[:1], lay)
+    assert_output(y, L.svdq_linear_ref(x[:1], lay), f"linear M=1 {precision}")
+
+
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_linear_zero_identities(ragged, precision):
+    x, w, b = ragged
+    N, K = w.shape
+    lay = prepared(x, np.zeros((N, K)), None, precision, 0)
+    y = run_linear(x, lay)
+    assert not host_bits(y).any() or not np.any(F.bf16_to_f32(host_bits(y)))
+    lay = prepared(x, w, b, precision, 32, smooth="calibrated")
+    y = run_linear(np.zeros_like(x), lay)
+    assert np.array_equal(host_bits(y), np.broadcast_to(b, y.shape))
+
+
+@pytest.mark.parametrize("which", ["int4", "nvfp4"])
+def test_linear_full_size(cfg1_layers, which):
+    c, lay4, layfp4 = cfg1_layers
+    lay = lay4 if which == "int4" else layfp4
+    y = run_linear(c["x"], lay)
+    assert_output(y, L.svdq_linear_ref(c["x"], lay), f"linear cfg1 {which}")
+
+
+def test_linear_deterministic_with_poisoned_workspace(ragged):
+    x, w, b = ragged
+    for p in ("int4", "nvfp4"):
+        lay = prepared(x, w, b, p, 32, smooth="calibrated")
+        y1 = host_bits(run_linear(x, lay, poison=0x00))
+        y2 = host_bits(run_linear(x, lay, poison=0xFF))
+        assert np.array_equal(y1, y2)
+
+
+# ------------------------------------------------------------------ AWQ
+def run_awq(x_bits, lay):
+    layer = bq.AWQLinear.from_numpy(lay)
+    y = layer(dev_bf16(x_bits))
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("M", [1, 2, 16, 33])
+def test_awq_ragged(M):
+    rng = np.random.default_rng(M)
+    K, N = 384, 320
+    w = rng.standard_normal((N, K)) * 0.02
+    lay = L.prepare_awq_layer(w, S.bias(N, rng))
+    x = S.activations(M, K, 0, rng)
+    assert_output(run_awq(x, lay), L.awq_linear_ref(x, lay), f"awq ragged M={M}")
+
+
+def test_awq_config3():
+    c = S.config3()
+    lay = L.prepare_awq_layer(c["w"], c["bias"])
+    for M, x in c["xs"].items():
+        assert_output(run_awq(x, lay), L.awq_linear_ref(x, lay), f"awq cfg3 M={M}")
+
+
+def test_awq_no_bias_and_extreme_codes():
+    rng = np.random.default_rng(3)
+    K, N = 256, 128
+    w = rng.standard_normal((N, K)) * 0.02
+    w[0] = 0.0           # all-zero rows -> zero scale groups
+    w[1, :64] = 5.0      # one-sided range (min clamps to 0)
+    lay = L.prepare_awq_layer(w, None)
+    x = S.activations(4, K, 0, rng)
+    assert_output(run_awq(x, lay), L.awq_linear_ref(x, lay), "awq extremes")
