@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 SVDQ W4A4 linear; prints ONE JSON line.
+
+Workload (the headline): one svdq_w4a4 int4 linear of DiT attention-projection
+shape, X bf16 [4096, 3072] (1 % outlier channels), W [3072, 3072], rank 32,
+group 64 -- a "step" is one svdq_w4a4_linear call (kernel 1 + kernel 2), inputs
+resident in HBM.  value = effective TOPS = 2 M N K / step time.
+
+Also measured in the same run (reported under "extra"):
+  * the nvfp4 variant of the same layer;
+  * per-kernel durations (HIP events on the launch stream) of
+    quantize_act_lora_down and gemm_w4a4_lora_up, from which the roofline
+    object of the dominant kernel (gemm_w4a4_lora_up) is computed;
+  * awq_w4a16 at M in {1, 2, 16}, K=3072, N=18432, rotating over 12 weight
+    copies (382 MB > the 256 MB last-level cache) so weights come from HBM.
+The weights of the timed legs are random but valid packed layers (prepared
+weight values do not change the work); parity with the oracle is the job of
+tests/.  The cpu_baseline leg times the CPU oracle on the same inputs.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective W4A4 linear TOPS at M=4096,K=N=3072 (int4 & nvfp4); % MFMA/HBM roofline"
+PEAK = {"fp8": 5000.0, "f16": 2500.0, "bf16": 2500.0, "hbm": 8000.0}  # TFLOP/s, GB/s (MI355X dense)
+KERNEL_SOURCES = {"gemm_w4a4_lora_up": ["gemm_w4a4.hip", "device_common.hpp"],
+                  "quantize_act_lora_down": ["quantize_act.hip", "device_common.hpp"],
+                  "awq_w4a16": ["awq_gemv.hip", "device_common.hpp"]}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "bit_quantized_linear_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}|{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_events(fn, steps, stream):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per call
+
+
+ONLY_LEGS = {"quant_int4", "quant_nvfp4", "gemm_int4", "gemm_nvfp4", "awq_m1", "awq_m16", "copy"}
+
+
+def run_only(leg, steps):
+    """Launch a single kernel of the headline workload `steps` times (after one
+    warm-up call), for per-kernel hardware-counter passes.  `copy` is a plain
+    device-to-device copy of 256 MiB, the reference for scaling HBM byte
+    counters."""
+    import numpy as np
+    import torch
+
+    import synthetic as S
+    import bit_quantized_linear_quantize_amd as bq
+
+    bq.lib()
+    torch.cuda.set_device(0)
+    M, K, N, rank = 4096, 3072, 3072, 32
+    if leg == "copy":
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        fn = lambda: b.copy_(a)
+    elif leg.startswith("awq"):
+        Ma = 1 if leg == "awq_m1" else 16
+        ra = S.streams(7, 13)
+        layers = [bq.AWQLinear.from_numpy(S.random_awq_layer(18432, 3072, ra[i])) for i in range(12)]
+        xa = torch.from_numpy(S.activations(Ma, 3072, 0, ra[-1]).view(np.int16).copy()).view(torch.bfloat16).cuda()
+        oa = torch.empty((Ma, 18432), dtype=torch.bfloat16, device="cuda")
+        it = [0]
+
+        def fn():
+            layers[it[0] % 12](xa, out=oa)
+            it[0] += 1
+    else:
+        precision = "int4" if leg.endswith("int4") else "nvfp4"
+        rx, rl = S.streams(0, 2)
+        x = torch.from_numpy(S.activations(M, K, round(0.01 * K), rx).view(np.int16).copy()).view(torch.bfloat16).cuda()
+        layer = bq.SVDQLinear.from_numpy(S.random_svdq_layer(N, K, precision, rank, rl))
+        ws = torch.empty(layer.workspace_bytes(M), dtype=torch.uint8, device="cuda")
+        bq.svdq_w4a4_quantize(x, layer, ws)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        if leg.startswith("quant"):
+            fn = lambda: bq.svdq_w4a4_quantize(x, layer, ws)
+        else:
+            fn = lambda: bq.svdq_w4a4_gemm(ws, M, layer, out=out)
+    fn()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    log(f"ran {leg} x{steps}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-extra", action="store_true", help="skip the nvfp4 and AWQ legs")
+    ap.add_argument("--only", choices=sorted(ONLY_LEGS),
+                    help="run one kernel --steps times and exit (for rocprofv3 counter passes)")
+    args = ap.parse_args()
+    if args.only:
+        run_only(args.only, args.steps)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU kernel path only: this library has no multi-GPU "
+              "path (sharding is described in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic as S
+    import bit_quantized_linear_quantize_amd as bq
+
+    bq.lib()  # fails loudly when the HIP library is missing
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')}")
+
+    M, K, N, rank = 4096, 3072, 3072, 32
+    rx, rl4, rl8 = S.streams(0, 3)
+    x_bits = S.activations(M, K, round(0.01 * K), rx)
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    ops = 2.0 * M * N * K
+
+    def bench_svdq(precision, rng, steps, warmup):
+        lay_np = S.random_svdq_layer(N, K, precision, rank, rng)
+        layer = bq.SVDQLinear.from_numpy(lay_np)
+        ws = torch.empty(layer.workspace_bytes(M), dtype=torch.uint8, device="cuda")
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        G = bq.GROUP_SIZE[precision]
+        step = lambda: layer(x, out=out, workspace=ws)
+        k1 = lambda: bq.svdq_w4a4_quantize(x, layer, ws)
+        k2 = lambda: bq.svdq_w4a4_gemm(ws, M, layer, out=out)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        if torch.distributed.is_available() and torch.distributed.is_initialized():
+            torch.distributed.barrier()
+        ms = time_events(step, steps, stream)
+        for _ in range(warmup):
+            k1()
+            k2()
+        t1 = time_events(k1, steps, stream)
+        t2 = time_events(k2, steps, stream)
+        sb = 2 if precision == "int4" else 1
+        # algorithmic bytes of kernel 1: read x, smooth, lora_down; write 4-bit codes
+        # (counted at 4 bits even where the workspace keeps 8-bit operands), scales, lora_act
+        k1_bytes = M * K * 2 + K * 2 + rank * K * 2 + M * K // 2 + M * (K // G) * sb + M * rank * 4
+        return dict(ms=ms, k1_ms=t1, k2_ms=t2, k1_bytes=k1_bytes, lay=lay_np)
+
+    log("timing svdq_w4a4 int4 ...")
+    r4 = bench_svdq("int4", rl4, args.steps, args.warmup)
+    value = ops / (r4["ms"] * 1e-3) / 1e12
+    k2_tops = ops / (r4["k2_ms"] * 1e-3) / 1e12
+    roofline = {"kernel": "gemm_w4a4_lora_up<int4>", "bound": "mfma", "achieved": round(k2_tops, 2),
+                "peak": PEAK["fp8"], "unit": "TFLOP/s", "frac": round(k2_tops / PEAK["fp8"], 4),
+                "traffic": measured_traffic("gemm_w4a4_lora_up", "int4_4096x3072x3072_r32"),
+                "avg_launch_us": round(r4["k2_ms"] * 1e3, 2),
+                "instruction": "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands holding int4 codes)"}
+
+    extra = {"int4": {"step_us": round(r4["ms"] * 1e3, 2),
+                      "quantize_act_lora_down_us": round(r4["k1_ms"] * 1e3, 2),
+                      "quantize_act_lora_down_GBps": round(r4["k1_bytes"] / (r4["k1_ms"] * 1e-3) / 1e9, 1),
+                      "gemm_w4a4_lora_up_us": round(r4["k2_ms"] * 1e3, 2),
+                      "gemm_w4a4_lora_up_TOPS": round(k2_tops, 1)}}
+
+    if not args.no_extra:
+        log("timing svdq_w4a4 nvfp4 ...")
+        r8 = bench_svdq("nvfp4", rl8, args.steps, args.warmup)
+        k2n = ops / (r8["k2_ms"] * 1e-3) / 1e12
+        extra["nvfp4"] = {"value_TOPS": round(ops / (r8["ms"] * 1e-3) / 1e12, 1),
+                          "step_us": round(r8["ms"] * 1e3, 2),
+                          "quantize_act_lora_down_us": round(r8["k1_ms"] * 1e3, 2),
+                          "quantize_act_lora_down_GBps": round(r8["k1_bytes"] / (r8["k1_ms"] * 1e-3) / 1e9, 1),
+                          "gemm_w4a4_lora_up_us": round(r8["k2_ms"] * 1e3, 2),
+                          "gemm_w4a4_lora_up_TOPS": round(k2n, 1),
+                          "gemm_frac_of_f16_peak": round(k2n / PEAK["f16"], 4),
+                          "instruction": "v_mfma_f32_32x32x16_f16 (exactly dequantized E2M1 x E4M3)"}
+        log("timing awq_w4a16 ...")
+        Na, Ka, copies = 18432, 3072, 12
+        ra = S.streams(7, copies + 1)
+        layers = [bq.AWQLinear.from_numpy(S.random_awq_layer(Na, Ka, ra[i])) for i in range(copies)]
+        awq = {}
+        for Ma in (1, 2, 16):
+            xa = torch.from_numpy(S.activations(Ma, Ka, 0, ra[-1]).view(np.int16).copy()).view(torch.bfloat16).cuda()
+            oa = torch.empty((Ma, Na), dtype=torch.bfloat16, device="cuda")
+            it = [0]
+
+            def call():
+                layers[it[0] % copies](xa, out=oa)
+                it[0] += 1
+            for _ in range(2 * copies):
+                call()
+            reps = max(args.steps, 10 * copies)
+            ms = time_events(call, reps, stream)
+            nbytes = Na * Ka // 2 + 2 * Na * (Ka // 64) * 2 + Ma * Ka * 2 + Ma * Na * 2 + Na * 2
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            awq[f"M={Ma}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                              "frac_of_hbm": round(gbps / PEAK["hbm"], 4), "bytes": nbytes}
+        extra["awq_w4a16_N18432_K3072"] = awq
+        del layers
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        from oracle import formats as F, layers as L
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        except Exception:
+            threads = os.cpu_count()
+        lay = dict(r4["lay"])
+        lay["w_codes"] = F.unpack_nibbles(lay["packed_w"])
+        rows = M
+        reps, t0 = 0, time.perf_counter()
+        while True:  # the full workload, repeated for ~10 s of CPU work
+            L.svdq_linear_ref(x_bits[:rows], lay)
+            reps += 1
+            if time.perf_counter() - t0 >= 10.0 or reps >= 50:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TOPS", "cores": threads,
+               "kind": "oracle", "seconds_per_call": round(dt, 3), "calls": reps,
+               "sample": f"the full workload ({rows}x{K} activations, {N}x{K} int4 layer, rank {rank}), "
+                         f"{reps} calls: activation quantizer + fp64 dequantized GEMM + low-rank + bias "
+                         "(numpy/OpenBLAS)"}
+
+    rec = {"metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r4["ms"], 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int4",
+           "data": "synthetic",
+           "config": {"workload": "svdq_w4a4 int4 linear, M=4096 K=N=3072, rank 32, group 64 "
+                                  "(DiT attention projection, 1% outlier channels)",
+                      "M": M, "K": K, "N": N, "rank": rank, "group_size": 64, "precision": "int4",
+                      "parallelism": "none (1 GPU)"},
+           "roofline": roofline, "cpu_baseline": cpu, "extra": extra}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,8 @@ STATUS = {0: "SVDQ_OK", -1: "SVDQ_EINVAL", -2: "SVDQ_EUNSUPPORTED", -3: "SVDQ_EA
           -4: "SVDQ_EWORKSPACE", -5: "SVDQ_EDEVICE"}
 
 # entry points declared in include/svdq_w4a4.h
-EXPORTS = ("svdq_w4a4_workspace_bytes", "svdq_w4a4_linear", "awq_w4a16_linear",
+EXPORTS = ("svdq_w4a4_workspace_bytes", "svdq_w4a4_linear", "svdq_w4a4_quantize", "svdq_w4a4_gemm",
+           "awq_w4a16_linear",
            "svdq_w4a4_quantize_act", "svdq_w4a4_gemm_partials", "svdq_w4a4_check",
            "awq_w4a16_check", "svdq_last_error")
 
@@ -52,6 +53,11 @@ def lib():
         L.svdq_w4a4_linear.argtypes = [P, I64, I64, I64, P, P, ctypes.c_float, P, P, P, P, I, I, I,
                                        P, P, ctypes.c_size_t, P]
         L.svdq_w4a4_linear.restype = I
+        L.svdq_w4a4_quantize.argtypes = [P, I64, I64, P, P, I, I, I, P, ctypes.c_size_t, P]
+        L.svdq_w4a4_quantize.restype = I
+        L.svdq_w4a4_gemm.argtypes = [P, ctypes.c_size_t, I64, I64, I64, P, P, ctypes.c_float, P, P, I, I, I,
+                                     P, P]
+        L.svdq_w4a4_gemm.restype = I
         L.awq_w4a16_linear.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P]
         L.awq_w4a16_linear.restype = I
         L.svdq_w4a4_quantize_act.argtypes = [P, I64, I64, P, P, I, I, I, P, P, P, P]
@@ -158,6 +164,27 @@ def svdq_w4a4_linear(x, layer, out=None, workspace=None, stream=None):
     return out
 
 
+def svdq_w4a4_quantize(x, layer, workspace, stream=None):
+    """First phase of svdq_w4a4_linear: quantize x into `workspace`."""
+    x = _contig(x, torch.bfloat16, "x")
+    M, K = x.shape
+    _check(lib().svdq_w4a4_quantize(
+        _ptr(x), M, K, _ptr(layer.smooth), _ptr(layer.lora_down), PRECISIONS[layer.precision],
+        GROUP_SIZE[layer.precision], layer.rank, _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def svdq_w4a4_gemm(workspace, M, layer, out=None, stream=None):
+    """Second phase of svdq_w4a4_linear: the 4-bit product from `workspace`."""
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=torch.bfloat16, device=workspace.device)
+    _check(lib().svdq_w4a4_gemm(
+        _ptr(workspace), workspace.numel(), M, layer.K, layer.N, _ptr(layer.packed_w), _ptr(layer.wscales),
+        layer.wtscale, _ptr(layer.lora_up), _ptr(layer.bias), PRECISIONS[layer.precision],
+        GROUP_SIZE[layer.precision], layer.rank, _ptr(out), _stream(stream)))
+    return out
+
+
 class AWQLinear:
     """Device-resident inputs of one awq_w4a16 layer: packed_w uint8 [N, K/2],
     wscales / wzeros bf16 [N, K/64], bias bf16 [N] or None."""
@@ -194,16 +221,20 @@ def awq_w4a16_linear(x, layer, out=None, stream=None):
     return out
 
 
-def svdq_w4a4_quantize_act(x, smooth, lora_down, precision, stream=None):
-    """Parity export of kernel 1: returns (codes uint8 [M, K/2], scales, lora_act fp32 [M, rank])."""
+def svdq_w4a4_quantize_act(x, smooth, lora_down, precision, stream=None, out=None):
+    """Kernel 1 on its own: returns (codes uint8 [M, K/2], scales, lora_act fp32 [M, rank]).
+    ``out`` may pass preallocated (codes, scales, lora_act) tensors."""
     x = _contig(x, torch.bfloat16, "x")
     M, K = x.shape
     rank = 0 if lora_down is None else lora_down.shape[0]
     G = GROUP_SIZE[precision]
-    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
     sdt = torch.bfloat16 if precision == "int4" else torch.uint8
-    scales = torch.empty((M, K // G), dtype=sdt, device=x.device)
-    lora_act = torch.empty((M, rank), dtype=torch.float32, device=x.device) if rank else None
+    if out is not None:
+        codes, scales, lora_act = out
+    else:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((M, K // G), dtype=sdt, device=x.device)
+        lora_act = torch.empty((M, rank), dtype=torch.float32, device=x.device) if rank else None
     _check(lib().svdq_w4a4_quantize_act(
         _ptr(x), M, K, _ptr(smooth), _ptr(lora_down), PRECISIONS[precision], G, rank,
         _ptr(codes), _ptr(scales), _ptr(lora_act), _stream(stream)))

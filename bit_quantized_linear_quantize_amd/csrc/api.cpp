@@ -105,8 +105,14 @@ size_t w_scale_bytes(int64_t N, int64_t K, int precision) {
   return precision == SVDQ_INT4 ? size_t(N) * size_t(K / 64) * 2 : size_t(N) * size_t(K / 16);
 }
 
+// int4 activation codes are kept as E4M3 bytes (the product kernel's operand
+// format); nvfp4 codes as packed nibbles.
+size_t act_code_bytes(int64_t M, int64_t K, int precision) {
+  return precision == SVDQ_INT4 ? size_t(M) * size_t(K) : size_t(M) * size_t(K / 2);
+}
+
 size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
-  return round_up(size_t(M) * size_t(K / 2)) + round_up(act_scale_bytes(M, K, precision)) +
+  return round_up(act_code_bytes(M, K, precision)) + round_up(act_scale_bytes(M, K, precision)) +
          round_up(size_t(M) * size_t(rank) * 4);
 }
 
@@ -172,6 +178,38 @@ int launch_status(hipError_t e, const char* what) {
   return SVDQ_OK;
 }
 
+struct Carve {
+  uint8_t* codes;   // int4: E4M3 bytes [M, K]; nvfp4: nibbles [M, K/2]
+  uint8_t* scales;  // bf16 [M, K/64] | u8 [M, K/16]
+  float* lora_act;  // f32 [M, rank]
+};
+
+Carve carve(void* workspace, int64_t M, int64_t K, int precision) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  Carve c;
+  c.codes = ws;
+  c.scales = c.codes + round_up(act_code_bytes(M, K, precision));
+  c.lora_act = reinterpret_cast<float*>(c.scales + round_up(act_scale_bytes(M, K, precision)));
+  return c;
+}
+
+int launch_quantize(const void* x, int64_t M, int64_t K, const void* smooth, const void* lora_down,
+                    int precision, int rank, void* workspace, hipStream_t s) {
+  const Carve c = carve(workspace, M, K, precision);
+  svdq::QuantActArgs qa{x, smooth, lora_down, c.codes, c.scales, c.lora_act, M, K, precision, rank,
+                        precision == SVDQ_INT4};
+  return launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
+}
+
+int launch_gemm(const void* workspace, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                const void* wscales, float wtscale, const void* lora_up, const void* bias, int precision,
+                int rank, void* out, hipStream_t s) {
+  const Carve c = carve(const_cast<void*>(workspace), M, K, precision);
+  svdq::GemmArgs ga{c.codes, c.scales, c.lora_act, packed_w, wscales, lora_up, bias, out, nullptr,
+                    wtscale, M, K, N, precision, rank};
+  return launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,6 +246,63 @@ int awq_w4a16_check(const void* x, int64_t M, int64_t K, int64_t N, const void* 
   return SVDQ_OK;
 }
 
+int svdq_w4a4_quantize(const void* x, int64_t M, int64_t K, const void* smooth, const void* lora_down,
+                       int precision, int group_size, int rank, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  int rc = check_svdq_kind(precision, group_size, rank);
+  if (rc) return rc;
+  rc = check_shape(M, K, 64);
+  if (rc) return rc;
+  if (!x || !smooth || !workspace) return fail(SVDQ_EINVAL, "null pointer argument");
+  if ((rank > 0) != (lora_down != nullptr))
+    return fail(SVDQ_EINVAL, "lora_down must be non-null exactly when rank > 0");
+  const void* ptrs[] = {x, smooth, lora_down, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  const size_t need = workspace_bytes(M, K, precision, rank);
+  if (overlaps(Range{x, size_t(M) * size_t(K) * 2}, Range{workspace, need}))
+    return fail(SVDQ_EINVAL, "workspace overlaps x");
+  if (ws_bytes < need) return fail(SVDQ_EWORKSPACE, "workspace too small");
+  rc = check_device_arch();
+  if (rc) return rc;
+  return launch_quantize(x, M, K, smooth, lora_down, precision, rank, workspace,
+                         static_cast<hipStream_t>(stream));
+}
+
+int svdq_w4a4_gemm(const void* workspace, size_t ws_bytes, int64_t M, int64_t K, int64_t N,
+                   const void* packed_w, const void* wscales, float wtscale, const void* lora_up,
+                   const void* bias, int precision, int group_size, int rank, void* out, void* stream) {
+  g_last_error.clear();
+  int rc = check_svdq_kind(precision, group_size, rank);
+  if (rc) return rc;
+  rc = check_shape(M, K, N);
+  if (rc) return rc;
+  if (!workspace || !packed_w || !wscales || !out) return fail(SVDQ_EINVAL, "null pointer argument");
+  if ((rank > 0) != (lora_up != nullptr))
+    return fail(SVDQ_EINVAL, "lora_up must be non-null exactly when rank > 0");
+  const void* ptrs[] = {workspace, packed_w, wscales, lora_up, bias, out};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  if (precision == SVDQ_INT4 && wtscale != 1.0f) return fail(SVDQ_EINVAL, "wtscale must be 1.0 for int4");
+  if (precision == SVDQ_NVFP4 && !(std::isfinite(wtscale) && wtscale > 0.f))
+    return fail(SVDQ_EINVAL, "wtscale must be finite and positive");
+  const size_t need = workspace_bytes(M, K, precision, rank);
+  const Range o{out, size_t(M) * size_t(N) * 2};
+  const Range ins[] = {{workspace, need},
+                       {packed_w, size_t(N) * size_t(K / 2)},
+                       {wscales, w_scale_bytes(N, K, precision)},
+                       {lora_up, size_t(N) * size_t(rank) * 2},
+                       {bias, size_t(N) * 2}};
+  for (const Range& r : ins)
+    if (overlaps(o, r)) return fail(SVDQ_EINVAL, "out overlaps an input or the workspace");
+  if (ws_bytes < need) return fail(SVDQ_EWORKSPACE, "workspace too small");
+  rc = check_device_arch();
+  if (rc) return rc;
+  return launch_gemm(workspace, M, K, N, packed_w, wscales, wtscale, lora_up, bias, precision, rank, out,
+                     static_cast<hipStream_t>(stream));
+}
+
 int svdq_w4a4_linear(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
                      const void* wscales, float wtscale, const void* smooth, const void* lora_down,
                      const void* lora_up, const void* bias, int precision, int group_size, int rank,
@@ -218,18 +313,10 @@ int svdq_w4a4_linear(const void* x, int64_t M, int64_t K, int64_t N, const void*
   if (rc) return rc;
   rc = check_device_arch();
   if (rc) return rc;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* codes = ws;
-  uint8_t* scales = codes + round_up(size_t(M) * size_t(K / 2));
-  float* lora_act = reinterpret_cast<float*>(scales + round_up(act_scale_bytes(M, K, precision)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-
-  svdq::QuantActArgs qa{x, smooth, lora_down, codes, scales, lora_act, M, K, precision, rank};
-  rc = launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
+  rc = launch_quantize(x, M, K, smooth, lora_down, precision, rank, workspace, s);
   if (rc) return rc;
-  svdq::GemmArgs ga{codes, scales, lora_act, packed_w, wscales, lora_up, bias, out, nullptr,
-                    wtscale, M, K, N, precision, rank};
-  return launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up launch");
+  return launch_gemm(workspace, M, K, N, packed_w, wscales, wtscale, lora_up, bias, precision, rank, out, s);
 }
 
 int awq_w4a16_linear(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
@@ -260,7 +347,8 @@ int svdq_w4a4_quantize_act(const void* x, int64_t M, int64_t K, const void* smoo
     if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
   rc = check_device_arch();
   if (rc) return rc;
-  svdq::QuantActArgs qa{x, smooth, lora_down, codes_out, scales_out, lora_act_out, M, K, precision, rank};
+  svdq::QuantActArgs qa{x, smooth, lora_down, codes_out, scales_out, lora_act_out, M, K, precision, rank,
+                        false};
   return launch_status(svdq::launch_quantize_act(qa, static_cast<hipStream_t>(stream)),
                        "quantize_act_lora_down launch");
 }

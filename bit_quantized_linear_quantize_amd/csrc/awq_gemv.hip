@@ -6,25 +6,31 @@
 // format: unsigned codes q (0..15), per-group bf16 scale s and integer
 // zero-point z, W = (q - z) s;  Y = X W^T + bias with fp32 accumulation.
 //
-// gfx950 design: bandwidth-bound (4.5 bits per weight streamed once per call).
-// One wave owns 32 weight rows (output columns) and all of K; a workgroup has
-// 4 waves.  Lane (n = lane%32, h = lane/32) streams 16 bytes of row n per group
-// (columns 64g + 32h .. +31), several groups in flight.  Codes become bf16
-// operands 128 + q with one v_perm + one OR per pair (0x4300 | q is the bf16
-// bit pattern of 128 + q), and one 32x32x16 bf16 matrix instruction per 16
-// columns contracts them with up to 32 rows of X.  Per group,
-//   sum_k x (q - z) s = s * (P - (128 + z) * sum_k x),
-// with P the matrix-instruction result (exact products, fp32 sums) and
-// sum_k x precomputed per workgroup in LDS.  Rows of X beyond M are zero and
-// skip the epilogue.  X is re-read from L2 by every wave (it is small).
+// gfx950 design -- bandwidth-bound: 4.5 bits per weight streamed once per 32
+// rows of X.
+// * A workgroup owns 32 weight rows (output columns); its 4 waves split K in
+//   four contiguous ranges, so 4 x N/32 waves stream independently.  Each lane
+//   issues all of its 16-byte code loads (one per group in its range) before
+//   computing, so the whole weight matrix is in flight at once.
+// * Lane (n = lane%32, h = lane/32) covers columns 64g + 32h .. +31 of weight
+//   row n: four 32x32x16 bf16 matrix instructions per group, each mixing only
+//   columns of that group.
+// * Codes become bf16 operands 128 + q (0x4300 | q is the bit pattern of
+//   128 + q) with one v_perm and one OR per pair.  A second operand set holds
+//   -(128 + z) in every slot, so the same accumulator collects
+//   sum_k x (128 + q) - sum_k x (128 + z) = sum_k x (q - z) exactly in the
+//   matrix unit (exact bf16 products, fp32 sums), and the scale needs one FMA
+//   per output: acc += t * s.
+// * Rows of X beyond M are zero; the epilogue skips blocks of rows beyond M.
+//   The four K-range partials are summed in LDS in a fixed order.
 
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace svdq {
 
-constexpr int kAwqWaves = 4;
-constexpr int kAwqPF = 4;  // groups in flight per lane
+constexpr int kAwqWaves = 4;     // K ranges per workgroup
+constexpr int kAwqMaxG = 16;     // groups per wave held in registers at once
 
 __device__ __forceinline__ bf16x8 awq_operand(uint32_t w) {
   const uint32_t lo = w & 0x0F0F0F0Fu;          // nibbles 0, 2, 4, 6
@@ -38,7 +44,7 @@ __device__ __forceinline__ bf16x8 awq_operand(uint32_t w) {
 }
 
 __global__ __launch_bounds__(256) void awq_w4a16_kernel(AwqArgs args) {
-  extern __shared__ float xsum[];  // [32 rows][G]
+  __shared__ float part[kAwqWaves][32][33];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -49,85 +55,92 @@ __global__ __launch_bounds__(256) void awq_w4a16_kernel(AwqArgs args) {
   const int rows = min(32, M - m0);
   const uint16_t* __restrict__ x = (const uint16_t*)args.x;
 
-  // sum of X over each group, for the 128 + q offset of the operands
-  for (int o = tid; o < 32 * G; o += 256) {
-    const int m = o / G, g = o - m * G;
-    float s = 0.f;
-    if (m < rows) {
-      const u32x4* p = (const u32x4*)(x + (size_t)(m0 + m) * K + g * 64);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const u32x4 w = p[v];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s += bf16_lo(w[i]) + bf16_hi(w[i]);
-      }
-    }
-    xsum[o] = s;
-  }
-  __syncthreads();
-
   const int n_l = lane & 31;
   const int h = lane >> 5;
-  const int n = blockIdx.x * (32 * kAwqWaves) + wave * 32 + n_l;
+  const int n = blockIdx.x * 32 + n_l;
   const int nc = min(n, N - 1);
+  // this wave's contiguous range of groups
+  const int gpw = (G + kAwqWaves - 1) / kAwqWaves;
+  const int g0 = min(G, wave * gpw);
+  const int g1 = min(G, g0 + gpw);
   const uint8_t* wrow = (const uint8_t*)args.w_codes + (size_t)nc * K2 + h * 16;
   const uint16_t* srow = (const uint16_t*)args.scales + (size_t)nc * G;
   const uint16_t* zrow = (const uint16_t*)args.zeros + (size_t)nc * G;
-  const int xm = m0 + n_l;  // row of X this lane feeds into the A operand
   const bool x_ok = n_l < rows;
-  const uint16_t* xrow = x + (size_t)(x_ok ? xm : 0) * K + h * 32;
+  const uint16_t* xrow = x + (size_t)(m0 + (x_ok ? n_l : 0)) * K + h * 32;
 
   f32x16 acc = {};
   const f32x16 zero16 = {};
-  u32x4 wbuf[kAwqPF];
+  for (int gb = g0; gb < g1; gb += kAwqMaxG) {
+    // every load of this batch is issued before any use, so only one memory
+    // latency is exposed per batch (codes, scales and zero-points)
+    u32x4 wbuf[kAwqMaxG];
+    uint16_t sbuf[kAwqMaxG], zbuf[kAwqMaxG];
 #pragma unroll
-  for (int p = 0; p < kAwqPF; ++p)
-    if (p < G) wbuf[p] = *(const u32x4*)(wrow + p * 32);
-
-  for (int gb = 0; gb < G; gb += kAwqPF) {
+    for (int p = 0; p < kAwqMaxG; ++p)
+      if (gb + p < g1) wbuf[p] = *(const u32x4*)(wrow + (gb + p) * 32);
 #pragma unroll
-    for (int p = 0; p < kAwqPF; ++p) {
+    for (int p = 0; p < kAwqMaxG; ++p)
+      if (gb + p < g1) {
+        sbuf[p] = srow[gb + p];
+        zbuf[p] = zrow[gb + p];
+      }
+    // rows of X for the A operand: 64 bytes per lane and group, two groups ahead
+    u32x4 xbuf[3][4];
+    auto load_x = [&](int slot, int g) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xbuf[slot][j] = (x_ok && g < g1) ? *(const u32x4*)(xrow + g * 64 + j * 8) : u32x4{0u, 0u, 0u, 0u};
+    };
+    load_x(0, gb);
+    load_x(1, gb + 1);
+#pragma unroll
+    for (int p = 0; p < kAwqMaxG; ++p) {
       const int g = gb + p;
-      if (g >= G) break;
-      const u32x4 wv = wbuf[p];
-      if (g + kAwqPF < G) wbuf[p] = *(const u32x4*)(wrow + (g + kAwqPF) * 32);
-      f32x16 P = zero16;
+      if (g >= g1) continue;
+      if (p + 2 < kAwqMaxG) load_x((p + 2) % 3, g + 2);
+      const float s = bf16_bits_to_f32(sbuf[p]);
+      const uint32_t zb = f32_to_bf16_bits(-(128.0f + bf16_bits_to_f32(zbuf[p])));  // exact
+      const uint32_t zz = zb | (zb << 16);
+      const bf16x8 zop = __builtin_bit_cast(bf16x8, u32x4{zz, zz, zz, zz});
+      f32x16 t = zero16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bf16x8 a = {};
-        if (x_ok) a = __builtin_bit_cast(bf16x8, *(const u32x4*)(xrow + g * 64 + j * 8));
-        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, awq_operand(wv[j]), P, 0, 0, 0);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, xbuf[p % 3][j]);
+        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, awq_operand(wbuf[p][j]), t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, zop, t, 0, 0, 0);
       }
-      const float s = bf16_bits_to_f32(srow[g]);
-      const float zoff = -(128.0f + bf16_bits_to_f32(zrow[g]));
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = (e >> 2) * 8 + h * 4 + (e & 3);
-        if ((e >> 2) * 8 < rows) {  // wave-uniform skip of blocks of rows beyond M
-          const float t = __builtin_fmaf(zoff, xsum[m * G + g], P[e]);
-          acc[e] = __builtin_fmaf(t, s, acc[e]);
-        }
-      }
+      for (int e = 0; e < 16; ++e)
+        if ((e >> 2) * 8 < rows) acc[e] = __builtin_fmaf(t[e], s, acc[e]);  // wave-uniform skip
     }
   }
 
-  const uint16_t* bias = (const uint16_t*)args.bias;
-  const float bv = bias ? bf16_bits_to_f32(bias[nc]) : 0.f;
-  uint16_t* out = (uint16_t*)args.out;
-  if (n < N) {
+  // ---- sum the K-range partials in a fixed order, add bias, store -----------
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = (e >> 2) * 8 + h * 4 + (e & 3);
-      if (m < rows) out[(size_t)(m0 + m) * N + n] = (uint16_t)f32_to_bf16_bits(acc[e] + bv);
+  for (int e = 0; e < 16; ++e) {
+    const int m = (e >> 2) * 8 + h * 4 + (e & 3);
+    part[wave][m][n_l] = acc[e];
+  }
+  __syncthreads();
+  const uint16_t* bias = (const uint16_t*)args.bias;
+  uint16_t* out = (uint16_t*)args.out;
+  for (int o = tid; o < 32 * 32; o += 256) {
+    const int m = o >> 5, c = o & 31;
+    const int col = blockIdx.x * 32 + c;
+    if (m < rows && col < N) {
+      float v = part[0][m][c];
+#pragma unroll
+      for (int w = 1; w < kAwqWaves; ++w) v += part[w][m][c];
+      if (bias) v += bf16_bits_to_f32(bias[col]);
+      out[(size_t)(m0 + m) * N + col] = (uint16_t)f32_to_bf16_bits(v);
     }
   }
 }
 
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream) {
-  const int G = (int)(a.K >> 6);
-  const size_t lds = (size_t)32 * G * sizeof(float);
-  dim3 grid((unsigned)((a.N + 32 * kAwqWaves - 1) / (32 * kAwqWaves)), (unsigned)((a.M + 31) / 32));
-  hipLaunchKernelGGL(awq_w4a16_kernel, grid, dim3(256), lds, stream, a);
+  dim3 grid((unsigned)((a.N + 31) / 32), (unsigned)((a.M + 31) / 32));
+  hipLaunchKernelGGL(awq_w4a16_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -13,15 +13,17 @@ struct QuantActArgs {
   const void* x;          // bf16 [M, K]
   const void* smooth;     // bf16 [K]
   const void* lora_down;  // bf16 [rank, K]
-  void* codes;            // u8 [M, K/2]
+  void* codes;            // u8 [M, K/2] nibbles, or (int4, fp8_codes) E4M3 [M, K]
   void* scales;           // bf16 [M, K/64] | u8 [M, K/16]
   float* lora_act;        // f32 [M, rank]
   int64_t M, K;
   int precision, rank;
+  bool fp8_codes;         // int4 only: write E4M3 bytes in expansion order
 };
 
 struct GemmArgs {
-  const void* act_codes;   // u8 [M, K/2]
+  const void* act_codes;   // int4: E4M3 [M, K] (expansion order), or nibbles [M, K/2]
+                           // when computing partials; nvfp4: nibbles [M, K/2]
   const void* act_scales;  // bf16 [M, K/64] | u8 [M, K/16]
   const float* lora_act;   // f32 [M, rank]
   const void* w_codes;     // u8 [N, K/2]

@@ -21,7 +21,14 @@
 // of the 16x16x32 bf16 matrix instruction used for the low-rank product.  X_hat
 // is split into bf16 hi + lo parts so the low-rank product keeps ~16 bits.
 // The per-wave low-rank partials are summed in LDS in a fixed order
-// (deterministic).  Loads of X are 16 bytes per lane, four chunks in flight.
+// (deterministic).  Loads of X are 16 bytes per lane, several chunks in flight.
+//
+// Output formats: the parity export writes packed nibbles (low nibble = even
+// column).  Inside svdq_w4a4_linear the int4 codes go to the workspace already
+// expanded to E4M3 bytes (the operand format of the int4 product kernel), in
+// "expansion order": each run of 8 columns k0..k0+7 is stored as columns
+// k0+{0,2,4,6,1,3,5,7} -- the order in which the product kernel expands the
+// packed weight codes, so both operands agree column by column.
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -36,14 +43,16 @@ struct K1Prefetch {
   static constexpr int value = RB <= 2 ? 4 : 2;
 };
 
-template <int PREC, int RB>
-__global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(
-    const uint16_t* __restrict__ x, int M, int K, const uint16_t* __restrict__ smooth,
-    const uint16_t* __restrict__ lora_down, uint8_t* __restrict__ codes,
-    void* __restrict__ scales, float* __restrict__ lora_act) {
+template <int PREC, int RB, bool FP8OUT>
+__global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArgs args) {
   extern __shared__ float lds[];
   constexpr int PF = K1Prefetch<RB>::value;
   constexpr int NB = RB > 0 ? RB : 1;
+  const int M = (int)args.M, K = (int)args.K;
+  const uint16_t* __restrict__ x = (const uint16_t*)args.x;
+  const uint16_t* __restrict__ smooth = (const uint16_t*)args.smooth;
+  const uint16_t* __restrict__ lora_down = (const uint16_t*)args.lora_down;
+  uint8_t* __restrict__ codes = (uint8_t*)args.codes;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -58,7 +67,6 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(
   const bool row_ok = row < M;
   const uint16_t* xr = x + (size_t)(row_ok ? row : M - 1) * K;
   const int nchunks = K >> 6;
-  const int K2 = K >> 1;
 
   f32x4 acc[NB];
 #pragma unroll
@@ -90,83 +98,97 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       const int c = base + p * kK1Waves;
-      if (c >= nchunks) break;
-      const int k0 = c * 64 + q * 16;
-      // ---- unpack + smooth ------------------------------------------------
-      float xh[16];
-      const f32x4* mu4 = (const f32x4*)(lds + k0);
+      if (c < nchunks) {
+        const int k0 = c * 64 + q * 16;
+        // ---- unpack + smooth ----------------------------------------------
+        float xh[16];
+        const f32x4* mu4 = (const f32x4*)(lds + k0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = xbuf[p][h][i];
-          const f32x4 mu = mu4[h * 2 + (i >> 1)];
-          xh[h * 8 + 2 * i] = __fmul_rn(bf16_lo(w), mu[(2 * i) & 3]);
-          xh[h * 8 + 2 * i + 1] = __fmul_rn(bf16_hi(w), mu[(2 * i + 1) & 3]);
-        }
-      }
-      float amax = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-
-      // ---- quantize -------------------------------------------------------
-      uint32_t cw0 = 0, cw1 = 0;
-      if constexpr (PREC == kInt4) {
-        amax = wave_max_xor(amax, 16);
-        amax = wave_max_xor(amax, 32);
-        const bool zero = !(amax >= kTiny);
-        const uint32_t sbits = zero ? 0u : f32_to_bf16_bits(__fdiv_rn(amax, 7.0f));
-        const float s = __uint_as_float(sbits << 16);
-        const float inv = zero ? 0.f : __fdiv_rn(1.0f, s);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float t = __fmul_rn(xh[i], inv);
-          const uint32_t mag = (uint32_t)fminf(rintf(fabsf(t)), 7.0f);
-          const uint32_t nib = zero ? 0u : (mag | ((__float_as_uint(t) >> 28) & 8u));
-          if (i < 8) cw0 |= nib << (4 * i);
-          else cw1 |= nib << (4 * (i - 8));
-        }
-        if (row_ok && q == 0) ((uint16_t*)scales)[(size_t)row * (K >> 6) + c] = (uint16_t)sbits;
-      } else {
-        const float sf = __fdiv_rn(amax, 6.0f);
-        const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sf, 448.0f), 0.0f, 0, false) & 0xffu;
-        const float S = __builtin_amdgcn_cvt_f32_fp8((int)s8, 0);
-        const bool zero = !(amax >= kTiny) || S == 0.0f;
-        const float inv = zero ? 0.f : __fdiv_rn(1.0f, S);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float t0 = __fmul_rn(xh[2 * j], inv);
-          const float t1 = __fmul_rn(xh[2 * j + 1], inv);
-          const uint32_t byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t0, t1, 1.0f, 0) & 0xffu;
-          const uint32_t b = zero ? 0u : byte;
-          if (j < 4) cw0 |= b << (8 * j);
-          else cw1 |= b << (8 * (j - 4));
-        }
-        if (row_ok) ((uint8_t*)scales)[(size_t)row * (K >> 4) + 4 * c + q] = (uint8_t)(zero ? 0u : s8);
-      }
-      if (row_ok) *(u32x2*)(codes + (size_t)row * K2 + (k0 >> 1)) = u32x2{cw0, cw1};
-
-      // ---- low-rank down projection (bf16 hi + lo, fp32 accumulate) --------
-      if constexpr (RB > 0) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          bf16x8 ahi, alo;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float v = xh[8 * j + i];
-            const __bf16 h = (__bf16)v;
-            ahi[i] = h;
-            alo[i] = (__bf16)(v - (float)h);
-          }
-#pragma unroll
-          for (int b = 0; b < RB; ++b) {
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, lbuf[p][b][j]);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bop, acc[b], 0, 0, 0);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bop, acc[b], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t w = xbuf[p][h][i];
+            const f32x4 mu = mu4[h * 2 + (i >> 1)];
+            xh[h * 8 + 2 * i] = __fmul_rn(bf16_lo(w), mu[(2 * i) & 3]);
+            xh[h * 8 + 2 * i + 1] = __fmul_rn(bf16_hi(w), mu[(2 * i + 1) & 3]);
           }
         }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+
+        // ---- quantize -----------------------------------------------------
+        uint32_t cw0 = 0, cw1 = 0;
+        if constexpr (PREC == kInt4) {
+          amax = wave_max_xor(amax, 16);
+          amax = wave_max_xor(amax, 32);
+          const bool zero = !(amax >= kTiny);
+          const uint32_t sbits = zero ? 0u : f32_to_bf16_bits(__fdiv_rn(amax, 7.0f));
+          const float inv = zero ? 0.f : __fdiv_rn(1.0f, __uint_as_float(sbits << 16));
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float t = __fmul_rn(xh[i], inv);
+            // |t| < 7.5, so adding 1.5 * 2^23 rounds it to the nearest integer
+            // (ties to even) in the low mantissa bits
+            const uint32_t m = __float_as_uint(__fadd_rn(fabsf(t), 12582912.0f));
+            const uint32_t nib = (m & 7u) | ((__float_as_uint(t) >> 28) & 8u);
+            if (i < 8) cw0 |= nib << (4 * i);
+            else cw1 |= nib << (4 * (i - 8));
+          }
+          cw0 = zero ? 0u : cw0;
+          cw1 = zero ? 0u : cw1;
+          if (row_ok && q == 0) ((uint16_t*)args.scales)[(size_t)row * (K >> 6) + c] = (uint16_t)sbits;
+        } else {
+          const float sf = __fdiv_rn(amax, 6.0f);
+          const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sf, 448.0f), 0.0f, 0, false) & 0xffu;
+          const float S = __builtin_amdgcn_cvt_f32_fp8((int)s8, 0);
+          const bool zero = !(amax >= kTiny) || S == 0.0f;
+          const float inv = zero ? 0.f : __fdiv_rn(1.0f, S);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float t0 = __fmul_rn(xh[2 * j], inv);
+            const float t1 = __fmul_rn(xh[2 * j + 1], inv);
+            const uint32_t byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t0, t1, 1.0f, 0) & 0xffu;
+            if (j < 4) cw0 |= byte << (8 * j);
+            else cw1 |= byte << (8 * (j - 4));
+          }
+          cw0 = zero ? 0u : cw0;
+          cw1 = zero ? 0u : cw1;
+          if (row_ok) ((uint8_t*)args.scales)[(size_t)row * (K >> 4) + 4 * c + q] = (uint8_t)(zero ? 0u : s8);
+        }
+        if (row_ok) {
+          if constexpr (FP8OUT) {
+            uint32_t e0, e1, e2, e3;
+            nibbles_to_e4m3(cw0, kInt4LutLo, kInt4LutHi, e0, e1);
+            nibbles_to_e4m3(cw1, kInt4LutLo, kInt4LutHi, e2, e3);
+            *(u32x4*)(codes + (size_t)row * K + k0) = u32x4{e0, e1, e2, e3};
+          } else {
+            *(u32x2*)(codes + (size_t)row * (K >> 1) + (k0 >> 1)) = u32x2{cw0, cw1};
+          }
+        }
+
+        // ---- low-rank down projection (bf16 hi + lo, fp32 accumulate) ------
+        if constexpr (RB > 0) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            bf16x8 ahi, alo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float v = xh[8 * j + i];
+              const __bf16 hb = (__bf16)v;
+              ahi[i] = hb;
+              alo[i] = (__bf16)(v - (float)hb);
+            }
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+              const bf16x8 bop = __builtin_bit_cast(bf16x8, lbuf[p][b][j]);
+              acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bop, acc[b], 0, 0, 0);
+              acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bop, acc[b], 0, 0, 0);
+            }
+          }
+        }
+        issue(p, c + PF * kK1Waves);
       }
-      issue(p, c + PF * kK1Waves);
     }
   }
 
@@ -187,42 +209,43 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(
 #pragma unroll
       for (int w = 0; w < kK1Waves; ++w) s += red[(w * kK1Rows + rr) * rank + cc];
       const int grow = blockIdx.x * kK1Rows + rr;
-      if (grow < M) lora_act[(size_t)grow * rank + cc] = s;
+      if (grow < M) args.lora_act[(size_t)grow * rank + cc] = s;
     }
   }
 }
 
-template <int PREC, int RB>
+template <int PREC, int RB, bool FP8OUT>
 static hipError_t launch_k1(const QuantActArgs& a, hipStream_t stream) {
   const int rank = RB * 16;
   size_t lds = (size_t)a.K * sizeof(float);
   const size_t red = (size_t)kK1Waves * kK1Rows * rank * sizeof(float);
   if (red > lds) lds = red;
-  dim3 grid((unsigned)((a.M + kK1Rows - 1) / kK1Rows));
-  hipLaunchKernelGGL((quantize_act_lora_down_kernel<PREC, RB>), grid, dim3(512), lds, stream,
-                     (const uint16_t*)a.x, (int)a.M, (int)a.K, (const uint16_t*)a.smooth,
-                     (const uint16_t*)a.lora_down, (uint8_t*)a.codes, a.scales, a.lora_act);
+  const unsigned blocks = (unsigned)((a.M + kK1Rows - 1) / kK1Rows);
+  hipLaunchKernelGGL((quantize_act_lora_down_kernel<PREC, RB, FP8OUT>), dim3(blocks), dim3(512), lds,
+                     stream, a);
   return hipGetLastError();
 }
 
-template <int PREC>
+template <int PREC, bool FP8OUT>
 static hipError_t dispatch_rank(const QuantActArgs& a, hipStream_t s) {
   switch (a.rank / 16) {
-    case 0: return launch_k1<PREC, 0>(a, s);
-    case 1: return launch_k1<PREC, 1>(a, s);
-    case 2: return launch_k1<PREC, 2>(a, s);
-    case 3: return launch_k1<PREC, 3>(a, s);
-    case 4: return launch_k1<PREC, 4>(a, s);
-    case 5: return launch_k1<PREC, 5>(a, s);
-    case 6: return launch_k1<PREC, 6>(a, s);
-    case 7: return launch_k1<PREC, 7>(a, s);
-    case 8: return launch_k1<PREC, 8>(a, s);
+    case 0: return launch_k1<PREC, 0, FP8OUT>(a, s);
+    case 1: return launch_k1<PREC, 1, FP8OUT>(a, s);
+    case 2: return launch_k1<PREC, 2, FP8OUT>(a, s);
+    case 3: return launch_k1<PREC, 3, FP8OUT>(a, s);
+    case 4: return launch_k1<PREC, 4, FP8OUT>(a, s);
+    case 5: return launch_k1<PREC, 5, FP8OUT>(a, s);
+    case 6: return launch_k1<PREC, 6, FP8OUT>(a, s);
+    case 7: return launch_k1<PREC, 7, FP8OUT>(a, s);
+    case 8: return launch_k1<PREC, 8, FP8OUT>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream) {
-  return a.precision == kInt4 ? dispatch_rank<kInt4>(a, stream) : dispatch_rank<kNvfp4>(a, stream);
+  if (a.precision == kInt4)
+    return a.fp8_codes ? dispatch_rank<kInt4, true>(a, stream) : dispatch_rank<kInt4, false>(a, stream);
+  return dispatch_rank<kNvfp4, false>(a, stream);
 }
 
 }  // namespace svdq

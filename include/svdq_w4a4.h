@@ -52,10 +52,11 @@ enum svdq_status {
   SVDQ_EDEVICE = -5       /* HIP runtime error (no device, launch failure)     */
 };
 
-/* Bytes of scratch svdq_w4a4_linear needs: activation codes [M, K/2],
- * activation scales [M, K/G] (bf16 for int4, E4M3 bytes for nvfp4) and the
- * low-rank activations [M, rank] fp32, each 256-byte aligned.  Returns 0 for
- * arguments svdq_w4a4_linear would reject. */
+/* Bytes of scratch svdq_w4a4_linear needs: activation codes (int4: M*K bytes,
+ * kept as 8-bit operands; nvfp4: M*K/2), activation scales [M, K/G] (bf16 for
+ * int4, E4M3 bytes for nvfp4) and the low-rank activations [M, rank] fp32,
+ * each 256-byte aligned.  Returns 0 for arguments svdq_w4a4_linear would
+ * reject. */
 size_t svdq_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision,
                                  int group_size, int rank);
 
@@ -87,6 +88,25 @@ int svdq_w4a4_linear(const void* x, int64_t M, int64_t K, int64_t N,
                      const void* smooth, const void* lora_down, const void* lora_up,
                      const void* bias, int precision, int group_size, int rank,
                      void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* svdq_w4a4_linear in two phases, for callers that reuse one quantized input
+ * (or time the two kernels apart):
+ *   svdq_w4a4_quantize  smoothing, activation quantization and the low-rank
+ *                       down projection of x into `workspace`;
+ *   svdq_w4a4_gemm      the 4-bit product, group scales, low-rank up
+ *                       projection, bias and bf16 store, reading `workspace`.
+ * The workspace contents between the two calls are private to the library
+ * (not the parity-export formats).  Calling quantize then gemm on one stream
+ * gives bit-identical results to svdq_w4a4_linear.  Arguments and rules as
+ * for svdq_w4a4_linear; the gemm must use the M, K, precision, group_size and
+ * rank of the quantize call that filled the workspace. */
+int svdq_w4a4_quantize(const void* x, int64_t M, int64_t K, const void* smooth,
+                       const void* lora_down, int precision, int group_size, int rank,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int svdq_w4a4_gemm(const void* workspace, size_t workspace_bytes, int64_t M, int64_t K,
+                   int64_t N, const void* packed_w, const void* wscales, float wtscale,
+                   const void* lora_up, const void* bias, int precision, int group_size,
+                   int rank, void* out, void* stream);
 
 /* AWQ W4A16 linear ("Supported quantization types": awq_w4a16, int4, group 64).
  *

@@ -135,10 +135,11 @@ def test_wtscale_rules(L):
 
 def test_workspace_size(L):
     M, K, N = 300, 512, 320
-    for prec, g, sb in ((0, 64, 2 * 8), (1, 16, 32)):
+    # int4 codes are kept as 8-bit operands (M*K bytes), nvfp4 as nibbles (M*K/2)
+    for prec, g, cb, sb in ((0, 64, M * K, 2 * 8), (1, 16, M * K // 2, 32)):
         need = L.svdq_w4a4_workspace_bytes(M, K, N, prec, g, 32)
         rnd = lambda v: (v + 255) // 256 * 256
-        assert need == rnd(M * K // 2) + rnd(M * sb) + rnd(M * 32 * 4)
+        assert need == rnd(cb) + rnd(M * sb) + rnd(M * 32 * 4)
         a = Args(M=M, K=K, N=N, precision=prec, group=g)
         assert a.call(L, wsb=need - 1) == EWS
         assert a.call(L, wsb=need) == OK

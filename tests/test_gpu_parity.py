@@ -237,6 +237,21 @@ def test_linear_deterministic_with_poisoned_workspace(ragged):
         assert np.array_equal(y1, y2)
 
 
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_two_phase_entry_matches_linear(ragged, precision):
+    # quantize + gemm as two calls reproduce the fused call bit for bit
+    x, w, b = ragged
+    lay = prepared(x, w, b, precision, 32, smooth="calibrated")
+    layer = bq.SVDQLinear.from_numpy(lay)
+    xd = dev_bf16(x)
+    ws = torch.empty(layer.workspace_bytes(x.shape[0]), dtype=torch.uint8, device="cuda")
+    bq.svdq_w4a4_quantize(xd, layer, ws)
+    y2 = bq.svdq_w4a4_gemm(ws, x.shape[0], layer)
+    y1 = layer(xd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y1), host_bits(y2))
+
+
 # ------------------------------------------------------------------ AWQ
 def run_awq(x_bits, lay):
     layer = bq.AWQLinear.from_numpy(lay)
