@@ -6,142 +6,295 @@
 // format: unsigned codes q (0..15), per-group bf16 scale s and integer
 // zero-point z, W = (q - z) s;  Y = X W^T + bias with fp32 accumulation.
 //
-// gfx950 design -- bandwidth-bound: 4.5 bits per weight streamed once per 32
+// gfx950 design -- bandwidth-bound: 4.5 bits per weight streamed once per 16
 // rows of X.
-// * A workgroup owns 32 weight rows (output columns); its 4 waves split K in
-//   four contiguous ranges, so 4 x N/32 waves stream independently.  Each lane
-//   issues all of its 16-byte code loads (one per group in its range) before
-//   computing, so the whole weight matrix is in flight at once.
-// * Lane (n = lane%32, h = lane/32) covers columns 64g + 32h .. +31 of weight
-//   row n: four 32x32x16 bf16 matrix instructions per group, each mixing only
-//   columns of that group.
+// * A workgroup owns 32 weight rows (output columns) and 16 rows of X; its 4
+//   waves split K into four contiguous group ranges.  Every wave issues all the
+//   code, scale and zero-point loads of its range before computing, and the
+//   register budget (<= 168 VGPRs, 3 waves per SIMD) keeps every workgroup of
+//   an N = 18432 layer resident at once, so the whole weight matrix is in
+//   flight together and no second round of workgroups forms a tail.
+// * Matrix instruction 16x16x32 bf16 (D = 16 rows of X x 16 weight rows): it
+//   consumes 512 weights per 4 passes, half the matrix-core time of the 32x32
+//   shape per weight, which matters at M <= 16 where most of D is padding.
+//   Lane (c = lane%16, kq = lane/16) holds, per group and 32-wide k step s,
+//   the k values 16 kq + 8 s + 0..7 of weight row c (4 code bytes, so one
+//   8-byte load covers a group) and the same k of X row c.
 // * Codes become bf16 operands 128 + q (0x4300 | q is the bit pattern of
-//   128 + q) with one v_perm and one OR per pair.  A second operand set holds
+//   128 + q) with one v_perm and one OR per pair.  A second operand holds
 //   -(128 + z) in every slot, so the same accumulator collects
-//   sum_k x (128 + q) - sum_k x (128 + z) = sum_k x (q - z) exactly in the
-//   matrix unit (exact bf16 products, fp32 sums), and the scale needs one FMA
-//   per output: acc += t * s.
-// * Rows of X beyond M are zero; the epilogue skips blocks of rows beyond M.
-//   The four K-range partials are summed in LDS in a fixed order.
+//   sum_k x (128 + q) - sum_k x (128 + z) = sum_k x (q - z): exact bf16
+//   products, fp32 sums; the scale costs one FMA per output: acc += t * s.
+// * Rows of X beyond M are zero (their loads are masked off).  The four
+//   K-range partials are summed in LDS in a fixed order.
 
 #include "device_common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace svdq {
 
-constexpr int kAwqWaves = 4;     // K ranges per workgroup
-constexpr int kAwqMaxG = 16;     // groups per wave held in registers at once
+constexpr int kAwqWaves = 4;       // K ranges per workgroup
+constexpr int kAwqStepG = 4;       // groups per step: 128 contiguous bytes of each weight row
+constexpr int kAwqRowPitch = 144;  // LDS bytes per staged weight row (128 + 16 pad)
+constexpr int kAwqXPitch = 528;    // LDS bytes per staged X row (256 bf16 + 16 pad)
 
+// Operand order within every 8 consecutive k: {0, 2, 4, 6, 1, 3, 5, 7}.  Codes
+// reach it with one v_perm per pair of codes (bytes 0x43 from a constant
+// give the bf16 pattern 0x4300 | q of 128 + q); X is put in the same order
+// once, when a step of X is staged in LDS.
 __device__ __forceinline__ bf16x8 awq_operand(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;          // nibbles 0, 2, 4, 6
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // nibbles 1, 3, 5, 7
+  constexpr uint32_t kHi = 0x43434343u;
+  const uint32_t lo = w & 0x0F0F0F0Fu;          // codes k0, k2, k4, k6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // codes k1, k3, k5, k7
   u32x4 r;
-  r[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;  // (n0, n1)
-  r[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;  // (n2, n3)
-  r[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u;  // (n4, n5)
-  r[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u;  // (n6, n7)
+  r[0] = __builtin_amdgcn_perm(kHi, lo, 0x04010400u);  // (k0, k2)
+  r[1] = __builtin_amdgcn_perm(kHi, lo, 0x04030402u);  // (k4, k6)
+  r[2] = __builtin_amdgcn_perm(kHi, hi, 0x04010400u);  // (k1, k3)
+  r[3] = __builtin_amdgcn_perm(kHi, hi, 0x04030402u);  // (k5, k7)
   return __builtin_bit_cast(bf16x8, r);
 }
 
-__global__ __launch_bounds__(256) void awq_w4a16_kernel(AwqArgs args) {
-  __shared__ float part[kAwqWaves][32][33];
+// 8 bf16 of X in k order (pairs (0,1) (2,3) (4,5) (6,7)) -> operand order
+__device__ __forceinline__ u32x4 awq_x_order(u32x4 v) {
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);  // (x0, x2)
+  r[1] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);  // (x4, x6)
+  r[2] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);  // (x1, x3)
+  r[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);  // (x5, x7)
+  return r;
+}
+
+// MT: rows of X per workgroup (1, 2, 4 or 16); D: steps in flight per wave.
+//
+// Dynamic LDS: the workgroup's scale table float2 [32 rows][G] holding
+// (s, -s (128 + z)) per weight row and group, then per wave a staged step of
+// codes [32 rows][kAwqRowPitch] and of X [MT rows][kAwqXPitch].
+template <int MT, int D, bool WIDE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 16 ? 2 : 3, 3)))
+void awq_w4a16_kernel(AwqArgs args) {
+  constexpr int XV = MT == 1 ? 1 : MT / 2;  // X loads per lane and step (8 bytes if MT == 1, else 16)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ float part[kAwqWaves][16][33];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int M = (int)args.M, K = (int)args.K, N = (int)args.N;
   const int G = K >> 6;
   const int K2 = K >> 1;
-  const int m0 = blockIdx.y * 32;
-  const int rows = min(32, M - m0);
-  const uint16_t* __restrict__ x = (const uint16_t*)args.x;
+  const int m0 = blockIdx.y * MT;
+  const int rows = min(MT, M - m0);
+  const int n0 = blockIdx.x * 32;
 
-  const int n_l = lane & 31;
-  const int h = lane >> 5;
-  const int n = blockIdx.x * 32 + n_l;
-  const int nc = min(n, N - 1);
-  // this wave's contiguous range of groups
-  const int gpw = (G + kAwqWaves - 1) / kAwqWaves;
+  float2* stab = (float2*)smem;
+  uint8_t* ws = smem + (size_t)32 * G * 8 + (size_t)wave * (32 * kAwqRowPitch + MT * kAwqXPitch);
+  uint8_t* xs = ws + 32 * kAwqRowPitch;
+
+  const int c = lane & 15;
+  const int kq = lane >> 4;
+  // this wave's contiguous range of groups, whole steps except at the end of K
+  const int gpw = kAwqStepG * ((G + kAwqStepG * kAwqWaves - 1) / (kAwqStepG * kAwqWaves));
   const int g0 = min(G, wave * gpw);
   const int g1 = min(G, g0 + gpw);
-  const uint8_t* wrow = (const uint8_t*)args.w_codes + (size_t)nc * K2 + h * 16;
-  const uint16_t* srow = (const uint16_t*)args.scales + (size_t)nc * G;
-  const uint16_t* zrow = (const uint16_t*)args.zeros + (size_t)nc * G;
-  const bool x_ok = n_l < rows;
-  const uint16_t* xrow = x + (size_t)(m0 + (x_ok ? n_l : 0)) * K + h * 32;
+  const int nsteps = (g1 - g0 + kAwqStepG - 1) / kAwqStepG;
 
-  f32x16 acc = {};
-  const f32x16 zero16 = {};
-  for (int gb = g0; gb < g1; gb += kAwqMaxG) {
-    // every load of this batch is issued before any use, so only one memory
-    // latency is exposed per batch (codes, scales and zero-points)
-    u32x4 wbuf[kAwqMaxG];
-    uint16_t sbuf[kAwqMaxG], zbuf[kAwqMaxG];
+  // ---- scale table: item (row r, group pair p) for r < 32, p < G/2 ----------
+  const uint32_t* s32 = (const uint32_t*)args.scales + (size_t)n0 * (G / 2);
+  const uint32_t* z32 = (const uint32_t*)args.zeros + (size_t)n0 * (G / 2);
+  const int items = 16 * G;  // 32 rows x G/2 pairs, contiguous in both tables
+  uint32_t sraw[4], zraw[4];
+  auto load_items = [&](int base) {  // unconditional (clamped) loads keep the wait counts exact
 #pragma unroll
-    for (int p = 0; p < kAwqMaxG; ++p)
-      if (gb + p < g1) wbuf[p] = *(const u32x4*)(wrow + (gb + p) * 32);
+    for (int u = 0; u < 4; ++u) {
+      const int it = min(base + tid + 256 * u, items - 1);
+      sraw[u] = s32[it];
+      zraw[u] = z32[it];
+    }
+  };
+  // (s, -s (128 + z)) per row and group; both factors of the product are
+  // exact (8-bit significands), so the fp32 product is exact
+  auto store_items = [&](int base) {
 #pragma unroll
-    for (int p = 0; p < kAwqMaxG; ++p)
-      if (gb + p < g1) {
-        sbuf[p] = srow[gb + p];
-        zbuf[p] = zrow[gb + p];
+    for (int u = 0; u < 4; ++u) {
+      const int it = base + tid + 256 * u;
+      if (it < items) {
+        const float sl = bf16_lo(sraw[u]), sh = bf16_hi(sraw[u]);
+        const float zl = bf16_lo(zraw[u]), zh = bf16_hi(zraw[u]);
+        *(float4*)(stab + 2 * it) = float4{sl, -sl * (128.0f + zl), sh, -sh * (128.0f + zh)};
       }
-    // rows of X for the A operand: 64 bytes per lane and group, two groups ahead
-    u32x4 xbuf[3][4];
-    auto load_x = [&](int slot, int g) {
+    }
+  };
+  load_items(0);
+
+  // codes: lane l streams 16 bytes (half of group (l%8)/2 of the step) of
+  // weight rows n0 + l/8 + 8j, j = 0..3 -- 128 contiguous bytes per row
+  const int q8 = lane & 7;
+  const uint8_t* wstream = (const uint8_t*)args.w_codes + (size_t)(n0 + (lane >> 3)) * K2 + (q8 & 1) * 16;
+  // X: MT rows x 256 k of the step; with MT == 1 lane l holds k 4l..4l+3,
+  // else load v covers rows 2v + l/32, k 8 (l%32) .. +7.  Rows beyond M read
+  // row M - 1: each output row depends on its own X row only, and rows
+  // beyond M are never stored.
+  const uint16_t* xbase = (const uint16_t*)args.x + (size_t)m0 * K;
+
+  // D steps in flight; all loads of a step (codes and X) are issued together,
+  // so the in-order memory counter releases whole steps.  Past the wave's
+  // range (a partial last step, or the prologue of a short range) the loads
+  // re-read the last valid group.
+  typedef typename std::conditional<MT == 1, u32x2, u32x4>::type XVec;
+  u32x4 wr[D][4];
+  XVec xr[D][XV];
+  auto issue = [&](int slot, int step) {
+    const int gs = g0 + step * kAwqStepG;
+    const int gw = min(gs + (q8 >> 1), g1 - 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xbuf[slot][j] = (x_ok && g < g1) ? *(const u32x4*)(xrow + g * 64 + j * 8) : u32x4{0u, 0u, 0u, 0u};
-    };
-    load_x(0, gb);
-    load_x(1, gb + 1);
+    for (int j = 0; j < 4; ++j)
+      wr[slot][j] = *(const u32x4*)(wstream + (size_t)(8 * j) * K2 + (size_t)gw * 32);
+    if constexpr (MT == 1) {
+      const int g = min(gs + (lane >> 4), g1 - 1);
+      xr[slot][0] = *(const u32x2*)(xbase + (size_t)g * 64 + (lane & 15) * 4);
+    } else {
 #pragma unroll
-    for (int p = 0; p < kAwqMaxG; ++p) {
-      const int g = gb + p;
-      if (g >= g1) continue;
-      if (p + 2 < kAwqMaxG) load_x((p + 2) % 3, g + 2);
-      const float s = bf16_bits_to_f32(sbuf[p]);
-      const uint32_t zb = f32_to_bf16_bits(-(128.0f + bf16_bits_to_f32(zbuf[p])));  // exact
-      const uint32_t zz = zb | (zb << 16);
-      const bf16x8 zop = __builtin_bit_cast(bf16x8, u32x4{zz, zz, zz, zz});
-      f32x16 t = zero16;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, xbuf[p % 3][j]);
-        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, awq_operand(wbuf[p][j]), t, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, zop, t, 0, 0, 0);
+      for (int v = 0; v < XV; ++v) {
+        const int r = min(2 * v + (lane >> 5), rows - 1);
+        const int g = min(gs + ((lane & 31) >> 3), g1 - 1);
+        xr[slot][v] = *(const u32x4*)(xbase + (size_t)r * K + (size_t)g * 64 + (lane & 7) * 8);
       }
+    }
+  };
+  // always in bounds (clamped to the last group), so issued unconditionally:
+  // straight-line code keeps the compiler's memory-counter waits exact
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if ((e >> 2) * 8 < rows) acc[e] = __builtin_fmaf(t[e], s, acc[e]);  // wave-uniform skip
+  for (int d = 0; d < D; ++d) issue(d, d);
+
+  store_items(0);
+  if constexpr (WIDE) {  // K > 4096: the table takes more than one batch
+    for (int base = 1024; base < items; base += 1024) {
+      load_items(base);
+      store_items(base);
+    }
+  }
+  lds_barrier();  // the code and X prefetches stay in flight
+
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  f32x4 accA = {}, accB = {};
+  auto group = [&](int g, int i) {
+    const f32x4 zero4 = {};
+    // operands from this wave's LDS rows: codes 8 bytes of rows c and 16 + c,
+    // X 32 bytes of row min(c, MT - 1)
+    const u32x2 wa = *(const u32x2*)(ws + c * kAwqRowPitch + i * 32 + kq * 8);
+    const u32x2 wb = *(const u32x2*)(ws + (16 + c) * kAwqRowPitch + i * 32 + kq * 8);
+    const uint8_t* xp = xs + min(c, MT - 1) * kAwqXPitch + i * 128 + kq * 32;
+    const bf16x8 x0 = __builtin_bit_cast(bf16x8, *(const u32x4*)xp);
+    const bf16x8 x1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xp + 16));
+    const float2 pa = stab[c * G + g];
+    const float2 pb = stab[(16 + c) * G + g];
+    // k step 0 uses code bytes 0..3 (k = 16 kq + 0..7), step 1 bytes 4..7
+    f32x4 tA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, awq_operand(wa[0]), zero4, 0, 0, 0);
+    f32x4 tB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, awq_operand(wb[0]), zero4, 0, 0, 0);
+    f32x4 xsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, ones, zero4, 0, 0, 0);
+    tA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, awq_operand(wa[1]), tA, 0, 0, 0);
+    tB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, awq_operand(wb[1]), tB, 0, 0, 0);
+    xsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, ones, xsum, 0, 0, 0);
+    // sum_k x (q - z) s = s sum_k x (128 + q) - s (128 + z) sum_k x.  D row
+    // kq * 4 + j sits in register j, so with MT < 4 only registers j < MT
+    // carry rows of X (in lanes kq == 0); the others are never stored.
+#pragma unroll
+    for (int j = 0; j < (MT < 4 ? MT : 4); ++j) {
+      accA[j] = __builtin_fmaf(tA[j], pa.x, accA[j]);
+      accB[j] = __builtin_fmaf(tB[j], pb.x, accB[j]);
+      accA[j] = __builtin_fmaf(xsum[j], pa.y, accA[j]);
+      accB[j] = __builtin_fmaf(xsum[j], pb.y, accB[j]);
+    }
+  };
+
+  // move a step's codes and X into this wave's LDS rows (the wave's own
+  // LDS accesses execute in order, so the previous step's reads are done)
+  auto stage = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(u32x4*)(ws + (8 * j + (lane >> 3)) * kAwqRowPitch + q8 * 16) = wr[slot][j];
+    if constexpr (MT == 1) {
+      // lanes 2t, 2t + 1 hold k 8t..8t+3 and 8t+4..8t+7
+      const u32x2 v = xr[slot][0];
+      const uint32_t even = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);  // (x0, x2) / (x4, x6)
+      const uint32_t odd = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);   // (x1, x3) / (x5, x7)
+      uint32_t* dst = (uint32_t*)(xs + (lane >> 1) * 16 + (lane & 1) * 4);
+      dst[0] = even;
+      dst[2] = odd;
+    } else {
+#pragma unroll
+      for (int v = 0; v < XV; ++v)
+        *(u32x4*)(xs + (2 * v + (lane >> 5)) * kAwqXPitch + (lane & 31) * 16) = awq_x_order(xr[slot][v]);
+    }
+  };
+
+  if (nsteps > 0) {
+    int s0 = 0;
+    // steady state: whole steps only, every slot refilled right after use
+    for (; s0 + 2 * D <= nsteps; s0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        stage(d);
+        const int gs = g0 + (s0 + d) * kAwqStepG;
+#pragma unroll
+        for (int i = 0; i < kAwqStepG; ++i) group(gs + i, i);
+        issue(d, s0 + D + d);
+      }
+    }
+    // tail: fewer than 2 D steps left, the first D of them in flight
+#pragma unroll
+    for (int d = 0; d < 2 * D; ++d) {
+      const int step = s0 + d;
+      if (step < nsteps) {
+        stage(d % D);
+        const int gs = g0 + step * kAwqStepG;
+#pragma unroll
+        for (int i = 0; i < kAwqStepG; ++i)
+          if (gs + i < g1) group(gs + i, i);
+        if (d < D && step + D < nsteps) issue(d, step + D);
+      }
     }
   }
 
   // ---- sum the K-range partials in a fixed order, add bias, store -----------
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int m = (e >> 2) * 8 + h * 4 + (e & 3);
-    part[wave][m][n_l] = acc[e];
+  for (int j = 0; j < 4; ++j) {
+    part[wave][kq * 4 + j][c] = accA[j];
+    part[wave][kq * 4 + j][16 + c] = accB[j];
   }
   __syncthreads();
   const uint16_t* bias = (const uint16_t*)args.bias;
   uint16_t* out = (uint16_t*)args.out;
-  for (int o = tid; o < 32 * 32; o += 256) {
-    const int m = o >> 5, c = o & 31;
-    const int col = blockIdx.x * 32 + c;
-    if (m < rows && col < N) {
-      float v = part[0][m][c];
+  for (int o = tid; o < 16 * 32; o += 256) {
+    const int m = o >> 5, cc = o & 31;
+    if (m < rows) {
+      float v = part[0][m][cc];
 #pragma unroll
-      for (int w = 1; w < kAwqWaves; ++w) v += part[w][m][c];
-      if (bias) v += bf16_bits_to_f32(bias[col]);
-      out[(size_t)(m0 + m) * N + col] = (uint16_t)f32_to_bf16_bits(v);
+      for (int w = 1; w < kAwqWaves; ++w) v += part[w][m][cc];
+      if (bias) v += bf16_bits_to_f32(bias[n0 + cc]);
+      out[(size_t)(m0 + m) * N + n0 + cc] = (uint16_t)f32_to_bf16_bits(v);
     }
   }
 }
 
-hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)((a.N + 31) / 32), (unsigned)((a.M + 31) / 32));
-  hipLaunchKernelGGL(awq_w4a16_kernel, grid, dim3(256), 0, stream, a);
+template <int MT, int D>
+static hipError_t launch_awq_mt(const AwqArgs& a, hipStream_t stream) {
+  const int G = (int)(a.K / 64);
+  const size_t lds = (size_t)32 * G * 8 + (size_t)kAwqWaves * (32 * kAwqRowPitch + MT * kAwqXPitch);
+  dim3 grid((unsigned)(a.N / 32), (unsigned)((a.M + MT - 1) / MT));
+  if (G <= 64)
+    hipLaunchKernelGGL((awq_w4a16_kernel<MT, D, false>), grid, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL((awq_w4a16_kernel<MT, D, true>), grid, dim3(256), lds, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream) {
+  if (a.M == 1) return launch_awq_mt<1, 2>(a, stream);
+  if (a.M == 2) return launch_awq_mt<2, 2>(a, stream);
+  if (a.M <= 4) return launch_awq_mt<4, 2>(a, stream);
+  return launch_awq_mt<16, 2>(a, stream);
 }
 
 }  // namespace svdq

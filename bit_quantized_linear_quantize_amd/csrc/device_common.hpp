@@ -44,6 +44,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for the
+// wave's outstanding global loads (its release fence covers global memory),
+// which would stall a software pipeline whose prefetches are still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

@@ -270,6 +270,18 @@ def test_awq_ragged(M):
     assert_output(run_awq(x, lay), L.awq_linear_ref(x, lay), f"awq ragged M={M}")
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 128, 64), (3, 640, 128), (4, 1152, 192), (5, 8192, 64),
+                                   (2, 16384, 64), (17, 3200, 128)])
+def test_awq_shapes(M, K, N):
+    # X-row tiles of 1, 2, 4 and 16 rows; K from one group pair to the maximum
+    # (a scale table wider than one load batch); partial 4-group steps
+    rng = np.random.default_rng(K + M)
+    w = rng.standard_normal((N, K)) * 0.02
+    lay = L.prepare_awq_layer(w, S.bias(N, rng))
+    x = S.activations(M, K, 0, rng)
+    assert_output(run_awq(x, lay), L.awq_linear_ref(x, lay), f"awq M={M} K={K} N={N}")
+
+
 def test_awq_config3():
     c = S.config3()
     lay = L.prepare_awq_layer(c["w"], c["bias"])
