@@ -131,7 +131,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first; about 0.1 s, enough for the GPU clock to settle")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the nvfp4 and AWQ legs")
     ap.add_argument("--only", choices=sorted(ONLY_LEGS),
