@@ -142,8 +142,9 @@ def main():
         run_only(args.only, args.steps)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the single-GPU kernel path only: this library has no multi-GPU "
-              "path (sharding is described in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures the single-GPU kernel path only: the library has no multi-GPU "
+              "path (it would shard along tokens with replicated weights); run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

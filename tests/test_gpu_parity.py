@@ -1,12 +1,16 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Bars (the bf16 output reading is derived in the design doc):
+Bars:
 * activation codes, activation scales and per-group integer partials: bit-exact;
 * low-rank activations (fp32): max |err| <= 1e-4 * max |ref|;
 * bf16 output Y against the fp64 oracle:
-    max(|err| - half a bf16 ulp of Y_ref) <= 1e-2 * RMS(Y_ref)   (the final
-    rounding to the bf16 output dtype is not charged to the kernel), and
+    max(|err| - half a bf16 ulp of Y_ref) <= 1e-2 * RMS(Y_ref), and
     mean relative error sum|err| / sum|Y_ref| <= 2e-3 (rounding included).
+  The first bar does not charge the final rounding to the bf16 output dtype
+  to the kernel: with outlier channels |Y| reaches many times RMS(Y), and half
+  a bf16 ulp of such an element alone exceeds 1e-2 * RMS(Y), so no bf16 result
+  could meet a bound on the raw error.  What remains (fp32 accumulation order,
+  the bf16 hi/lo split of the low-rank operands) must stay within the bound.
 """
 
 import numpy as np
