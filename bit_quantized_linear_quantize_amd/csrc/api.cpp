@@ -98,22 +98,18 @@ int check_svdq_kind(int precision, int group_size, int rank) {
   return SVDQ_OK;
 }
 
-size_t act_scale_bytes(int64_t M, int64_t K, int precision) {
-  return precision == SVDQ_INT4 ? size_t(M) * size_t(K / 64) * 2 : size_t(M) * size_t(K / 16);
-}
 size_t w_scale_bytes(int64_t N, int64_t K, int precision) {
   return precision == SVDQ_INT4 ? size_t(N) * size_t(K / 64) * 2 : size_t(N) * size_t(K / 16);
 }
 
-// int4 activation codes are kept as E4M3 bytes (the product kernel's operand
-// format); nvfp4 codes as packed nibbles.
-size_t act_code_bytes(int64_t M, int64_t K, int precision) {
-  return precision == SVDQ_INT4 ? size_t(M) * size_t(K) : size_t(M) * size_t(K / 2);
-}
-
+// Workspace of svdq_w4a4_linear (each part 256-byte aligned):
+//   act_f16    f16 [M, K]   dequantized activations, the product operand
+//   row_scale  int4 only: f32 [M], the power of two factored out of each row
+//   lora_act   f32 [M, rank]
 size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
-  return round_up(act_code_bytes(M, K, precision)) + round_up(act_scale_bytes(M, K, precision)) +
-         round_up(size_t(M) * size_t(rank) * 4);
+  size_t b = round_up(size_t(M) * size_t(K) * 2);
+  if (precision == SVDQ_INT4) b += round_up(size_t(M) * 4);
+  return b + round_up(size_t(M) * size_t(rank) * 4);
 }
 
 int validate_svdq(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
@@ -179,25 +175,29 @@ int launch_status(hipError_t e, const char* what) {
 }
 
 struct Carve {
-  uint8_t* codes;   // int4: E4M3 bytes [M, K]; nvfp4: nibbles [M, K/2]
-  uint8_t* scales;  // bf16 [M, K/64] | u8 [M, K/16]
-  float* lora_act;  // f32 [M, rank]
+  uint8_t* act_f16;   // f16 [M, K]
+  float* row_scale;   // int4: f32 [M]; else null
+  float* lora_act;    // f32 [M, rank]
 };
 
 Carve carve(void* workspace, int64_t M, int64_t K, int precision) {
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  Carve c;
-  c.codes = ws;
-  c.scales = c.codes + round_up(act_code_bytes(M, K, precision));
-  c.lora_act = reinterpret_cast<float*>(c.scales + round_up(act_scale_bytes(M, K, precision)));
+  uint8_t* p = static_cast<uint8_t*>(workspace);
+  Carve c{};
+  c.act_f16 = p;
+  p += round_up(size_t(M) * size_t(K) * 2);
+  if (precision == SVDQ_INT4) {
+    c.row_scale = reinterpret_cast<float*>(p);
+    p += round_up(size_t(M) * 4);
+  }
+  c.lora_act = reinterpret_cast<float*>(p);
   return c;
 }
 
 int launch_quantize(const void* x, int64_t M, int64_t K, const void* smooth, const void* lora_down,
                     int precision, int rank, void* workspace, hipStream_t s) {
   const Carve c = carve(workspace, M, K, precision);
-  svdq::QuantActArgs qa{x, smooth, lora_down, c.codes, c.scales, c.lora_act, M, K, precision, rank,
-                        precision == SVDQ_INT4};
+  svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, c.lora_act, c.act_f16, c.row_scale,
+                        M, K, precision, rank};
   return launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
 }
 
@@ -205,7 +205,7 @@ int launch_gemm(const void* workspace, int64_t M, int64_t K, int64_t N, const vo
                 const void* wscales, float wtscale, const void* lora_up, const void* bias, int precision,
                 int rank, void* out, hipStream_t s) {
   const Carve c = carve(const_cast<void*>(workspace), M, K, precision);
-  svdq::GemmArgs ga{c.codes, c.scales, c.lora_act, packed_w, wscales, lora_up, bias, out, nullptr,
+  svdq::GemmArgs ga{c.act_f16, c.row_scale, c.lora_act, packed_w, wscales, lora_up, bias, out, nullptr,
                     wtscale, M, K, N, precision, rank};
   return launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up launch");
 }
@@ -347,8 +347,8 @@ int svdq_w4a4_quantize_act(const void* x, int64_t M, int64_t K, const void* smoo
     if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
   rc = check_device_arch();
   if (rc) return rc;
-  svdq::QuantActArgs qa{x, smooth, lora_down, codes_out, scales_out, lora_act_out, M, K, precision, rank,
-                        false};
+  svdq::QuantActArgs qa{x, smooth, lora_down, codes_out, scales_out, lora_act_out, nullptr, nullptr, M, K,
+                        precision, rank};
   return launch_status(svdq::launch_quantize_act(qa, static_cast<hipStream_t>(stream)),
                        "quantize_act_lora_down launch");
 }

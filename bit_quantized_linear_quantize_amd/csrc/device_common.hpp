@@ -57,26 +57,50 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
-// Sign-magnitude nibbles -> OCP E4M3 bytes.  Magnitude codes 0..7 map to the
-// E4M3 encodings of the values given by `lut_lo` (codes 0..3) and `lut_hi`
-// (codes 4..7); bit 3 of a nibble becomes bit 7 of its byte.  For the eight
-// nibbles of `w` (nibble i = bits 4i..4i+3) the results are returned as
-//   lo = bytes for nibbles 0, 2, 4, 6 and hi = bytes for nibbles 1, 3, 5, 7.
-// (Any fixed order of k inside a group is a valid contraction as long as both
-// operands use the same one.)
-__device__ __forceinline__ void nibbles_to_e4m3(uint32_t w, uint32_t lut_lo, uint32_t lut_hi,
-                                                uint32_t& lo, uint32_t& hi) {
-  uint32_t sel_lo = w & 0x07070707u;
-  uint32_t sel_hi = (w >> 4) & 0x07070707u;
-  lo = __builtin_amdgcn_perm(lut_hi, lut_lo, sel_lo) | ((w << 4) & 0x80808080u);
-  hi = __builtin_amdgcn_perm(lut_hi, lut_lo, sel_hi) | (w & 0x80808080u);
+// Eight sign-magnitude int4 codes (nibble i = bits 4i..4i+3 = column i, bit 3
+// = sign, bits 0..2 = |q| <= 7) -> eight fp16 values q in column order, as
+// four (column 2i, column 2i+1) pairs.  Each |q| is looked up with v_perm in
+// the table of the high bytes of the fp16 encodings of 0..7 (their low bytes
+// are 0); the sign bit moves to bit 7 of the high byte.  Exact.
+__device__ __forceinline__ u32x4 int4x8_to_f16(uint32_t w) {
+  constexpr uint32_t kT0 = 0x42403C00u;  // fp16 high bytes of 0, 1, 2, 3
+  constexpr uint32_t kT1 = 0x47464544u;  // of 4, 5, 6, 7
+  const uint32_t mlo = w & 0x07070707u;          // |q| of columns 0, 2, 4, 6
+  const uint32_t mhi = (w >> 4) & 0x07070707u;   // |q| of columns 1, 3, 5, 7
+  const uint32_t hlo = __builtin_amdgcn_perm(kT1, kT0, mlo) | ((w << 4) & 0x80808080u);
+  const uint32_t hhi = __builtin_amdgcn_perm(kT1, kT0, mhi) | (w & 0x80808080u);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(hhi, hlo, 0x040C000Cu);  // (q0, q1)
+  r[1] = __builtin_amdgcn_perm(hhi, hlo, 0x050C010Cu);  // (q2, q3)
+  r[2] = __builtin_amdgcn_perm(hhi, hlo, 0x060C020Cu);  // (q4, q5)
+  r[3] = __builtin_amdgcn_perm(hhi, hlo, 0x070C030Cu);  // (q6, q7)
+  return r;
 }
 
-// E4M3 encodings of the int4 magnitudes 0..7 and of the E2M1 magnitudes
-// 0, .5, 1, 1.5, 2, 3, 4, 6 (as 4-byte lookup tables for v_perm_b32).
-constexpr uint32_t kInt4LutLo = 0x44403800u;   // 0, 1, 2, 3
-constexpr uint32_t kInt4LutHi = 0x4E4C4A48u;   // 4, 5, 6, 7
-constexpr uint32_t kE2m1LutLo = 0x3C383000u;   // 0, .5, 1, 1.5
-constexpr uint32_t kE2m1LutHi = 0x4C484440u;   // 2, 3, 4, 6
+// The same codes times an fp16 scale (exact whenever q * scale is an fp16).
+__device__ __forceinline__ f16x8 int4x8_to_f16_scaled(uint32_t w, _Float16 scale) {
+  const f16x8 v = __builtin_bit_cast(f16x8, int4x8_to_f16(w));
+  const f16x8 sc = {scale, scale, scale, scale, scale, scale, scale, scale};
+  return v * sc;
+}
+
+// Eight OCP E2M1 codes (nibble i = column i) times an fp16 scale -> fp16 in
+// column order.  E2M1 -> fp16 is exact (scale operand 1: the conversion
+// applies only a power of two); exact whenever value * scale is an fp16.
+__device__ __forceinline__ f16x8 e2m1x8_to_f16_scaled(uint32_t w, _Float16 scale) {
+  const f16x2 sc = {scale, scale};
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Power-of-two exponent E of a positive normal float s such that s * 2^-E
+// lies in [2^12, 2^13): then |q| * s * 2^-E < 7 * 2^13 fits fp16 for |q| <= 7,
+// and every s' >= 2^-17 (within 2^29 of the largest) keeps all its bits.
+__device__ __forceinline__ int fp16_fit_exponent(float smax) {
+  return (int)((__float_as_uint(smax) >> 23) & 0xffu) - 127 - 12;
+}
 
 }  // namespace svdq

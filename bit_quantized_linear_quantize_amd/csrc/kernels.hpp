@@ -13,25 +13,29 @@ struct QuantActArgs {
   const void* x;          // bf16 [M, K]
   const void* smooth;     // bf16 [K]
   const void* lora_down;  // bf16 [rank, K]
-  void* codes;            // u8 [M, K/2] nibbles, or (int4, fp8_codes) E4M3 [M, K]
-  void* scales;           // bf16 [M, K/64] | u8 [M, K/16]
+  void* codes;            // parity export: u8 [M, K/2] nibbles; else null
+  void* scales;           // parity export: bf16 [M, K/64] | u8 [M, K/16]; else null
   float* lora_act;        // f32 [M, rank]
+  void* act_f16;          // linear only: f16 [M, K] product operand q * s (see below), else null
+  float* row_scale;       // linear int4 only: f32 [M] power-of-two factor of each row of act_f16
   int64_t M, K;
   int precision, rank;
-  bool fp8_codes;         // int4 only: write E4M3 bytes in expansion order
 };
 
+// act_f16 holds the dequantized activations exactly: int4 q * s * 2^-E[m]
+// (E[m] chosen per row so every value fits fp16, row_scale[m] = 2^E[m]);
+// nvfp4 e2m1 * dec(s8), which always fits fp16.
+
 struct GemmArgs {
-  const void* act_codes;   // int4: E4M3 [M, K] (expansion order), or nibbles [M, K/2]
-                           // when computing partials; nvfp4: nibbles [M, K/2]
-  const void* act_scales;  // bf16 [M, K/64] | u8 [M, K/16]
-  const float* lora_act;   // f32 [M, rank]
-  const void* w_codes;     // u8 [N, K/2]
-  const void* w_scales;    // bf16 [N, K/64] | u8 [N, K/16]
-  const void* lora_up;     // bf16 [N, rank]
-  const void* bias;        // bf16 [N] or null
-  void* out;               // bf16 [M, N]
-  int32_t* partials;       // parity export: i32 [M, N, K/G] (then out is unused)
+  const void* act;          // linear: f16 [M, K] (act_f16 above); partials: nibbles [M, K/2]
+  const float* row_scale;   // linear int4: f32 [M]; else null
+  const float* lora_act;    // f32 [M, rank]
+  const void* w_codes;      // u8 [N, K/2]
+  const void* w_scales;     // bf16 [N, K/64] | u8 [N, K/16]
+  const void* lora_up;      // bf16 [N, rank]
+  const void* bias;         // bf16 [N] or null
+  void* out;                // bf16 [M, N]
+  int32_t* partials;        // parity export: i32 [M, N, K/G] (then out is unused)
   float wtscale;
   int64_t M, K, N;
   int precision, rank;

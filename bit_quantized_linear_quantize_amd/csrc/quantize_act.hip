@@ -23,12 +23,17 @@
 // The per-wave low-rank partials are summed in LDS in a fixed order
 // (deterministic).  Loads of X are 16 bytes per lane, several chunks in flight.
 //
-// Output formats: the parity export writes packed nibbles (low nibble = even
-// column).  Inside svdq_w4a4_linear the int4 codes go to the workspace already
-// expanded to E4M3 bytes (the operand format of the int4 product kernel), in
-// "expansion order": each run of 8 columns k0..k0+7 is stored as columns
-// k0+{0,2,4,6,1,3,5,7} -- the order in which the product kernel expands the
-// packed weight codes, so both operands agree column by column.
+// Outputs.  The parity export writes packed nibbles (low nibble = even
+// column), the group scales and lora_act.  Inside svdq_w4a4_linear the kernel
+// instead writes the activations already dequantized, as the fp16 operand of
+// the product kernel: nvfp4 e2m1 * dec(s8) (always an exact fp16), int4
+// q * s * 2^-E[m] with one power of two per row (row_scale[m] = 2^E[m] is
+// undone after the product).  E = 0 whenever every group scale s of the row
+// lies in [2^-17, 2^13): then q * s is an exact fp16 (at most 11 significant
+// bits, a multiple of 2^-24, below 2^16), so the values are written in the
+// same pass.  A row with a scale outside that range (known once the
+// workgroup has seen the whole row) is quantized again from X and rewritten
+// with E chosen from its largest scale.
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -43,10 +48,15 @@ struct K1Prefetch {
   static constexpr int value = RB <= 2 ? 4 : 2;
 };
 
-template <int PREC, int RB, bool FP8OUT>
+template <int PREC, int RB, bool LINEAR>
 __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArgs args) {
   extern __shared__ float lds[];
+  // int4 linear: per wave and row, the largest group scale and the smallest
+  // nonzero one
+  __shared__ float rmax[kK1Waves][kK1Rows];
+  __shared__ float rmin[kK1Waves][kK1Rows];
   constexpr int PF = K1Prefetch<RB>::value;
+  constexpr bool kRowExp = LINEAR && PREC == kInt4;
   constexpr int NB = RB > 0 ? RB : 1;
   const int M = (int)args.M, K = (int)args.K;
   const uint16_t* __restrict__ x = (const uint16_t*)args.x;
@@ -68,9 +78,52 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
   const uint16_t* xr = x + (size_t)(row_ok ? row : M - 1) * K;
   const int nchunks = K >> 6;
 
+  // X_hat of the lane's 16 columns k0 .. k0+15
+  auto smooth16 = [&](const u32x4* xb, int k0, float* xh) {
+    const f32x4* mu4 = (const f32x4*)(lds + k0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = xb[h][i];
+        const f32x4 mu = mu4[h * 2 + (i >> 1)];
+        xh[h * 8 + 2 * i] = __fmul_rn(bf16_lo(w), mu[(2 * i) & 3]);
+        xh[h * 8 + 2 * i + 1] = __fmul_rn(bf16_hi(w), mu[(2 * i + 1) & 3]);
+      }
+    }
+  };
+  // int4: the group (the four lanes q = 0..3 of the row) scale, returned as
+  // bf16 bits, and the lane's 16 codes
+  auto quant_int4 = [&](const float* xh, uint32_t& cw0, uint32_t& cw1) -> uint32_t {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+    amax = wave_max_xor(amax, 16);
+    amax = wave_max_xor(amax, 32);
+    const bool zero = !(amax >= kTiny);
+    const uint32_t sbits = zero ? 0u : f32_to_bf16_bits(__fdiv_rn(amax, 7.0f));
+    const float inv = zero ? 0.f : __fdiv_rn(1.0f, __uint_as_float(sbits << 16));
+    cw0 = 0;
+    cw1 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float t = __fmul_rn(xh[i], inv);
+      // |t| < 7.5, so adding 1.5 * 2^23 rounds it to the nearest integer
+      // (ties to even) in the low mantissa bits
+      const uint32_t m = __float_as_uint(__fadd_rn(fabsf(t), 12582912.0f));
+      const uint32_t nib = (m & 7u) | ((__float_as_uint(t) >> 28) & 8u);
+      if (i < 8) cw0 |= nib << (4 * i);
+      else cw1 |= nib << (4 * (i - 8));
+    }
+    cw0 = zero ? 0u : cw0;
+    cw1 = zero ? 0u : cw1;
+    return sbits;
+  };
+
   f32x4 acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float smax = 0.f, smin = __builtin_huge_valf();  // int4 linear: over the lane's groups
 
   u32x4 xbuf[PF][2];
   u32x4 lbuf[PF][NB][2];
@@ -100,45 +153,33 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
       const int c = base + p * kK1Waves;
       if (c < nchunks) {
         const int k0 = c * 64 + q * 16;
-        // ---- unpack + smooth ----------------------------------------------
         float xh[16];
-        const f32x4* mu4 = (const f32x4*)(lds + k0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t w = xbuf[p][h][i];
-            const f32x4 mu = mu4[h * 2 + (i >> 1)];
-            xh[h * 8 + 2 * i] = __fmul_rn(bf16_lo(w), mu[(2 * i) & 3]);
-            xh[h * 8 + 2 * i + 1] = __fmul_rn(bf16_hi(w), mu[(2 * i + 1) & 3]);
-          }
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+        smooth16(xbuf[p], k0, xh);
 
         // ---- quantize -----------------------------------------------------
         uint32_t cw0 = 0, cw1 = 0;
         if constexpr (PREC == kInt4) {
-          amax = wave_max_xor(amax, 16);
-          amax = wave_max_xor(amax, 32);
-          const bool zero = !(amax >= kTiny);
-          const uint32_t sbits = zero ? 0u : f32_to_bf16_bits(__fdiv_rn(amax, 7.0f));
-          const float inv = zero ? 0.f : __fdiv_rn(1.0f, __uint_as_float(sbits << 16));
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float t = __fmul_rn(xh[i], inv);
-            // |t| < 7.5, so adding 1.5 * 2^23 rounds it to the nearest integer
-            // (ties to even) in the low mantissa bits
-            const uint32_t m = __float_as_uint(__fadd_rn(fabsf(t), 12582912.0f));
-            const uint32_t nib = (m & 7u) | ((__float_as_uint(t) >> 28) & 8u);
-            if (i < 8) cw0 |= nib << (4 * i);
-            else cw1 |= nib << (4 * (i - 8));
+          const uint32_t sbits = quant_int4(xh, cw0, cw1);
+          const float sv = __uint_as_float(sbits << 16);
+          if constexpr (LINEAR) {
+            // speculatively with row exponent 0: q * s is an exact fp16
+            // whenever 2^-17 <= s < 2^13; rows with a scale outside that
+            // range are rewritten below
+            smax = fmaxf(smax, sv);
+            if (sbits != 0u) smin = fminf(smin, sv);
+            if (row_ok) {
+              const _Float16 s16 = (_Float16)sv;
+              _Float16* dst = (_Float16*)args.act_f16 + (size_t)row * K + k0;
+              *(f16x8*)dst = int4x8_to_f16_scaled(cw0, s16);
+              *(f16x8*)(dst + 8) = int4x8_to_f16_scaled(cw1, s16);
+            }
+          } else if (row_ok && q == 0) {
+            ((uint16_t*)args.scales)[(size_t)row * (K >> 6) + c] = (uint16_t)sbits;
           }
-          cw0 = zero ? 0u : cw0;
-          cw1 = zero ? 0u : cw1;
-          if (row_ok && q == 0) ((uint16_t*)args.scales)[(size_t)row * (K >> 6) + c] = (uint16_t)sbits;
         } else {
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
           const float sf = __fdiv_rn(amax, 6.0f);
           const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sf, 448.0f), 0.0f, 0, false) & 0xffu;
           const float S = __builtin_amdgcn_cvt_f32_fp8((int)s8, 0);
@@ -154,18 +195,19 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
           }
           cw0 = zero ? 0u : cw0;
           cw1 = zero ? 0u : cw1;
-          if (row_ok) ((uint8_t*)args.scales)[(size_t)row * (K >> 4) + 4 * c + q] = (uint8_t)(zero ? 0u : s8);
-        }
-        if (row_ok) {
-          if constexpr (FP8OUT) {
-            uint32_t e0, e1, e2, e3;
-            nibbles_to_e4m3(cw0, kInt4LutLo, kInt4LutHi, e0, e1);
-            nibbles_to_e4m3(cw1, kInt4LutLo, kInt4LutHi, e2, e3);
-            *(u32x4*)(codes + (size_t)row * K + k0) = u32x4{e0, e1, e2, e3};
-          } else {
-            *(u32x2*)(codes + (size_t)row * (K >> 1) + (k0 >> 1)) = u32x2{cw0, cw1};
+          if constexpr (LINEAR) {
+            // the product operand e2m1 * dec(s8): an exact fp16 (|v| <= 2688, >= 2^-10)
+            if (row_ok) {
+              const _Float16 S16 = (_Float16)S;
+              _Float16* dst = (_Float16*)args.act_f16 + (size_t)row * K + k0;
+              *(f16x8*)dst = e2m1x8_to_f16_scaled(cw0, S16);
+              *(f16x8*)(dst + 8) = e2m1x8_to_f16_scaled(cw1, S16);
+            }
+          } else if (row_ok) {
+            ((uint8_t*)args.scales)[(size_t)row * (K >> 4) + 4 * c + q] = (uint8_t)(zero ? 0u : s8);
           }
         }
+        if (row_ok && !LINEAR) *(u32x2*)(codes + (size_t)row * (K >> 1) + (k0 >> 1)) = u32x2{cw0, cw1};
 
         // ---- low-rank down projection (bf16 hi + lo, fp32 accumulate) ------
         if constexpr (RB > 0) {
@@ -192,6 +234,42 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
     }
   }
 
+  // ---- int4 linear: the row's power of two; rows that do not fit exponent 0
+  // are quantized again from X and rewritten as q * s * 2^-E[row] ------------
+  if constexpr (kRowExp) {
+    if (q == 0) {  // the four lanes of a row hold the same groups' scales
+      rmax[wave][r] = smax;
+      rmin[wave][r] = smin;
+    }
+    __syncthreads();
+    float mx = rmax[0][r], mn = rmin[0][r];
+#pragma unroll
+    for (int w = 1; w < kK1Waves; ++w) {
+      mx = fmaxf(mx, rmax[w][r]);
+      mn = fminf(mn, rmin[w][r]);
+    }
+    const bool fits = mx < 8192.0f && mn >= 7.62939453125e-06f;  // [2^-17, 2^13)
+    const int E = fits || !(mx > 0.f) ? 0 : fp16_fit_exponent(mx);
+    if (row_ok && wave == 0 && q == 0) args.row_scale[row] = __builtin_ldexpf(1.0f, E);
+    if (!fits && row_ok) {  // uniform over the four lanes of the row
+      const float down = __builtin_ldexpf(1.0f, -E);
+      _Float16* dst = (_Float16*)args.act_f16 + (size_t)row * K;
+      for (int c = wave; c < nchunks; c += kK1Waves) {
+        const int k0 = c * 64 + q * 16;
+        u32x4 xb[2];
+        xb[0] = *(const u32x4*)(xr + k0);
+        xb[1] = *(const u32x4*)(xr + k0 + 8);
+        float xh[16];
+        smooth16(xb, k0, xh);
+        uint32_t cw0, cw1;
+        const uint32_t sbits = quant_int4(xh, cw0, cw1);
+        const _Float16 s16 = (_Float16)(__uint_as_float(sbits << 16) * down);  // exact power-of-two scaling
+        *(f16x8*)(dst + k0) = int4x8_to_f16_scaled(cw0, s16);
+        *(f16x8*)(dst + k0 + 8) = int4x8_to_f16_scaled(cw1, s16);
+      }
+    }
+  }
+
   // ---- reduce the low-rank partials of the 8 waves (fixed order) ----------
   if constexpr (RB > 0) {
     constexpr int rank = RB * 16;
@@ -214,38 +292,39 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
   }
 }
 
-template <int PREC, int RB, bool FP8OUT>
+template <int PREC, int RB, bool LINEAR>
 static hipError_t launch_k1(const QuantActArgs& a, hipStream_t stream) {
   const int rank = RB * 16;
   size_t lds = (size_t)a.K * sizeof(float);
   const size_t red = (size_t)kK1Waves * kK1Rows * rank * sizeof(float);
   if (red > lds) lds = red;
   const unsigned blocks = (unsigned)((a.M + kK1Rows - 1) / kK1Rows);
-  hipLaunchKernelGGL((quantize_act_lora_down_kernel<PREC, RB, FP8OUT>), dim3(blocks), dim3(512), lds,
+  hipLaunchKernelGGL((quantize_act_lora_down_kernel<PREC, RB, LINEAR>), dim3(blocks), dim3(512), lds,
                      stream, a);
   return hipGetLastError();
 }
 
-template <int PREC, bool FP8OUT>
+template <int PREC, bool LINEAR>
 static hipError_t dispatch_rank(const QuantActArgs& a, hipStream_t s) {
   switch (a.rank / 16) {
-    case 0: return launch_k1<PREC, 0, FP8OUT>(a, s);
-    case 1: return launch_k1<PREC, 1, FP8OUT>(a, s);
-    case 2: return launch_k1<PREC, 2, FP8OUT>(a, s);
-    case 3: return launch_k1<PREC, 3, FP8OUT>(a, s);
-    case 4: return launch_k1<PREC, 4, FP8OUT>(a, s);
-    case 5: return launch_k1<PREC, 5, FP8OUT>(a, s);
-    case 6: return launch_k1<PREC, 6, FP8OUT>(a, s);
-    case 7: return launch_k1<PREC, 7, FP8OUT>(a, s);
-    case 8: return launch_k1<PREC, 8, FP8OUT>(a, s);
+    case 0: return launch_k1<PREC, 0, LINEAR>(a, s);
+    case 1: return launch_k1<PREC, 1, LINEAR>(a, s);
+    case 2: return launch_k1<PREC, 2, LINEAR>(a, s);
+    case 3: return launch_k1<PREC, 3, LINEAR>(a, s);
+    case 4: return launch_k1<PREC, 4, LINEAR>(a, s);
+    case 5: return launch_k1<PREC, 5, LINEAR>(a, s);
+    case 6: return launch_k1<PREC, 6, LINEAR>(a, s);
+    case 7: return launch_k1<PREC, 7, LINEAR>(a, s);
+    case 8: return launch_k1<PREC, 8, LINEAR>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream) {
+  const bool linear = a.act_f16 != nullptr;
   if (a.precision == kInt4)
-    return a.fp8_codes ? dispatch_rank<kInt4, true>(a, stream) : dispatch_rank<kInt4, false>(a, stream);
-  return dispatch_rank<kNvfp4, false>(a, stream);
+    return linear ? dispatch_rank<kInt4, true>(a, stream) : dispatch_rank<kInt4, false>(a, stream);
+  return linear ? dispatch_rank<kNvfp4, true>(a, stream) : dispatch_rank<kNvfp4, false>(a, stream);
 }
 
 }  // namespace svdq

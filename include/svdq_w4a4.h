@@ -52,11 +52,11 @@ enum svdq_status {
   SVDQ_EDEVICE = -5       /* HIP runtime error (no device, launch failure)     */
 };
 
-/* Bytes of scratch svdq_w4a4_linear needs: activation codes (int4: M*K bytes,
- * kept as 8-bit operands; nvfp4: M*K/2), activation scales [M, K/G] (bf16 for
- * int4, E4M3 bytes for nvfp4) and the low-rank activations [M, rank] fp32,
- * each 256-byte aligned.  Returns 0 for arguments svdq_w4a4_linear would
- * reject. */
+/* Bytes of scratch svdq_w4a4_linear needs, each part 256-byte aligned: the
+ * dequantized activations as fp16 [M, K] (the operand of the product kernel:
+ * code times group scale is exact in fp16); for int4 also one fp32
+ * power-of-two row factor [M]; and the low-rank activations fp32 [M, rank].
+ * Returns 0 for arguments svdq_w4a4_linear would reject. */
 size_t svdq_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision,
                                  int group_size, int rank);
 

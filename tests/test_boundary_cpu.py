@@ -135,11 +135,14 @@ def test_wtscale_rules(L):
 
 def test_workspace_size(L):
     M, K, N = 300, 512, 320
-    # int4 codes are kept as 8-bit operands (M*K bytes), nvfp4 as nibbles (M*K/2)
-    for prec, g, cb, sb in ((0, 64, M * K, 2 * 8), (1, 16, M * K // 2, 32)):
+    rnd = lambda v: (v + 255) // 256 * 256
+    # fp16 activations [M, K]; int4 adds a row factor [M]; then lora_act
+    # fp32 [M, 32]
+    want = {0: rnd(2 * M * K) + rnd(4 * M) + rnd(M * 32 * 4),
+            1: rnd(2 * M * K) + rnd(M * 32 * 4)}
+    for prec, g in ((0, 64), (1, 16)):
         need = L.svdq_w4a4_workspace_bytes(M, K, N, prec, g, 32)
-        rnd = lambda v: (v + 255) // 256 * 256
-        assert need == rnd(cb) + rnd(M * sb) + rnd(M * 32 * 4)
+        assert need == want[prec]
         a = Args(M=M, K=K, N=N, precision=prec, group=g)
         assert a.call(L, wsb=need - 1) == EWS
         assert a.call(L, wsb=need) == OK

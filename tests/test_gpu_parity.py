@@ -232,6 +232,47 @@ def test_linear_full_size(cfg1_layers, which):
     assert_output(y, L.svdq_linear_ref(c["x"], lay), f"linear cfg1 {which}")
 
 
+def test_linear_int4_row_exponents():
+    # int4 activations enter the product as fp16 q * s * 2^-E[row]; E = 0 when
+    # every group scale s of the row is in [2^-17, 2^13), else the row is
+    # rewritten with E from its largest scale.  Rows of each kind, and rows
+    # on both sides of both bounds, each class checked on its own.
+    rng = np.random.default_rng(23)
+    M, K, N = 100, 512, 192
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    xf[16:32] *= 3e5                      # scales far above 2^13
+    xf[32:48] *= 1e-7                     # scales below 2^-17
+    xf[48:64, 256:] *= 1e-9               # one row, scales 2^-33 .. 2^-1
+    xf[64:80] = np.clip(xf[64:80], -3, 3)  # other groups: s ~ 0.4
+    xf[64, 5] = 57088.0                   # s = bf16(57088 / 7) = 8160: fits
+    xf[65, 70] = 57344.0                  # s = 8192: rewritten
+    xf[66, 128:192] *= 1e-9
+    xf[66, 130] = 7 * 2.0 ** -17          # smallest s = 2^-17: fits
+    xf[67, 128:192] *= 1e-9
+    xf[67, 130] = 1.734375 * 2.0 ** -15   # smallest s just below 2^-17: rewritten
+    xf[80:84] = 0.0                       # zero rows
+    xf[84, 64:] = 0.0                     # one nonzero group
+    x = S.to_bf16_bits(xf)
+    w = S.weight(N, K, 0.02, rng, spike_rank=4)
+    b = S.bias(N, rng)
+    lay = prepared(x, w, b, "int4", 32)
+    y = run_linear(x, lay)
+    yf = F.bf16_to_f32(host_bits(y)).astype(np.float64)
+    ref = L.svdq_linear_ref(x, lay)
+    assert np.all(np.isfinite(yf))
+    classes = {"normal": list(range(0, 16)) + list(range(85, 100)), "huge": range(16, 32),
+               "tiny": range(32, 48), "mixed": range(48, 64), "bounds": range(64, 80),
+               "zero-ish": range(80, 85)}
+    for name, rows in classes.items():
+        rows = list(rows)
+        for rr in rows if name == "bounds" else [rows]:
+            sel = [rr] if name == "bounds" else rr
+            _, excess, mre = L.output_errors(yf[sel], ref[sel])
+            print(f"[int4 row exponent {name} {sel if name == 'bounds' else ''}] excess {excess:.3e} MRE {mre:.3e}",
+                  flush=True)
+            assert excess <= 1e-2 and mre <= 2e-3, (name, sel)
+
+
 def test_linear_deterministic_with_poisoned_workspace(ragged):
     x, w, b = ragged
     for p in ("int4", "nvfp4"):
