@@ -40,6 +40,8 @@
 // instructions with unit scales (A from packed codes), writing the exact
 // per-group integer partials (nvfp4: doubled E2M1 codes) instead.
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -50,28 +52,46 @@ constexpr int kBN = 192;
 constexpr int kBK = 64;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWM = 4;   // waves along M
-constexpr int kIB = 2;   // 32-row blocks per wave
-constexpr int kJB = 3;   // 32-column blocks per wave
+constexpr int kWM = 4;                    // waves along M
+constexpr int kIB = kBM / (32 * kWM);     // 32-row blocks per wave (2)
+constexpr int kJB = kBN / (32 * (kWaves / kWM));  // 32-column blocks per wave (3)
+constexpr int kRP = kThreads / 8;         // tile rows per register-loader pass (8 threads per row)
+constexpr int kAP = kBM / kRP;            // parity export: A pieces per thread and stage (4)
+constexpr int kWP = kBN / kRP;            // W pieces per thread and stage (3)
 constexpr int kGroupM = 4;
-constexpr int kRow = 144;  // LDS bytes per staged row: 64 fp16 + 16 pad
-constexpr int kMaxScaleG = 64;  // int4 weight-scale table in LDS for K <= 4096
+constexpr int kAStages = 3;               // A ring depth
+constexpr int kARow = 128;                // A LDS row: 64 fp16 in 8 XOR-swizzled 16-byte chunks
+constexpr int kWRow = 144;                // W LDS row: 64 fp16 + 16 pad
+constexpr int kADma = kBM * 8 / kThreads; // A direct-to-LDS loads per thread and stage (4)
+static_assert(kAP % 4 == 0 && kWP == 3 && kThreads >= kBN && kADma * kThreads == kBM * 8, "loader layout");
 
-struct alignas(16) Stage {
-  uint8_t a[kBM * kRow];
-  uint8_t w[kBN * kRow];
-};
+template <int I>
+using IC = std::integral_constant<int, I>;
 
-// One stage of raw operands in registers.  Every thread has the same role:
-// A piece i (0..3) = 16 bytes of fp16 (linear) or 4 bytes of codes (partials)
-// holding columns 8c..8c+7 (c = tid % 8) of tile row tid/8 + 64 i; W piece j
-// (0..2) = 4 bytes of codes for columns 8c..8c+7 of tile row tid/8 + 64 j.  A
-// load instruction therefore covers whole 128-byte (A) or 32-byte (W) row
-// slices of 8 rows, and the staging code has no per-wave branches.
+// Workgroup barrier for the main loop: this wave's LDS reads and writes are
+// complete (lgkmcnt 0), and the compiler moves no memory access across it.
+// Unlike a release fence it does not wait for the wave's direct-to-LDS loads
+// that are still in flight for later stages.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Position of 16-byte chunk c (columns 8c .. 8c+7 of the stage) in A row
+// `row`: the XOR spreads the 16 rows one matrix-instruction operand read
+// covers over all 64 banks.
+__device__ __forceinline__ int a_pos(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+// One stage of raw W (and, for the parity export, A) data in registers.  Every
+// thread has the same role: W piece j = 4 bytes of codes for columns 8c ..
+// 8c+7 (c = tid % 8) of tile row tid/8 + 64 j, and its scale; A piece i
+// likewise for A row tid/8 + 64 i.
 struct RawStage {
-  u32x4 a[4];
-  uint32_t w[3];
-  uint32_t sw[3];  // nvfp4: the E4M3 scale byte of each W piece (int4 reads a table)
+  uint32_t w[kWP];
+  uint32_t sw[kWP];  // the scale of each W piece: nvfp4 E4M3 byte, int4 bf16 bits
+  uint32_t a[kAP];   // parity export only
 };
 
 // Raw buffer descriptor over `bytes` bytes at p (sizes past 2^31 - 1 are
@@ -97,17 +117,20 @@ __device__ __forceinline__ void tile_of(int bid, int nmt, int nnt, int& mt, int&
   nt = r / gsize;
 }
 
-// WT (int4 only, K <= 64 kMaxScaleG): the weight group scales come from a
-// table in LDS filled once per workgroup instead of one load per row and stage.
-template <int PREC, int RB, bool PARTIALS, bool WT>
+template <int PREC, int RB, bool PARTIALS>
 __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs args) {
-  __shared__ Stage st[2];
+  // separate LDS objects, selected at compile time, so that the compiler can
+  // tell the buffers apart from those that direct-to-LDS loads are filling
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a0[kBM * kARow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a1[kBM * kARow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a2[kBM * kARow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w0[kBN * kWRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w1[kBN * kWRow];
   __shared__ float wexp[kBN];   // int4: 2^F[n] of this tile's weight rows
   __shared__ float wdown[kBN];  // int4: 2^-F[n]
-  __shared__ _Float16 wsc[WT ? kBN * kMaxScaleG : 1];  // int4: s_w * 2^-F[n]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
   const int M = (int)args.M, K = (int)args.K, N = (int)args.N;
   const int K2 = K >> 1;
@@ -118,10 +141,11 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   const int nstages = K / kBK;
   constexpr bool kRowExp = PREC == kInt4 && !PARTIALS;
 
-  // ---- loader roles --------------------------------------------------------
+  // ---- loaders ---------------------------------------------------------------
   // Buffer loads: one descriptor per operand based at this tile's first row,
   // 32-bit lane offsets, the stage offset in a scalar register.  Rows past
-  // the end of the matrix lie beyond the descriptor's size and read as zero.
+  // the end of the matrix, and stages past the last, lie beyond the
+  // descriptor's size or in rows that are never used, and read as zero.
   const int lc = tid & 7;    // column chunk: columns 8 lc .. 8 lc + 7 of the stage
   const int lr = tid >> 3;   // tile row of piece 0 (piece i: lr + 64 i)
   const size_t a_row_bytes = PARTIALS ? (size_t)K2 : (size_t)K * 2;
@@ -132,105 +156,94 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   const size_t ws_row_bytes = PREC == kInt4 ? (size_t)(K >> 6) * 2 : (size_t)(K >> 4);
   const __amdgpu_buffer_rsrc_t ws_rs = make_rsrc((const uint8_t*)args.w_scales + (size_t)n0 * ws_row_bytes,
                                                  PARTIALS ? 0 : (size_t)(N - n0) * ws_row_bytes);
-  int a_off[4], w_off[3], ws_off[3];
+  // stages past the last read through an empty descriptor: all zeros
+  const __amdgpu_buffer_rsrc_t zero_rs = make_rsrc(args.w_codes, 0);
+  int w_off[kWP], ws_off[kWP], pa_off[kAP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_off[i] = (lr + 64 * i) * (int)a_row_bytes + lc * (PARTIALS ? 4 : 16);
+  for (int j = 0; j < kWP; ++j) {
+    w_off[j] = (lr + kRP * j) * K2 + lc * 4;
+    ws_off[j] = (lr + kRP * j) * (int)ws_row_bytes + (PREC == kNvfp4 ? (lc >> 1) : 0);
+  }
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    w_off[j] = (lr + 64 * j) * K2 + lc * 4;
-    ws_off[j] = (lr + 64 * j) * (int)ws_row_bytes + (PREC == kNvfp4 ? (lc >> 1) : 0);
+  for (int i = 0; i < kAP; ++i) pa_off[i] = (lr + kRP * i) * K2 + lc * 4;
+  // A (fp16) goes straight from memory to LDS: load d of a wave fills the
+  // 1 KB of LDS units u0 .. u0+63 (u0 = 64 (kADma wave + d)), lane l unit
+  // u0 + l = row u/8, position u%8, which holds chunk a_pos(row, u%8).
+  int dma_off[kADma];
+#pragma unroll
+  for (int d = 0; d < kADma; ++d) {
+    const int u = (wave * kADma + d) * 64 + lane;
+    const int row = u >> 3;
+    dma_off[d] = row * (int)a_row_bytes + a_pos(row, u & 7) * 16;
   }
 
-  // int4: per weight row the power of two 2^-F that makes every q * s_w * 2^-F
-  // an exact fp16 (from the row's largest group scale); for K <= 4096 the
-  // scaled group scales s_w * 2^-F themselves go to an LDS table, read here
-  // with whole-row loads instead of one scattered load per row and stage
-  const int G64 = K >> 6;
-  if constexpr (kRowExp) {
-    if (tid < kBN) {
-      // the row's scales, two per load (G64 is even: rows are 4-byte aligned)
-      const uint16_t* srow = (const uint16_t*)args.w_scales + (size_t)min(n0 + tid, N - 1) * G64;
-      float m = 0.f;
-      if constexpr (WT) {
-        uint32_t v[kMaxScaleG / 2];  // all of them in flight at once, kept for the table
-#pragma unroll
-        for (int p = 0; p < kMaxScaleG / 2; ++p)
-          if (2 * p < G64) v[p] = *(const uint32_t*)(srow + 2 * p);
-#pragma unroll
-        for (int p = 0; p < kMaxScaleG / 2; ++p)
-          if (2 * p < G64) m = fmaxf(m, fmaxf(bf16_lo(v[p]), bf16_hi(v[p])));
-        const int F = m > 0.f ? fp16_fit_exponent(m) : 0;
-        wexp[tid] = __builtin_ldexpf(1.0f, F);
-        const float down = __builtin_ldexpf(1.0f, -F);
-        wdown[tid] = down;
-#pragma unroll
-        for (int p = 0; p < kMaxScaleG / 2; ++p)
-          if (2 * p < G64) {
-            wsc[tid * kMaxScaleG + 2 * p] = (_Float16)(bf16_lo(v[p]) * down);
-            wsc[tid * kMaxScaleG + 2 * p + 1] = (_Float16)(bf16_hi(v[p]) * down);
-          }
-      } else {
-        for (int g0 = 0; g0 < G64; g0 += 16) {
-          uint32_t v[8];
-#pragma unroll
-          for (int p = 0; p < 8; ++p)
-            if (g0 + 2 * p < G64) v[p] = *(const uint32_t*)(srow + g0 + 2 * p);
-#pragma unroll
-          for (int p = 0; p < 8; ++p)
-            if (g0 + 2 * p < G64) m = fmaxf(m, fmaxf(bf16_lo(v[p]), bf16_hi(v[p])));
-        }
-        const int F = m > 0.f ? fp16_fit_exponent(m) : 0;
-        wexp[tid] = __builtin_ldexpf(1.0f, F);
-        wdown[tid] = __builtin_ldexpf(1.0f, -F);
-      }
-    }
-    __syncthreads();
-  }
+  auto abuf = [&](auto c) -> uint8_t* {
+    constexpr int i = decltype(c)::value % kAStages;
+    if constexpr (i == 0) return lds_a0;
+    else if constexpr (i == 1) return lds_a1;
+    else return lds_a2;
+  };
+  auto wbuf = [&](auto c) -> uint8_t* {
+    if constexpr (decltype(c)::value % 2 == 0) return lds_w0;
+    else return lds_w1;
+  };
 
-  auto load = [&](RawStage& r, int s) {
+  // loads of stage s: A into A buffer ab (direct to LDS), W into r
+  auto group = [&](RawStage& r, int s, auto ab) {
+    const bool live = s < nstages;
+    const __amdgpu_buffer_rsrc_t ars = live ? a_rs : zero_rs;
+    const __amdgpu_buffer_rsrc_t wrs = live ? w_rs : zero_rs;
+    const __amdgpu_buffer_rsrc_t srs = live ? ws_rs : zero_rs;
+    if constexpr (!PARTIALS) {
+      uint8_t* dst = abuf(ab) + wave * (kADma * 64 * 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (PARTIALS) r.a[i][0] = __builtin_amdgcn_raw_buffer_load_b32(a_rs, a_off[i], s * 32, 0);
-      else r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[i], s * 128, 0);
+      for (int d = 0; d < kADma; ++d)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (__attribute__((address_space(3))) void*)(dst + d * 1024), 16,
+                                                 dma_off[d], s * 128, 0, 0);
+      // the W loads of the stage stay behind its A loads: a wave that has
+      // waited for its W registers has also received its A stage
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      r.w[j] = __builtin_amdgcn_raw_buffer_load_b32(w_rs, w_off[j], s * 32, 0);
-      if constexpr (PREC == kNvfp4 && !PARTIALS) r.sw[j] = __builtin_amdgcn_raw_buffer_load_b8(ws_rs, ws_off[j], s * 4, 0);
-      if constexpr (PREC == kInt4 && !PARTIALS && !WT)
-        r.sw[j] = __builtin_amdgcn_raw_buffer_load_b16(ws_rs, ws_off[j], s * 2, 0);
+    for (int j = 0; j < kWP; ++j) {
+      r.w[j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, w_off[j], s * 32, 0);
+      if constexpr (PREC == kNvfp4 && !PARTIALS) r.sw[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, ws_off[j], s * 4, 0);
+      if constexpr (PREC == kInt4 && !PARTIALS) r.sw[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, ws_off[j], s * 2, 0);
+    }
+    if constexpr (PARTIALS) {
+#pragma unroll
+      for (int i = 0; i < kAP; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b32(ars, pa_off[i], s * 32, 0);
     }
   };
 
-  // staging of one raw stage in four parts (A piece i and W piece i), so that
-  // it can be interleaved with the matrix instructions of the previous stage
-  auto store_part = [&](Stage& T, const RawStage& r, int i, int s) {
-    uint8_t* pa = T.a + (lr + 64 * i) * kRow + lc * 16;
+  const int G64 = K >> 6;
+  float wdn[kWP];  // int4: 2^-F[n] of this thread's weight rows (set after the prologue)
+
+  // staging of one raw stage in three parts (part p: W piece p and, for the
+  // parity export, A pieces of part p), so that it can be interleaved with
+  // the matrix instructions of the previous stage
+  auto store_part = [&](uint8_t* Ta, uint8_t* Tw, const RawStage& r, int p) {
     if constexpr (PARTIALS) {
       // unit scales; nvfp4 doubles the E2M1 codes so that they are integers
       const _Float16 one = (_Float16)(PREC == kInt4 ? 1.0f : 2.0f);
-      *(f16x8*)pa = PREC == kInt4 ? int4x8_to_f16_scaled(r.a[i][0], one) : e2m1x8_to_f16_scaled(r.a[i][0], one);
-    } else {
-      *(u32x4*)pa = r.a[i];
-    }
-    if (i < 3) {
-      const int wrow = lr + 64 * i;
-      uint8_t* pw = T.w + wrow * kRow + lc * 16;
-      _Float16 sc = (_Float16)(PREC == kInt4 ? 1.0f : 2.0f);
-      if constexpr (!PARTIALS) {
-        if constexpr (PREC == kInt4) {
-          if constexpr (WT) sc = wsc[wrow * kMaxScaleG + s];
-          else sc = (_Float16)(bf16_bits_to_f32((uint16_t)r.sw[i]) * wdown[wrow]);  // exact: a power of two
-        } else {
-          sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw[i], 0);
-        }
-      }
-      *(f16x8*)pw = PREC == kInt4 ? int4x8_to_f16_scaled(r.w[i], sc) : e2m1x8_to_f16_scaled(r.w[i], sc);
-    }
-  };
-  auto store = [&](Stage& T, const RawStage& r, int s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store_part(T, r, i, s);
+      for (int i = 0; i < kAP; ++i) {
+        if (i * 3 / kAP != p) continue;
+        const int row = lr + kRP * i;
+        *(f16x8*)(Ta + row * kARow + a_pos(row, lc) * 16) =
+            PREC == kInt4 ? int4x8_to_f16_scaled(r.a[i], one) : e2m1x8_to_f16_scaled(r.a[i], one);
+      }
+    }
+    const int wrow = lr + kRP * p;
+    _Float16 sc = (_Float16)(PREC == kInt4 ? 1.0f : 2.0f);
+    if constexpr (!PARTIALS) {
+      if constexpr (PREC == kInt4)
+        sc = (_Float16)(bf16_bits_to_f32((uint16_t)r.sw[p]) * wdn[p]);  // exact: a power of two
+      else
+        sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw[p], 0);
+    }
+    *(f16x8*)(Tw + wrow * kWRow + lc * 16) =
+        PREC == kInt4 ? int4x8_to_f16_scaled(r.w[p], sc) : e2m1x8_to_f16_scaled(r.w[p], sc);
   };
 
   f32x16 acc[kIB][kJB];
@@ -260,80 +273,130 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       }
   };
 
-  // one stage: 4 k steps of 16, each 2 A and 3 W operand reads and 6 products.
-  // The operands of k step ks+1 are read before the products of step ks are
-  // issued (two register sets); with `nxt`, part ks of the next stage is
-  // staged among the products of step ks (its VALU work and LDS writes issue
-  // while the matrix instructions execute).
-  auto compute = [&](const Stage& T, int s, Stage* nxt, const RawStage* r) {
-    f16x8 aop[2][kIB], bop[2][kJB];
-    auto rd = [&](int ks, f16x8* ao, f16x8* bo) {
+  // operands of two k steps of 16 (set ks & 1); the A offsets of the
+  // swizzled rows are fixed per k step
+  int a_rd[kIB][4];
 #pragma unroll
-      for (int i = 0; i < kIB; ++i)
-        ao[i] = *(const f16x8*)(T.a + (wm * (kIB * 32) + i * 32 + l32) * kRow + ks * 32 + h * 16);
+  for (int i = 0; i < kIB; ++i) {
+    const int row = wm * (kIB * 32) + i * 32 + l32;
 #pragma unroll
-      for (int j = 0; j < kJB; ++j)
-        bo[j] = *(const f16x8*)(T.w + (wn * (kJB * 32) + j * 32 + l32) * kRow + ks * 32 + h * 16);
-    };
-    rd(0, aop[0], bop[0]);
+    for (int ks = 0; ks < 4; ++ks) a_rd[i][ks] = row * kARow + a_pos(row, 2 * ks + h) * 16;
+  }
+  f16x8 aop[2][kIB], bop[2][kJB];
+  auto rd = [&](const uint8_t* Ta, const uint8_t* Tw, int ks, int set) {
+#pragma unroll
+    for (int i = 0; i < kIB; ++i) aop[set][i] = *(const f16x8*)(Ta + a_rd[i][ks]);
+#pragma unroll
+    for (int j = 0; j < kJB; ++j)
+      bop[set][j] = *(const f16x8*)(Tw + (wn * (kJB * 32) + j * 32 + l32) * kWRow + ks * 32 + h * 16);
+  };
+
+  // One stage s: 4 k steps of 16, each 6 products.  On entry the operands of
+  // k step 0 are in set 0; those of step ks+1 are read before the products of
+  // step ks are issued.  The raw stage r (stage s+1) is staged among the
+  // products of steps 0..2 (its VALU work and LDS writes issue while the
+  // matrix instructions execute).  The barrier comes before the products of
+  // the last step: every wave has then finished reading stage s and writing
+  // stage s+1 (and holds its own A loads of stage s+1, which precede the W
+  // loads it waited for), so the operands of the next stage's step 0 are read
+  // while those products execute, and stage s+3 is loaded into the A buffer
+  // of stage s and into r.
+  // (P = s mod 6 at compile time: A buffer P mod 3, W buffer P mod 2)
+  auto compute = [&](auto P, int s, RawStage& r) {
+    constexpr int p = decltype(P)::value;
+    uint8_t* Ta = abuf(IC<p>{});
+    uint8_t* Tw = wbuf(IC<p>{});
+    uint8_t* Na = abuf(IC<p + 1>{});
+    uint8_t* Nw = wbuf(IC<p + 1>{});
+    const bool live = s < nstages;  // (parity export: only live stages have partials)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) rd(ks + 1, aop[(ks + 1) & 1], bop[(ks + 1) & 1]);
+      if (ks < 3) {
+        rd(Ta, Tw, ks + 1, (ks + 1) & 1);
+      } else {
+        stage_barrier();
+        rd(Na, Nw, 0, 0);
+      }
 #pragma unroll
       for (int i = 0; i < kIB; ++i)
 #pragma unroll
         for (int j = 0; j < kJB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[ks & 1][i], bop[ks & 1][j], acc[i][j], 0, 0, 0);
-      if (nxt) store_part(*nxt, *r, ks, s + 1);
+      if (ks < 3) store_part(Na, Nw, r, ks);
+      if (ks == 3) group(r, s + 3, IC<p>{});
       if constexpr (!PARTIALS) {
-        // order: next operands' LDS reads, then products interleaved with the
-        // staging arithmetic, then the staging LDS writes
-        if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, kIB + kJB, 0);
+        // order: LDS reads of the next operands, then the products
+        // interleaved with the staging arithmetic, then the staging write
+        __builtin_amdgcn_sched_group_barrier(0x100, kIB + kJB, 0);
+        if (ks < 3) {
 #pragma unroll
-        for (int m = 0; m < kIB * kJB; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          for (int m = 0; m < kIB * kJB; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
       }
-      if constexpr (PARTIALS && PREC == kNvfp4) partial_store(s * 4 + ks, nstages * 4);
+      if constexpr (PARTIALS && PREC == kNvfp4) {
+        if (live) partial_store(s * 4 + ks, nstages * 4);
+      }
     }
-    if constexpr (PARTIALS && PREC == kInt4) partial_store(s, nstages);
+    if constexpr (PARTIALS && PREC == kInt4) {
+      if (live) partial_store(s, nstages);
+    }
   };
 
   // ---- main loop -------------------------------------------------------------
-  // Two raw stages in registers: the one for stage s+1 is staged into LDS in
-  // parts among the k steps of stage s, and its slot is refilled with stage
-  // s+3 right after the barrier, so each load has two stages of compute to
-  // arrive.  The steady state is straight-line code (no conditions), so the
-  // staging can be scheduled among the matrix instructions; it is unrolled
-  // by two so that every register array index is a compile-time constant (a
-  // runtime index would move the array to scratch).
+  // Loads run three stages ahead for A (a ring of three LDS buffers) and two
+  // for W (two raw stages in registers, staged into two LDS buffers).  The
+  // loop is unrolled by two so that every register array index is a
+  // compile-time constant (a runtime index would move the array to scratch).
   RawStage r0, r1;
-  load(r0, 0);
-  if (nstages > 1) load(r1, 1);
-  store(st[0], r0, 0);
-  lds_barrier();
-  if (nstages > 2) load(r0, 2);
-  int s = 0;
-  for (; s + 4 < nstages; s += 2) {
-    compute(st[0], s, &st[1], &r1);
-    lds_barrier();
-    load(r1, s + 3);
-    compute(st[1], s + 1, &st[0], &r0);
-    lds_barrier();
-    load(r0, s + 4);
-  }
-  for (; s < nstages; s += 2) {  // the last (at most four) stages
-    compute(st[0], s, s + 1 < nstages ? &st[1] : nullptr, &r1);
-    lds_barrier();
-    if (s + 3 < nstages) load(r1, s + 3);
-    if (s + 1 < nstages) {
-      compute(st[1], s + 1, s + 2 < nstages ? &st[0] : nullptr, &r0);
-      lds_barrier();
-      if (s + 4 < nstages) load(r0, s + 4);
+  group(r0, 0, IC<0>{});
+  group(r1, 1, IC<1>{});
+  // int4: per weight row the power of two 2^-F that makes every q * s_w * 2^-F
+  // an exact fp16, from the row's largest group scale (its loads overlap the
+  // first two stages' loads)
+  if constexpr (kRowExp) {
+    if (tid < kBN) {
+      // the row's scales, two per load (G64 is even: rows are 4-byte aligned)
+      const uint16_t* srow = (const uint16_t*)args.w_scales + (size_t)min(n0 + tid, N - 1) * G64;
+      float m = 0.f;
+      for (int g0 = 0; g0 < G64; g0 += 16) {
+        uint32_t v[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          if (g0 + 2 * p < G64) v[p] = *(const uint32_t*)(srow + g0 + 2 * p);
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          if (g0 + 2 * p < G64) m = fmaxf(m, fmaxf(bf16_lo(v[p]), bf16_hi(v[p])));
+      }
+      const int F = m > 0.f ? fp16_fit_exponent(m) : 0;
+      wexp[tid] = __builtin_ldexpf(1.0f, F);
+      wdown[tid] = __builtin_ldexpf(1.0f, -F);
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kWP; ++j) wdn[j] = wdown[lr + kRP * j];
   }
+#pragma unroll
+  for (int p = 0; p < 3; ++p) store_part(lds_a0, lds_w0, r0, p);
+  group(r0, 2, IC<2>{});
+  stage_barrier();  // (each wave has its stage-0 A loads: they precede the W loads it staged)
+  rd(lds_a0, lds_w0, 0, 0);
+  // Six stages per iteration (the A ring of three times the two raw register
+  // stages), all straight-line code.  Stages past the last (up to four when
+  // the stage count is not a multiple of six) load zeros and add nothing.
+  for (int s = 0; s < nstages; s += 6) {
+    compute(IC<0>{}, s, r1);
+    compute(IC<1>{}, s + 1, r0);
+    compute(IC<2>{}, s + 2, r1);
+    compute(IC<3>{}, s + 3, r0);
+    compute(IC<4>{}, s + 4, r1);
+    compute(IC<5>{}, s + 5, r0);
+  }
+  // the direct-to-LDS loads of the stages past the end are still in flight
+  __builtin_amdgcn_s_waitcnt(0);
 
   if constexpr (!PARTIALS) {
     // ---- undo the operand powers of two / apply the tensor scale -------------
@@ -409,16 +472,16 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   }
 }
 
-template <int PREC, bool PARTIALS, bool WT>
+template <int PREC, bool PARTIALS>
 static hipError_t dispatch_rank(const GemmArgs& a, hipStream_t s) {
   const unsigned tiles = (unsigned)(((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN));
   dim3 grid(tiles), block(kThreads);
   if constexpr (PARTIALS) {
-    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, 0, true, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, 0, true>), grid, block, 0, s, a);
   } else {
 #define SVDQ_K2_CASE(rb)                                                                     \
   case rb:                                                                                   \
-    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, rb, false, WT>), grid, block, 0, s, a); \
+    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, rb, false>), grid, block, 0, s, a); \
     break;
     switch (a.rank / 16) {
       SVDQ_K2_CASE(0)
@@ -439,12 +502,9 @@ static hipError_t dispatch_rank(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream) {
   const bool partials = a.partials != nullptr;
-  if (a.precision == kInt4) {
-    if (partials) return dispatch_rank<kInt4, true, false>(a, stream);
-    return a.K / 64 <= kMaxScaleG ? dispatch_rank<kInt4, false, true>(a, stream)
-                                  : dispatch_rank<kInt4, false, false>(a, stream);
-  }
-  return partials ? dispatch_rank<kNvfp4, true, false>(a, stream) : dispatch_rank<kNvfp4, false, false>(a, stream);
+  if (a.precision == kInt4)
+    return partials ? dispatch_rank<kInt4, true>(a, stream) : dispatch_rank<kInt4, false>(a, stream);
+  return partials ? dispatch_rank<kNvfp4, true>(a, stream) : dispatch_rank<kNvfp4, false>(a, stream);
 }
 
 }  // namespace svdq
