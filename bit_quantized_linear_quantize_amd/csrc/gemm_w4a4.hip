@@ -90,8 +90,11 @@ __device__ __forceinline__ int a_pos(int row, int c) { return c ^ ((row >> 1) & 
 // likewise for A row tid/8 + 64 i.
 struct RawStage {
   uint32_t w[kWP];
-  uint32_t sw[kWP];  // the scale of each W piece: nvfp4 E4M3 byte, int4 bf16 bits
-  uint32_t a[kAP];   // parity export only
+  // the scale of each W piece, kept in its loaded width (a widening right
+  // after the load would make the wave wait for the load there)
+  uint8_t sw8[kWP];    // nvfp4: E4M3 byte
+  uint16_t sw16[kWP];  // int4: bf16 bits
+  uint32_t a[kAP];     // parity export only
 };
 
 // Raw buffer descriptor over `bytes` bytes at p (sizes past 2^31 - 1 are
@@ -207,8 +210,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
 #pragma unroll
     for (int j = 0; j < kWP; ++j) {
       r.w[j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, w_off[j], s * 32, 0);
-      if constexpr (PREC == kNvfp4 && !PARTIALS) r.sw[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, ws_off[j], s * 4, 0);
-      if constexpr (PREC == kInt4 && !PARTIALS) r.sw[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, ws_off[j], s * 2, 0);
+      if constexpr (PREC == kNvfp4 && !PARTIALS) r.sw8[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, ws_off[j], s * 4, 0);
+      if constexpr (PREC == kInt4 && !PARTIALS) r.sw16[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, ws_off[j], s * 2, 0);
     }
     if constexpr (PARTIALS) {
 #pragma unroll
@@ -238,9 +241,9 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     _Float16 sc = (_Float16)(PREC == kInt4 ? 1.0f : 2.0f);
     if constexpr (!PARTIALS) {
       if constexpr (PREC == kInt4)
-        sc = (_Float16)(bf16_bits_to_f32((uint16_t)r.sw[p]) * wdn[p]);  // exact: a power of two
+        sc = (_Float16)(bf16_bits_to_f32(r.sw16[p]) * wdn[p]);  // exact: a power of two
       else
-        sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw[p], 0);
+        sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw8[p], 0);
     }
     *(f16x8*)(Tw + wrow * kWRow + lc * 16) =
         PREC == kInt4 ? int4x8_to_f16_scaled(r.w[p], sc) : e2m1x8_to_f16_scaled(r.w[p], sc);
