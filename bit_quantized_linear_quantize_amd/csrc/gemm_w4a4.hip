@@ -28,11 +28,14 @@
 //
 // Workgroup tile 256 (M) x 192 (N) -- 256 workgroups for a 4096 x 3072
 // output, one per CU -- with 8 waves (4 x 2), each wave 64 x 96 = 2 x 3 blocks
-// of 32 x 32; 64 columns of K per stage, v_mfma_f32_32x32x16_f16.  Raw stages
-// are loaded two stages ahead into registers and written to a double-buffered
-// LDS stage (padded rows: conflict-free 16-byte reads).  Tiles are visited in
-// groups of 4 M-tiles, mapped so that the workgroups on one XCD share A and W
-// tiles in its L2.
+// of 32 x 32; 64 columns of K per stage, v_mfma_f32_32x32x16_f16.  A goes
+// from memory straight into a ring of three LDS stage buffers
+// (buffer_load ... lds, rows of 128 bytes with XOR-swizzled 16-byte chunks:
+// conflict-free operand reads), issued three stages ahead.  W codes and
+// scales are loaded two stages ahead into registers, converted, and written
+// to one of two padded LDS stage buffers among the matrix instructions of the
+// previous stage.  Tiles are visited in groups of 4 M-tiles, mapped so that
+// the workgroups on one XCD share A and W tiles in its L2.
 // Low-rank up: lora_act (fp32) split into bf16 hi + lo, times lora_up, with
 // bf16 matrix instructions accumulating into the same registers.
 //
