@@ -12,7 +12,12 @@ Also measured in the same run (reported under "extra"):
     quantize_act_lora_down and gemm_w4a4_lora_up, from which the roofline
     object of the dominant kernel (gemm_w4a4_lora_up) is computed;
   * awq_w4a16 at M in {1, 2, 16}, K=3072, N=18432, rotating over 12 weight
-    copies (382 MB > the 256 MB last-level cache) so weights come from HBM.
+    copies (382 MB > the 256 MB last-level cache) so weights come from HBM;
+  * the nvfp4 MLP pair 3072 -> 12288 -> 3072 at M=4096 (exact-erf GELU on the
+    bf16 up output, a torch op, between the two library calls);
+  * the DiT stack per pass: 24 blocks of QKV 3072->9216, out 3072->3072, MLP
+    up/GELU/down (svdq nvfp4, rank 32, 4096 tokens) and the adaLN modulation
+    linear 3072->18432 (awq_w4a16, one token), 8 passes (--no-stack skips it).
 The weights of the timed legs are random but valid packed layers (prepared
 weight values do not change the work); parity with the oracle is the job of
 tests/.  The cpu_baseline leg times the CPU oracle on the same inputs.
@@ -60,6 +65,103 @@ def measured_traffic(kernel, workload):
     if not rec or rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+def bench_mlp_pair(bq, S, torch, np, x, M, K, rank, stream, hidden=12288, reps=50):
+    """The nvfp4 MLP pair at M tokens: up K -> hidden, exact-erf GELU on the bf16
+    output (a torch op between the two library calls), down hidden -> K."""
+    import torch.nn.functional as Fn
+    log("timing the nvfp4 MLP pair ...")
+    r_up, r_dn = S.streams(11, 2)
+    up = bq.SVDQLinear.from_numpy(S.random_svdq_layer(hidden, K, "nvfp4", rank, r_up))
+    down = bq.SVDQLinear.from_numpy(S.random_svdq_layer(K, hidden, "nvfp4", rank, r_dn))
+    ws_up = torch.empty(up.workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    ws_dn = torch.empty(down.workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    h = torch.empty((M, hidden), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    g = [Fn.gelu(h)]
+    f_up = lambda: up(x, out=h, workspace=ws_up)
+    f_gelu = lambda: g.__setitem__(0, Fn.gelu(h))
+    f_dn = lambda: down(g[0], out=y, workspace=ws_dn)
+
+    def pair():
+        f_up()
+        f_gelu()
+        f_dn()
+    for _ in range(10):
+        pair()
+    t_up, t_gelu, t_dn = (time_events(f, reps, stream) for f in (f_up, f_gelu, f_dn))
+    t_pair = time_events(pair, reps, stream)
+    ops = 2.0 * M * hidden * K * 2
+    return {"up_us": round(t_up * 1e3, 2), "gelu_us": round(t_gelu * 1e3, 2), "down_us": round(t_dn * 1e3, 2),
+            "pair_us": round(t_pair * 1e3, 2),
+            "svdq_TOPS": round(ops / ((t_up + t_dn) * 1e-3) / 1e12, 1),
+            "pair_TOPS_incl_gelu": round(ops / (t_pair * 1e-3) / 1e12, 1)}
+
+
+def bench_stack(bq, S, torch, np, M, rank, stream):
+    """DiT stack per pass: every block runs QKV, out, MLP up, GELU, MLP down (svdq
+    nvfp4, rank 32, M tokens, each linear on its own pre-generated activation,
+    down on GELU(up)) and the adaLN modulation linear (awq_w4a16, one token).
+    Each layer shape is generated once and copied into one device buffer per
+    block."""
+    import torch.nn.functional as Fn
+    log("timing the DiT stack ...")
+    blocks, passes = S.STACK["blocks"], S.STACK["passes"]
+    shapes = S.STACK_LAYERS
+    rs = S.streams(13, len(shapes) + 6)
+    layers = {}
+    for i, (name, Kl, Nl) in enumerate(shapes):
+        base = S.random_svdq_layer(Nl, Kl, "nvfp4", rank, rs[i])
+        layers[name] = [bq.SVDQLinear.from_numpy(base) for _ in range(blocks)]
+    Ka, Na = S.STACK["adaln"]
+    ada_base = S.random_awq_layer(Na, Ka, rs[len(shapes)])
+    ada = [bq.AWQLinear.from_numpy(ada_base) for _ in range(blocks)]
+
+    def act(rows, cols, r):
+        return torch.from_numpy(S.activations(rows, cols, round(0.01 * cols), r).view(np.int16).copy()).view(
+            torch.bfloat16).cuda()
+    hid = S.STACK["hidden"]
+    xq, xo, xu = (act(M, hid, rs[len(shapes) + 1 + i]) for i in range(3))
+    xa = act(1, Ka, rs[len(shapes) + 4])
+    ws = {k: torch.empty(max(layers[n][0].workspace_bytes(M) for n, kk, _ in shapes if kk == k),
+                         dtype=torch.uint8, device="cuda") for k in {kk for _, kk, _ in shapes}}
+    outs = {n: torch.empty((M, Nl), dtype=torch.bfloat16, device="cuda") for n, _, Nl in shapes}
+    oa = torch.empty((1, Na), dtype=torch.bfloat16, device="cuda")
+    k_of = {n: kk for n, kk, _ in shapes}
+    g = [None]
+
+    def svdq_pass():
+        for b in range(blocks):
+            layers["qkv"][b](xq, out=outs["qkv"], workspace=ws[k_of["qkv"]])
+            layers["out"][b](xo, out=outs["out"], workspace=ws[k_of["out"]])
+            layers["up"][b](xu, out=outs["up"], workspace=ws[k_of["up"]])
+            g[0] = Fn.gelu(outs["up"])
+            layers["down"][b](g[0], out=outs["down"], workspace=ws[k_of["down"]])
+
+    def awq_pass():
+        for b in range(blocks):
+            ada[b](xa, out=oa)
+
+    def full_pass():
+        for b in range(blocks):
+            ada[b](xa, out=oa)
+            layers["qkv"][b](xq, out=outs["qkv"], workspace=ws[k_of["qkv"]])
+            layers["out"][b](xo, out=outs["out"], workspace=ws[k_of["out"]])
+            layers["up"][b](xu, out=outs["up"], workspace=ws[k_of["up"]])
+            g[0] = Fn.gelu(outs["up"])
+            layers["down"][b](g[0], out=outs["down"], workspace=ws[k_of["down"]])
+    full_pass()
+    t_full = time_events(full_pass, passes, stream)
+    t_svdq = time_events(svdq_pass, passes, stream)
+    t_awq = time_events(awq_pass, passes, stream)
+    svdq_ops = blocks * sum(2.0 * M * Nl * Kl for _, Kl, Nl in shapes)
+    awq_bytes = blocks * (Na * Ka // 2 + 2 * Na * (Ka // 64) * 2 + Ka * 2 + Na * 4)
+    return {"blocks": blocks, "passes": passes, "pass_ms": round(t_full, 3),
+            "svdq_and_gelu_pass_ms": round(t_svdq, 3), "awq_pass_ms": round(t_awq, 3),
+            "svdq_TOPS_incl_gelu": round(svdq_ops / (t_svdq * 1e-3) / 1e12, 1),
+            "awq_GBps": round(awq_bytes / (t_awq * 1e-3) / 1e9, 1),
+            "svdq_ops_per_pass": svdq_ops, "awq_bytes_per_pass": awq_bytes}
 
 
 def time_events(fn, steps, stream):
@@ -134,7 +236,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000,
                     help="untimed steps first; about 0.1 s, enough for the GPU clock to settle")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--no-extra", action="store_true", help="skip the nvfp4 and AWQ legs")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the nvfp4, AWQ, MLP-pair and DiT-stack legs")
+    ap.add_argument("--no-stack", action="store_true", help="skip the DiT-stack leg")
     ap.add_argument("--only", choices=sorted(ONLY_LEGS),
                     help="run one kernel --steps times and exit (for rocprofv3 counter passes)")
     args = ap.parse_args()
@@ -246,6 +350,12 @@ def main():
         extra["awq_w4a16_N18432_K3072"] = awq
         del layers
         torch.cuda.empty_cache()
+
+        extra["mlp_pair_nvfp4_3072_12288_3072"] = bench_mlp_pair(bq, S, torch, np, x, M, K, rank, stream)
+        torch.cuda.empty_cache()
+        if not args.no_stack:
+            extra["dit_stack_nvfp4"] = bench_stack(bq, S, torch, np, M, rank, stream)
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:

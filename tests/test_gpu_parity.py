@@ -327,6 +327,45 @@ def test_awq_shapes(M, K, N):
     assert_output(run_awq(x, lay), L.awq_linear_ref(x, lay), f"awq M={M} K={K} N={N}")
 
 
+# ------------------------------------------------------------------ MLP pair and stack shapes
+# Full-size layers, checked on a sample of rows (first, middle and last tiles,
+# ragged positions) against the oracle on the same input.
+SAMPLE_ROWS = np.r_[0:40, 255:258, 2047:2060, 4090:4096]
+
+
+@pytest.fixture(scope="module")
+def mlp_up():
+    c = S.config2()
+    x = c["proj"]["x"]
+    lay = prepared(x, c["w_up"], c["b_up"], "nvfp4", 32, smooth="calibrated")
+    h = run_linear(x, lay)
+    return c, x, lay, h
+
+
+def test_mlp_pair_up_config2_sampled(mlp_up):
+    # nvfp4 MLP up-projection 3072 -> 12288 at M = 4096
+    _, x, lay, h = mlp_up
+    assert_output(h[SAMPLE_ROWS], L.svdq_linear_ref(x[SAMPLE_ROWS], lay), "mlp up 3072->12288")
+
+
+def test_mlp_pair_down_config2_sampled(mlp_up):
+    # down-projection 12288 -> 3072 on GELU of the up output (exact erf on the
+    # bf16 tensor, a torch op between the two library calls)
+    c, _, _, h = mlp_up
+    g = host_bits(torch.nn.functional.gelu(h))
+    lay = prepared(g, c["w_down"], c["b_down"], "nvfp4", 32, smooth="calibrated")
+    y = run_linear(g, lay)
+    assert_output(y[SAMPLE_ROWS], L.svdq_linear_ref(g[SAMPLE_ROWS], lay), "mlp down 12288->3072")
+
+
+def test_stack_qkv_sampled():
+    # the DiT stack's fused QKV shape, 3072 -> 9216 nvfp4 rank 32 at 4096 tokens
+    x, w, b = S.svdq_problem(4096, 3072, 9216, seed=5, n_outliers=31)
+    lay = prepared(x, w, b, "nvfp4", 32, smooth="calibrated")
+    y = run_linear(x, lay)
+    assert_output(y[SAMPLE_ROWS], L.svdq_linear_ref(x[SAMPLE_ROWS], lay), "stack qkv 3072->9216")
+
+
 def test_awq_config3():
     c = S.config3()
     lay = L.prepare_awq_layer(c["w"], c["bias"])
