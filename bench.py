@@ -164,6 +164,36 @@ def bench_stack(bq, S, torch, np, M, rank, stream):
             "svdq_ops_per_pass": svdq_ops, "awq_bytes_per_pass": awq_bytes}
 
 
+def bench_mfma_peak(torch, stream, iters=20000):
+    """Measured rate of v_mfma_f32_32x32x16_f16 (the product kernel's
+    instruction): one 8-wave workgroup per CU, 8 independent accumulators per
+    wave, non-constant operands.  The published dense peak (2.5 PFLOP/s)
+    corresponds to 2.4 GHz; the clock implied by the measured rate is
+    reported beside it."""
+    import ctypes
+    path = os.path.join(ROOT, "bit_quantized_linear_quantize_amd", "lib", "libsvdq_peak.so")
+    if not os.path.exists(path):
+        return None
+    log("timing the matrix-instruction peak ...")
+    lib = ctypes.CDLL(path)
+    lib.svdq_peak_mfma_f16.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.svdq_peak_mfma_f16.restype = ctypes.c_int
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+
+    def run():
+        if lib.svdq_peak_mfma_f16(iters, blocks, sink.data_ptr(), stream.cuda_stream) != 0:
+            raise RuntimeError("peak probe launch failed")
+    for _ in range(3):
+        run()
+    ms = time_events(run, 5, stream)
+    flops = blocks * 8 * iters * 8 * 2.0 * 32 * 32 * 16
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"instruction": "v_mfma_f32_32x32x16_f16", "measured_TFLOPs": round(tflops, 1),
+            "implied_clock_GHz": round(2.4 * tflops / PEAK["f16"], 3),
+            "published_dense_peak_TFLOPs": PEAK["f16"], "workgroups": blocks, "rounds_per_wave": iters}
+
+
 def time_events(fn, steps, stream):
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
@@ -351,6 +381,11 @@ def main():
         del layers
         torch.cuda.empty_cache()
 
+        peak = bench_mfma_peak(torch, stream)
+        if peak:
+            extra["mfma_f16_peak"] = peak
+            roofline["measured_instruction_peak"] = peak["measured_TFLOPs"]
+            roofline["frac_of_measured_peak"] = round(k2_tops / peak["measured_TFLOPs"], 4)
         extra["mlp_pair_nvfp4_3072_12288_3072"] = bench_mlp_pair(bq, S, torch, np, x, M, K, rank, stream)
         torch.cuda.empty_cache()
         if not args.no_stack:

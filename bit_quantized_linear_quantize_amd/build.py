@@ -14,6 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libsvdq_w4a4.so")
+# benchmark helper (measured matrix-instruction peak), not part of the layer's interface
+PEAK_LIB = os.path.join(LIBDIR, "libsvdq_peak.so")
+PEAK_SOURCES = ["mfma_peak.hip"]
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 SOURCES = ["api.cpp", "quantize_act.hip", "gemm_w4a4.hip", "awq_gemv.hip"]
 
@@ -42,10 +45,11 @@ def build(verbose=False):
         return obj
 
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
+        objs = list(ex.map(compile_one, SOURCES + PEAK_SOURCES))
+    for lib, o in ((LIB, objs[:len(SOURCES)]), (PEAK_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + o)
+        os.replace(tmp, lib)
     if verbose:
         print("built", LIB)
     return LIB

@@ -41,6 +41,13 @@ def test_header_symbols_exported(L):
         assert getattr(L, n) is not None
 
 
+def test_peak_probe_library_exports(L):
+    # the benchmark helper (measured matrix-instruction peak) is its own library
+    path = os.path.join(os.path.dirname(bq.LIB_PATH), "libsvdq_peak.so")
+    assert os.path.exists(path)
+    assert ctypes.CDLL(path).svdq_peak_mfma_f16 is not None
+
+
 def _fake(base):
     return ctypes.c_void_p(base)
 
