@@ -68,7 +68,7 @@ __device__ __forceinline__ u32x4 awq_x_order(u32x4 v) {
 
 // MT: rows of X per workgroup (1, 2, 4 or 16); D: steps in flight per wave.
 //
-// Dynamic LDS: the workgroup's scale table float2 [32 rows][G] holding
+// Dynamic LDS: the workgroup's scale table float2 [32 rows][G + 2] holding
 // (s, -s (128 + z)) per weight row and group, then per wave a staged step of
 // codes [32 rows][kAwqRowPitch] and of X [MT rows][kAwqXPitch].
 template <int MT, int D, bool WIDE>
@@ -88,7 +88,9 @@ void awq_w4a16_kernel(AwqArgs args) {
   const int n0 = blockIdx.x * 32;
 
   float2* stab = (float2*)smem;
-  uint8_t* ws = smem + (size_t)32 * G * 8 + (size_t)wave * (32 * kAwqRowPitch + MT * kAwqXPitch);
+  const int G2 = G + 2;  // scale-table row pitch in float2: 400 bytes at G = 48, so the 16
+                        // rows one read covers fall on different banks
+  uint8_t* ws = smem + (size_t)32 * G2 * 8 + (size_t)wave * (32 * kAwqRowPitch + MT * kAwqXPitch);
   uint8_t* xs = ws + 32 * kAwqRowPitch;
 
   const int c = lane & 15;
@@ -121,7 +123,8 @@ void awq_w4a16_kernel(AwqArgs args) {
       if (it < items) {
         const float sl = bf16_lo(sraw[u]), sh = bf16_hi(sraw[u]);
         const float zl = bf16_lo(zraw[u]), zh = bf16_hi(zraw[u]);
-        *(float4*)(stab + 2 * it) = float4{sl, -sl * (128.0f + zl), sh, -sh * (128.0f + zh)};
+        const int row = it / (G / 2), pr = it - row * (G / 2);
+        *(float4*)(stab + row * G2 + 2 * pr) = float4{sl, -sl * (128.0f + zl), sh, -sh * (128.0f + zh)};
       }
     }
   };
@@ -187,8 +190,8 @@ void awq_w4a16_kernel(AwqArgs args) {
     const uint8_t* xp = xs + min(c, MT - 1) * kAwqXPitch + i * 128 + kq * 32;
     const bf16x8 x0 = __builtin_bit_cast(bf16x8, *(const u32x4*)xp);
     const bf16x8 x1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xp + 16));
-    const float2 pa = stab[c * G + g];
-    const float2 pb = stab[(16 + c) * G + g];
+    const float2 pa = stab[c * G2 + g];
+    const float2 pb = stab[(16 + c) * G2 + g];
     // k step 0 uses code bytes 0..3 (k = 16 kq + 0..7), step 1 bytes 4..7
     f32x4 tA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, awq_operand(wa[0]), zero4, 0, 0, 0);
     f32x4 tB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, awq_operand(wb[0]), zero4, 0, 0, 0);
@@ -281,7 +284,7 @@ void awq_w4a16_kernel(AwqArgs args) {
 template <int MT, int D>
 static hipError_t launch_awq_mt(const AwqArgs& a, hipStream_t stream) {
   const int G = (int)(a.K / 64);
-  const size_t lds = (size_t)32 * G * 8 + (size_t)kAwqWaves * (32 * kAwqRowPitch + MT * kAwqXPitch);
+  const size_t lds = (size_t)32 * (G + 2) * 8 + (size_t)kAwqWaves * (32 * kAwqRowPitch + MT * kAwqXPitch);
   dim3 grid((unsigned)(a.N / 32), (unsigned)((a.M + MT - 1) / MT));
   if (G <= 64)
     hipLaunchKernelGGL((awq_w4a16_kernel<MT, D, false>), grid, dim3(256), lds, stream, a);
