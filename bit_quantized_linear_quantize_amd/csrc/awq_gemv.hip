@@ -6,27 +6,34 @@
 // format: unsigned codes q (0..15), per-group bf16 scale s and integer
 // zero-point z, W = (q - z) s;  Y = X W^T + bias with fp32 accumulation.
 //
-// gfx950 design -- bandwidth-bound: 4.5 bits per weight streamed once per 16
-// rows of X.
-// * A workgroup owns 32 weight rows (output columns) and 16 rows of X; its 4
-//   waves split K into four contiguous group ranges.  Every wave issues all the
-//   code, scale and zero-point loads of its range before computing, and the
-//   register budget (<= 168 VGPRs, 3 waves per SIMD) keeps every workgroup of
-//   an N = 18432 layer resident at once, so the whole weight matrix is in
-//   flight together and no second round of workgroups forms a tail.
+// gfx950 design -- bandwidth-bound: 4.5 bits per weight streamed once per MT
+// rows of X (MT = 2, 4 or 16; one token runs in the 2-row tile, whose second
+// row is never stored).
+// * A workgroup owns 32 weight rows (output columns) and MT rows of X; its 4
+//   waves split K into four contiguous group ranges.  The workgroup first
+//   builds its (s, -s (128 + z)) table in LDS.
+// * Each wave streams its range in steps of 4 groups, with coalesced loads
+//   (lane l: 16 bytes of weight rows l/8 + 8j, so each row contributes 128
+//   contiguous bytes per instruction; non-temporal, the weights are read
+//   once), and moves every step into its own LDS rows in the layout the
+//   matrix instruction reads.  The loads of step s + 1 are issued as soon as
+//   step s is in LDS, before its products: one step in flight per wave.
+//   Deeper prefetch measured slower -- more bytes in flight lengthen every
+//   load's latency, and a step's products wait for its data either way.
 // * Matrix instruction 16x16x32 bf16 (D = 16 rows of X x 16 weight rows): it
 //   consumes 512 weights per 4 passes, half the matrix-core time of the 32x32
 //   shape per weight, which matters at M <= 16 where most of D is padding.
 //   Lane (c = lane%16, kq = lane/16) holds, per group and 32-wide k step s,
 //   the k values 16 kq + 8 s + 0..7 of weight row c (4 code bytes, so one
-//   8-byte load covers a group) and the same k of X row c.
+//   8-byte LDS read covers a group) and the same k of X row c.
 // * Codes become bf16 operands 128 + q (0x4300 | q is the bit pattern of
-//   128 + q) with one v_perm and one OR per pair.  A second operand holds
-//   -(128 + z) in every slot, so the same accumulator collects
-//   sum_k x (128 + q) - sum_k x (128 + z) = sum_k x (q - z): exact bf16
-//   products, fp32 sums; the scale costs one FMA per output: acc += t * s.
-// * Rows of X beyond M are zero (their loads are masked off).  The four
-//   K-range partials are summed in LDS in a fixed order.
+//   128 + q) with one v_perm and one OR per pair.  A second operand holds 1
+//   in every slot, so a third product collects sum_k x over the group, and
+//   sum_k x (q - z) s = s sum_k x (128 + q) - s (128 + z) sum_k x: exact bf16
+//   products, fp32 sums, two FMAs per output and group.
+// * Rows of X beyond M read row M - 1 (each output row depends on its own X
+//   row only, and rows beyond M are never stored).  The four K-range partials
+//   are summed in LDS in a fixed order.
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -66,7 +73,7 @@ __device__ __forceinline__ u32x4 awq_x_order(u32x4 v) {
   return r;
 }
 
-// MT: rows of X per workgroup (1, 2, 4 or 16); D: steps in flight per wave.
+// MT: rows of X per workgroup (2, 4 or 16); D: steps in flight per wave.
 //
 // Dynamic LDS: the workgroup's scale table float2 [32 rows][G + 2] holding
 // (s, -s (128 + z)) per weight row and group, then per wave a staged step of
@@ -74,7 +81,8 @@ __device__ __forceinline__ u32x4 awq_x_order(u32x4 v) {
 template <int MT, int D, bool WIDE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 16 ? 2 : 3, 3)))
 void awq_w4a16_kernel(AwqArgs args) {
-  constexpr int XV = MT == 1 ? 1 : MT / 2;  // X loads per lane and step (8 bytes if MT == 1, else 16)
+  static_assert(MT % 2 == 0, "X rows are loaded in pairs");
+  constexpr int XV = MT / 2;  // 16-byte X loads per lane and step
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float part[kAwqWaves][16][33];
   const int tid = threadIdx.x;
@@ -134,35 +142,27 @@ void awq_w4a16_kernel(AwqArgs args) {
   // weight rows n0 + l/8 + 8j, j = 0..3 -- 128 contiguous bytes per row
   const int q8 = lane & 7;
   const uint8_t* wstream = (const uint8_t*)args.w_codes + (size_t)(n0 + (lane >> 3)) * K2 + (q8 & 1) * 16;
-  // X: MT rows x 256 k of the step; with MT == 1 lane l holds k 4l..4l+3,
-  // else load v covers rows 2v + l/32, k 8 (l%32) .. +7.  Rows beyond M read
-  // row M - 1: each output row depends on its own X row only, and rows
-  // beyond M are never stored.
+  // X: MT rows x 256 k of the step; load v covers rows 2v + l/32, k 8 (l%32)
+  // .. +7.  Rows beyond M read row M - 1.
   const uint16_t* xbase = (const uint16_t*)args.x + (size_t)m0 * K;
 
   // D steps in flight; all loads of a step (codes and X) are issued together,
   // so the in-order memory counter releases whole steps.  Past the wave's
   // range (a partial last step, or the prologue of a short range) the loads
   // re-read the last valid group.
-  typedef typename std::conditional<MT == 1, u32x2, u32x4>::type XVec;
   u32x4 wr[D][4];
-  XVec xr[D][XV];
+  u32x4 xr[D][XV];
   auto issue = [&](int slot, int step) {
     const int gs = g0 + step * kAwqStepG;
     const int gw = min(gs + (q8 >> 1), g1 - 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      wr[slot][j] = *(const u32x4*)(wstream + (size_t)(8 * j) * K2 + (size_t)gw * 32);
-    if constexpr (MT == 1) {
-      const int g = min(gs + (lane >> 4), g1 - 1);
-      xr[slot][0] = *(const u32x2*)(xbase + (size_t)g * 64 + (lane & 15) * 4);
-    } else {
+      wr[slot][j] = __builtin_nontemporal_load((const u32x4*)(wstream + (size_t)(8 * j) * K2 + (size_t)gw * 32));
 #pragma unroll
-      for (int v = 0; v < XV; ++v) {
-        const int r = min(2 * v + (lane >> 5), rows - 1);
-        const int g = min(gs + ((lane & 31) >> 3), g1 - 1);
-        xr[slot][v] = *(const u32x4*)(xbase + (size_t)r * K + (size_t)g * 64 + (lane & 7) * 8);
-      }
+    for (int v = 0; v < XV; ++v) {
+      const int r = min(2 * v + (lane >> 5), rows - 1);
+      const int g = min(gs + ((lane & 31) >> 3), g1 - 1);
+      xr[slot][v] = *(const u32x4*)(xbase + (size_t)r * K + (size_t)g * 64 + (lane & 7) * 8);
     }
   };
   // always in bounds (clamped to the last group), so issued unconditionally:
@@ -200,7 +200,7 @@ void awq_w4a16_kernel(AwqArgs args) {
     tB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, awq_operand(wb[1]), tB, 0, 0, 0);
     xsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, ones, xsum, 0, 0, 0);
     // sum_k x (q - z) s = s sum_k x (128 + q) - s (128 + z) sum_k x.  D row
-    // kq * 4 + j sits in register j, so with MT < 4 only registers j < MT
+    // kq * 4 + j sits in register j, so with MT = 2 only registers 0 and 1
     // carry rows of X (in lanes kq == 0); the others are never stored.
 #pragma unroll
     for (int j = 0; j < (MT < 4 ? MT : 4); ++j) {
@@ -217,19 +217,9 @@ void awq_w4a16_kernel(AwqArgs args) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *(u32x4*)(ws + (8 * j + (lane >> 3)) * kAwqRowPitch + q8 * 16) = wr[slot][j];
-    if constexpr (MT == 1) {
-      // lanes 2t, 2t + 1 hold k 8t..8t+3 and 8t+4..8t+7
-      const u32x2 v = xr[slot][0];
-      const uint32_t even = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);  // (x0, x2) / (x4, x6)
-      const uint32_t odd = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);   // (x1, x3) / (x5, x7)
-      uint32_t* dst = (uint32_t*)(xs + (lane >> 1) * 16 + (lane & 1) * 4);
-      dst[0] = even;
-      dst[2] = odd;
-    } else {
 #pragma unroll
-      for (int v = 0; v < XV; ++v)
-        *(u32x4*)(xs + (2 * v + (lane >> 5)) * kAwqXPitch + (lane & 31) * 16) = awq_x_order(xr[slot][v]);
-    }
+    for (int v = 0; v < XV; ++v)
+      *(u32x4*)(xs + (2 * v + (lane >> 5)) * kAwqXPitch + (lane & 31) * 16) = awq_x_order(xr[slot][v]);
   };
 
   if (nsteps > 0) {
@@ -239,10 +229,10 @@ void awq_w4a16_kernel(AwqArgs args) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         stage(d);
+        issue(d, s0 + D + d);
         const int gs = g0 + (s0 + d) * kAwqStepG;
 #pragma unroll
         for (int i = 0; i < kAwqStepG; ++i) group(gs + i, i);
-        issue(d, s0 + D + d);
       }
     }
     // tail: fewer than 2 D steps left, the first D of them in flight
@@ -251,11 +241,11 @@ void awq_w4a16_kernel(AwqArgs args) {
       const int step = s0 + d;
       if (step < nsteps) {
         stage(d % D);
+        if (d < D && step + D < nsteps) issue(d, step + D);
         const int gs = g0 + step * kAwqStepG;
 #pragma unroll
         for (int i = 0; i < kAwqStepG; ++i)
           if (gs + i < g1) group(gs + i, i);
-        if (d < D && step + D < nsteps) issue(d, step + D);
       }
     }
   }
@@ -294,10 +284,9 @@ static hipError_t launch_awq_mt(const AwqArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream) {
-  if (a.M == 1) return launch_awq_mt<1, 2>(a, stream);
-  if (a.M == 2) return launch_awq_mt<2, 2>(a, stream);
-  if (a.M <= 4) return launch_awq_mt<4, 2>(a, stream);
-  return launch_awq_mt<16, 2>(a, stream);
+  if (a.M <= 2) return launch_awq_mt<2, 1>(a, stream);
+  if (a.M <= 4) return launch_awq_mt<4, 1>(a, stream);
+  return launch_awq_mt<16, 1>(a, stream);
 }
 
 }  // namespace svdq

@@ -44,6 +44,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
 }
 
+// Raw buffer descriptor over `bytes` bytes at p (sizes past 2^31 - 1 are
+// clamped: a tile never addresses that far from its base).  Loads at offsets
+// at or past `bytes` return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_t bytes) {
+  const int n = bytes > 0x7fffffffu ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for the
 // wave's outstanding global loads (its release fence covers global memory),
 // which would stall a software pipeline whose prefetches are still in flight.

@@ -100,13 +100,6 @@ struct RawStage {
   uint32_t a[kAP];     // parity export only
 };
 
-// Raw buffer descriptor over `bytes` bytes at p (sizes past 2^31 - 1 are
-// clamped: a tile never addresses that far from its base).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_t bytes) {
-  const int n = bytes > 0x7fffffffu ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
-}
-
 // Logical tile of this workgroup: consecutive workgroups land on different
 // XCDs, so first gather the ids that share an XCD, then walk groups of
 // kGroupM M-tiles column by column.
