@@ -39,6 +39,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats -> packed bf16 pair (RNE), low half = a, with the hardware
+// pair conversion (finite inputs).
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 // Two floats -> packed bf16 pair (RNE), low half = a.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);

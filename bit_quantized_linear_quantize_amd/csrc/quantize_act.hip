@@ -93,8 +93,8 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
     }
   };
   // int4: the group (the four lanes q = 0..3 of the row) scale, returned as
-  // bf16 bits, and the lane's 16 codes
-  auto quant_int4 = [&](const float* xh, uint32_t& cw0, uint32_t& cw1) -> uint32_t {
+  // bf16 bits (0 for a zero group), and 1/s (0 for a zero group)
+  auto int4_scale = [&](const float* xh, float& inv) -> uint32_t {
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
@@ -102,7 +102,11 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
     amax = wave_max_xor(amax, 32);
     const bool zero = !(amax >= kTiny);
     const uint32_t sbits = zero ? 0u : f32_to_bf16_bits(__fdiv_rn(amax, 7.0f));
-    const float inv = zero ? 0.f : __fdiv_rn(1.0f, __uint_as_float(sbits << 16));
+    inv = zero ? 0.f : __fdiv_rn(1.0f, __uint_as_float(sbits << 16));
+    return sbits;
+  };
+  // int4: the lane's 16 sign-magnitude codes of q = rne(x / s)
+  auto int4_codes = [&](const float* xh, float inv, uint32_t sbits, uint32_t& cw0, uint32_t& cw1) {
     cw0 = 0;
     cw1 = 0;
 #pragma unroll
@@ -115,9 +119,22 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
       if (i < 8) cw0 |= nib << (4 * i);
       else cw1 |= nib << (4 * (i - 8));
     }
-    cw0 = zero ? 0u : cw0;
-    cw1 = zero ? 0u : cw1;
-    return sbits;
+    cw0 = sbits == 0u ? 0u : cw0;
+    cw1 = sbits == 0u ? 0u : cw1;
+  };
+  // int4, product operand with row exponent 0: q * s for 8 of the lane's
+  // values, q = rne(x / s) (|q| <= 7), formed directly: the fp32 product is
+  // exact, and so is its fp16 value whenever 2^-17 <= s < 2^13 (at most 11
+  // significant bits, a multiple of 2^-24, below 2^16)
+  auto int4_qs_f16x8 = [&](const float* xh, float inv, float sv) -> u32x4 {
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float a = __fmul_rn(__builtin_rintf(__fmul_rn(xh[2 * p], inv)), sv);
+      const float b = __fmul_rn(__builtin_rintf(__fmul_rn(xh[2 * p + 1], inv)), sv);
+      r[p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+    }
+    return r;
   };
 
   f32x4 acc[NB];
@@ -159,7 +176,8 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
         // ---- quantize -----------------------------------------------------
         uint32_t cw0 = 0, cw1 = 0;
         if constexpr (PREC == kInt4) {
-          const uint32_t sbits = quant_int4(xh, cw0, cw1);
+          float inv;
+          const uint32_t sbits = int4_scale(xh, inv);
           const float sv = __uint_as_float(sbits << 16);
           if constexpr (LINEAR) {
             // speculatively with row exponent 0: q * s is an exact fp16
@@ -168,13 +186,13 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
             smax = fmaxf(smax, sv);
             if (sbits != 0u) smin = fminf(smin, sv);
             if (row_ok) {
-              const _Float16 s16 = (_Float16)sv;
               _Float16* dst = (_Float16*)args.act_f16 + (size_t)row * K + k0;
-              *(f16x8*)dst = int4x8_to_f16_scaled(cw0, s16);
-              *(f16x8*)(dst + 8) = int4x8_to_f16_scaled(cw1, s16);
+              *(u32x4*)dst = int4_qs_f16x8(xh, inv, sv);
+              *(u32x4*)(dst + 8) = int4_qs_f16x8(xh + 8, inv, sv);
             }
-          } else if (row_ok && q == 0) {
-            ((uint16_t*)args.scales)[(size_t)row * (K >> 6) + c] = (uint16_t)sbits;
+          } else {
+            int4_codes(xh, inv, sbits, cw0, cw1);
+            if (row_ok && q == 0) ((uint16_t*)args.scales)[(size_t)row * (K >> 6) + c] = (uint16_t)sbits;
           }
         } else {
           float amax = 0.f;
@@ -213,14 +231,18 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
         if constexpr (RB > 0) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            bf16x8 ahi, alo;
+            // hi = bf16(v), lo = bf16(v - hi), both round to nearest even,
+            // converted two at a time
+            u32x4 hi4, lo4;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float v = xh[8 * j + i];
-              const __bf16 hb = (__bf16)v;
-              ahi[i] = hb;
-              alo[i] = (__bf16)(v - (float)hb);
+            for (int p = 0; p < 4; ++p) {
+              const float a = xh[8 * j + 2 * p], b = xh[8 * j + 2 * p + 1];
+              const uint32_t h = bf16x2_rne(a, b);
+              hi4[p] = h;
+              lo4[p] = bf16x2_rne(__fsub_rn(a, bf16_lo(h)), __fsub_rn(b, bf16_hi(h)));
             }
+            const bf16x8 ahi = __builtin_bit_cast(bf16x8, hi4);
+            const bf16x8 alo = __builtin_bit_cast(bf16x8, lo4);
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
               const bf16x8 bop = __builtin_bit_cast(bf16x8, lbuf[p][b][j]);
@@ -262,7 +284,9 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
         float xh[16];
         smooth16(xb, k0, xh);
         uint32_t cw0, cw1;
-        const uint32_t sbits = quant_int4(xh, cw0, cw1);
+        float inv;
+        const uint32_t sbits = int4_scale(xh, inv);
+        int4_codes(xh, inv, sbits, cw0, cw1);
         const _Float16 s16 = (_Float16)(__uint_as_float(sbits << 16) * down);  // exact power-of-two scaling
         *(f16x8*)(dst + k0) = int4x8_to_f16_scaled(cw0, s16);
         *(f16x8*)(dst + k0 + 8) = int4x8_to_f16_scaled(cw1, s16);
