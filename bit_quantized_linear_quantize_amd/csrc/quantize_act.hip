@@ -13,8 +13,9 @@
 //          code = E2M1(fl32(X_hat * fl32(1/dec(s8)))), tensor scale 1;
 //   groups with amax < 2^-100 (or a zero E4M3 scale) get scale 0 and codes 0.
 //
-// Work layout (gfx950, wave64): a workgroup of 8 waves owns 16 token rows and
-// all K; wave w handles the 64-column chunks w, w+8, w+16, ...  Inside a wave,
+// Work layout (gfx950, wave64): a workgroup of W waves owns 16 token rows and
+// all K (W = 16 for ranks up to 32, else 8); wave w handles the 64-column
+// chunks w, w+W, w+2W, ...  Inside a wave,
 // lane (r = lane%16, q = lane/16) holds 16 consecutive columns 64c+16q..+15 of
 // row r.  That is exactly one nvfp4 group per lane, a quarter of an int4 group
 // (amax then needs two cross-lane max steps), and the A-operand slot group q
@@ -40,22 +41,28 @@
 
 namespace svdq {
 
-constexpr int kK1Waves = 8;
 constexpr int kK1Rows = 16;
 
+// Waves per workgroup (they split K) and 64-column chunks in flight per wave.
+// Ranks up to 32 run 16 waves (4 per SIMD, within 128 VGPRs) with two chunks
+// in flight; larger ranks need more registers for the low-rank operands and
+// run 8 waves.
 template <int RB>
-struct K1Prefetch {
-  static constexpr int value = RB <= 2 ? 4 : 2;
+struct K1Shape {
+  static constexpr int waves = RB <= 2 ? 16 : 8;
+  static constexpr int prefetch = 2;
 };
 
 template <int PREC, int RB, bool LINEAR>
-__global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArgs args) {
+__global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_down_kernel(QuantActArgs args) {
+  constexpr int kK1Waves = K1Shape<RB>::waves;
+  constexpr int kK1Threads = 64 * kK1Waves;
   extern __shared__ float lds[];
   // int4 linear: per wave and row, the largest group scale and the smallest
   // nonzero one
   __shared__ float rmax[kK1Waves][kK1Rows];
   __shared__ float rmin[kK1Waves][kK1Rows];
-  constexpr int PF = K1Prefetch<RB>::value;
+  constexpr int PF = K1Shape<RB>::prefetch;
   constexpr bool kRowExp = LINEAR && PREC == kInt4;
   constexpr int NB = RB > 0 ? RB : 1;
   const int M = (int)args.M, K = (int)args.K;
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
   const int wave = tid >> 6;
 
   // 1 / smooth for every input channel (IEEE division, one per channel).
-  for (int k = tid; k < K; k += 512) lds[k] = __fdiv_rn(1.0f, bf16_bits_to_f32(smooth[k]));
+  for (int k = tid; k < K; k += kK1Threads) lds[k] = __fdiv_rn(1.0f, bf16_bits_to_f32(smooth[k]));
   __syncthreads();
 
   const int r = lane & 15;
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
     }
   }
 
-  // ---- reduce the low-rank partials of the 8 waves (fixed order) ----------
+  // ---- reduce the low-rank partials of the waves (fixed order) -------------
   if constexpr (RB > 0) {
     constexpr int rank = RB * 16;
     __syncthreads();  // everyone is done with the 1/smooth table
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
 #pragma unroll
       for (int j = 0; j < 4; ++j) red[(wave * kK1Rows + q * 4 + j) * rank + b * 16 + r] = acc[b][j];
     __syncthreads();
-    for (int o = tid; o < kK1Rows * rank; o += 512) {
+    for (int o = tid; o < kK1Rows * rank; o += kK1Threads) {
       const int rr = o / rank;
       const int cc = o - rr * rank;
       float s = 0.f;
@@ -319,11 +326,12 @@ __global__ __launch_bounds__(512) void quantize_act_lora_down_kernel(QuantActArg
 template <int PREC, int RB, bool LINEAR>
 static hipError_t launch_k1(const QuantActArgs& a, hipStream_t stream) {
   const int rank = RB * 16;
+  constexpr int waves = K1Shape<RB>::waves;
   size_t lds = (size_t)a.K * sizeof(float);
-  const size_t red = (size_t)kK1Waves * kK1Rows * rank * sizeof(float);
+  const size_t red = (size_t)waves * kK1Rows * rank * sizeof(float);
   if (red > lds) lds = red;
   const unsigned blocks = (unsigned)((a.M + kK1Rows - 1) / kK1Rows);
-  hipLaunchKernelGGL((quantize_act_lora_down_kernel<PREC, RB, LINEAR>), dim3(blocks), dim3(512), lds,
+  hipLaunchKernelGGL((quantize_act_lora_down_kernel<PREC, RB, LINEAR>), dim3(blocks), dim3(64 * waves), lds,
                      stream, a);
   return hipGetLastError();
 }
