@@ -1,0 +1,113 @@
+"""The two linears as torch.library custom ops.
+
+CPU: the ops are registered and trace through their fake implementations.
+GPU: through the custom ops the outputs equal the plain binding's bit for bit
+and meet the oracle bar; torch.library.opcheck passes; a function calling
+both ops compiles with torch.compile(fullgraph=True) and gives the same bits.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from oracle import formats as F, layers as L
+
+bq = pytest.importorskip("bit_quantized_linear_quantize_amd")
+from bit_quantized_linear_quantize_amd import torch_ops as T  # noqa: E402
+
+
+def _fake_args():
+    bf, u8 = torch.bfloat16, torch.uint8
+    M, K, N, r, Na = 64, 256, 320, 32, 128
+    return (torch.zeros(M, K, dtype=bf), torch.zeros(N, K // 2, dtype=u8), torch.zeros(N, K // 64, dtype=bf),
+            torch.zeros(K, dtype=bf), torch.zeros(r, K, dtype=bf), torch.zeros(N, r, dtype=bf),
+            torch.zeros(N, dtype=bf), torch.zeros(Na, N // 2, dtype=u8), torch.zeros(Na, N // 64, dtype=bf),
+            torch.zeros(Na, N // 64, dtype=bf))
+
+
+def _pair(x, pw, ws, sm, ld, lu, b, apw, aws, awz):
+    h = torch.ops.svdq.w4a4_linear(x, pw, ws, 1.0, sm, ld, lu, b, "int4")
+    return torch.ops.svdq.awq_w4a16_linear(h, apw, aws, awz, None)
+
+
+def test_ops_trace_on_fake_tensors():
+    from torch.fx.experimental.proxy_tensor import make_fx
+    g = make_fx(_pair, tracing_mode="fake")(*_fake_args())
+    targets = [n.target for n in g.graph.nodes if n.op == "call_function"]
+    assert torch.ops.svdq.w4a4_linear.default in targets
+    assert torch.ops.svdq.awq_w4a16_linear.default in targets
+    out = [n for n in g.graph.nodes if n.op == "output"][0].args[0]
+    meta = out[0].meta["val"] if isinstance(out, (tuple, list)) else out.meta["val"]
+    assert tuple(meta.shape) == (64, 128) and meta.dtype == torch.bfloat16
+
+
+# ------------------------------------------------------------------ GPU
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.fixture(scope="module")
+def layers():
+    rng = np.random.default_rng(21)
+    M, K, N, Na = 96, 512, 384, 256
+    x = S.activations(M, K, 5, rng)
+    w = S.weight(N, K, 0.02, rng, spike_rank=2)
+    lay = L.prepare_svdq_layer(w, L.smooth_factors(x, w), 32, "int4", S.bias(N, rng))
+    wa = rng.standard_normal((Na, N)) * 0.02
+    alay = L.prepare_awq_layer(wa, S.bias(Na, rng))
+    return x, lay, alay
+
+
+@pytest.mark.gpu
+def test_custom_ops_match_binding_and_oracle(layers):
+    x, lay, alay = layers
+    layer, alayer = bq.SVDQLinear.from_numpy(lay), bq.AWQLinear.from_numpy(alay)
+    xd = dev_bf16(x)
+    y_op = T.svdq_linear(xd, layer)
+    y_b = bq.svdq_w4a4_linear(xd, layer)
+    h_op = T.awq_linear(y_op, alayer)
+    h_b = bq.awq_w4a16_linear(y_b, alayer)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y_op), host_bits(y_b))
+    assert np.array_equal(host_bits(h_op), host_bits(h_b))
+    y = F.bf16_to_f32(host_bits(y_op)).astype(np.float64)
+    _, excess, mre = L.output_errors(y, L.svdq_linear_ref(x, lay))
+    assert excess <= 1e-2 and mre <= 2e-3
+    h = F.bf16_to_f32(host_bits(h_op)).astype(np.float64)
+    _, excess, mre = L.output_errors(h, L.awq_linear_ref(host_bits(y_op), alay))
+    assert excess <= 1e-2 and mre <= 2e-3
+
+
+@pytest.mark.gpu
+def test_custom_ops_opcheck(layers):
+    x, lay, alay = layers
+    layer, alayer = bq.SVDQLinear.from_numpy(lay), bq.AWQLinear.from_numpy(alay)
+    xd = dev_bf16(x)
+    torch.library.opcheck(torch.ops.svdq.w4a4_linear.default,
+                          (xd, layer.packed_w, layer.wscales, layer.wtscale, layer.smooth, layer.lora_down,
+                           layer.lora_up, layer.bias, layer.precision))
+    h = bq.svdq_w4a4_linear(xd, layer)
+    torch.library.opcheck(torch.ops.svdq.awq_w4a16_linear.default,
+                          (h, alayer.packed_w, alayer.wscales, alayer.wzeros, alayer.bias))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("backend", ["aot_eager", "inductor"])
+def test_compile_fullgraph(layers, backend):
+    # an elementwise op between the two linears, which Inductor generates itself
+    x, lay, alay = layers
+    layer, alayer = bq.SVDQLinear.from_numpy(lay), bq.AWQLinear.from_numpy(alay)
+    xd = dev_bf16(x)
+
+    def f(inp):
+        return T.awq_linear(T.svdq_linear(inp, layer) * 0.5, alayer)
+
+    ref = f(xd)
+    got = torch.compile(f, fullgraph=True, backend=backend)(xd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(got), host_bits(ref))
