@@ -24,9 +24,17 @@ STATUS = {0: "SVDQ_OK", -1: "SVDQ_EINVAL", -2: "SVDQ_EUNSUPPORTED", -3: "SVDQ_EA
 
 # entry points declared in include/svdq_w4a4.h
 EXPORTS = ("svdq_w4a4_workspace_bytes", "svdq_w4a4_linear", "svdq_w4a4_quantize", "svdq_w4a4_gemm",
-           "awq_w4a16_linear",
+           "awq_w4a16_linear", "svdq_w4a4_mlp_workspace_bytes", "svdq_w4a4_mlp_gelu",
            "svdq_w4a4_quantize_act", "svdq_w4a4_gemm_partials", "svdq_w4a4_check",
-           "awq_w4a16_check", "svdq_last_error")
+           "awq_w4a16_check", "svdq_w4a4_mlp_gelu_check", "svdq_last_error")
+
+
+class LayerStruct(ctypes.Structure):
+    """svdq_w4a4_layer of include/svdq_w4a4.h."""
+    _fields_ = [("packed_w", ctypes.c_void_p), ("wscales", ctypes.c_void_p), ("wtscale", ctypes.c_float),
+                ("smooth", ctypes.c_void_p), ("lora_down", ctypes.c_void_p), ("lora_up", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("precision", ctypes.c_int), ("group_size", ctypes.c_int), ("rank", ctypes.c_int)]
 
 
 class SvdqError(RuntimeError):
@@ -69,6 +77,13 @@ def lib():
         L.svdq_w4a4_check.restype = I
         L.awq_w4a16_check.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, ctypes.c_char_p]
         L.awq_w4a16_check.restype = I
+        LP = ctypes.POINTER(LayerStruct)
+        L.svdq_w4a4_mlp_workspace_bytes.argtypes = [I64, LP, LP]
+        L.svdq_w4a4_mlp_workspace_bytes.restype = ctypes.c_size_t
+        L.svdq_w4a4_mlp_gelu.argtypes = [P, I64, LP, LP, P, P, ctypes.c_size_t, P]
+        L.svdq_w4a4_mlp_gelu.restype = I
+        L.svdq_w4a4_mlp_gelu_check.argtypes = [P, I64, LP, LP, P, P, ctypes.c_size_t, ctypes.c_char_p]
+        L.svdq_w4a4_mlp_gelu_check.restype = I
         L.svdq_last_error.argtypes = []
         L.svdq_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -182,6 +197,38 @@ def svdq_w4a4_gemm(workspace, M, layer, out=None, stream=None):
         _ptr(workspace), workspace.numel(), M, layer.K, layer.N, _ptr(layer.packed_w), _ptr(layer.wscales),
         layer.wtscale, _ptr(layer.lora_up), _ptr(layer.bias), PRECISIONS[layer.precision],
         GROUP_SIZE[layer.precision], layer.rank, _ptr(out), _stream(stream)))
+    return out
+
+
+def layer_struct(layer):
+    """The svdq_w4a4_layer view of an SVDQLinear (pointers into its tensors)."""
+    return LayerStruct(layer.packed_w.data_ptr(), layer.wscales.data_ptr(), layer.wtscale,
+                       layer.smooth.data_ptr(), _addr(layer.lora_down), _addr(layer.lora_up), _addr(layer.bias),
+                       layer.K, layer.N, PRECISIONS[layer.precision], GROUP_SIZE[layer.precision], layer.rank)
+
+
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
+def mlp_workspace_bytes(M, up, down):
+    u, d = layer_struct(up), layer_struct(down)
+    return lib().svdq_w4a4_mlp_workspace_bytes(M, ctypes.byref(u), ctypes.byref(d))
+
+
+def svdq_w4a4_mlp_gelu(x, up, down, out=None, workspace=None, stream=None):
+    """Y = down(GELU(up(x))) with the up projection's epilogue applying GELU and
+    quantizing for the down projection (nvfp4 down layer); returns bf16 [M, N_down]."""
+    x = _contig(x, torch.bfloat16, "x")
+    M = x.shape[0]
+    u, d = layer_struct(up), layer_struct(down)
+    if out is None:
+        out = torch.empty((M, down.N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        need = lib().svdq_w4a4_mlp_workspace_bytes(M, ctypes.byref(u), ctypes.byref(d))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().svdq_w4a4_mlp_gelu(_ptr(x), M, ctypes.byref(u), ctypes.byref(d), _ptr(out), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
     return out
 
 

@@ -210,6 +210,69 @@ int launch_gemm(const void* workspace, int64_t M, int64_t K, int64_t N, const vo
   return launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up launch");
 }
 
+// ---- fused GELU MLP ----------------------------------------------------------
+
+// One layer of svdq_w4a4_mlp_gelu: the svdq_w4a4_linear rules for its own
+// tensors (M rows of input), without the input and output buffers.
+int validate_layer(int64_t M, const svdq_w4a4_layer* L, const char* which) {
+  const std::string w(which);
+  if (!L) return fail(SVDQ_EINVAL, w + " layer is null");
+  int rc = check_svdq_kind(L->precision, L->group_size, L->rank);
+  if (rc) return rc;
+  rc = check_shape(M, L->K, L->N);
+  if (rc) return rc;
+  if (!L->packed_w || !L->wscales || !L->smooth) return fail(SVDQ_EINVAL, w + " layer: null pointer");
+  if ((L->rank > 0) != (L->lora_down != nullptr) || (L->rank > 0) != (L->lora_up != nullptr))
+    return fail(SVDQ_EINVAL, w + " layer: lora_down / lora_up must be non-null exactly when rank > 0");
+  const void* ptrs[] = {L->packed_w, L->wscales, L->smooth, L->lora_down, L->lora_up, L->bias};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return fail(SVDQ_EINVAL, w + " layer: pointers must be 16-byte aligned");
+  if (L->precision == SVDQ_INT4 && L->wtscale != 1.0f) return fail(SVDQ_EINVAL, w + " layer: wtscale must be 1.0 for int4");
+  if (L->precision == SVDQ_NVFP4 && !(std::isfinite(L->wtscale) && L->wtscale > 0.f))
+    return fail(SVDQ_EINVAL, w + " layer: wtscale must be finite and positive");
+  return SVDQ_OK;
+}
+
+size_t mlp_workspace_bytes(int64_t M, const svdq_w4a4_layer* up, const svdq_w4a4_layer* down) {
+  return workspace_bytes(M, up->K, up->precision, up->rank) + workspace_bytes(M, down->K, SVDQ_NVFP4, down->rank);
+}
+
+int validate_mlp(const void* x, int64_t M, const svdq_w4a4_layer* up, const svdq_w4a4_layer* down,
+                 const void* out, const void* workspace, size_t ws_bytes) {
+  int rc = validate_layer(M, up, "up");
+  if (rc) return rc;
+  rc = validate_layer(M, down, "down");
+  if (rc) return rc;
+  if (up->N != down->K) return fail(SVDQ_EINVAL, "up->N must equal down->K");
+  if (down->precision != SVDQ_NVFP4)
+    return fail(SVDQ_EUNSUPPORTED, "the fused MLP quantizes the hidden activations as nvfp4: down must be nvfp4");
+  if (!x || !out || !workspace) return fail(SVDQ_EINVAL, "null pointer argument");
+  if (!aligned(x) || !aligned(out) || !aligned(workspace))
+    return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  const size_t need = mlp_workspace_bytes(M, up, down);
+  const Range o{out, size_t(M) * size_t(down->N) * 2};
+  const Range ins[] = {{x, size_t(M) * size_t(up->K) * 2},
+                       {workspace, need},
+                       {up->packed_w, size_t(up->N) * size_t(up->K / 2)},
+                       {up->wscales, w_scale_bytes(up->N, up->K, up->precision)},
+                       {up->smooth, size_t(up->K) * 2},
+                       {up->lora_down, size_t(up->rank) * size_t(up->K) * 2},
+                       {up->lora_up, size_t(up->N) * size_t(up->rank) * 2},
+                       {up->bias, size_t(up->N) * 2},
+                       {down->packed_w, size_t(down->N) * size_t(down->K / 2)},
+                       {down->wscales, w_scale_bytes(down->N, down->K, down->precision)},
+                       {down->smooth, size_t(down->K) * 2},
+                       {down->lora_down, size_t(down->rank) * size_t(down->K) * 2},
+                       {down->lora_up, size_t(down->N) * size_t(down->rank) * 2},
+                       {down->bias, size_t(down->N) * 2}};
+  for (const Range& r : ins)
+    if (overlaps(o, r)) return fail(SVDQ_EINVAL, "out overlaps an input or the workspace");
+  if (overlaps(Range{x, size_t(M) * size_t(up->K) * 2}, Range{workspace, need}))
+    return fail(SVDQ_EINVAL, "workspace overlaps x");
+  if (ws_bytes < need) return fail(SVDQ_EWORKSPACE, "workspace too small");
+  return SVDQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -371,6 +434,54 @@ int svdq_w4a4_gemm_partials(const void* act_codes, const void* w_codes, int64_t 
                     partials_out, 1.0f, M, K, N, precision, 0};
   return launch_status(svdq::launch_gemm_w4a4(ga, static_cast<hipStream_t>(stream)),
                        "gemm_w4a4 partials launch");
+}
+
+size_t svdq_w4a4_mlp_workspace_bytes(int64_t M, const svdq_w4a4_layer* up, const svdq_w4a4_layer* down) {
+  const std::string saved = g_last_error;
+  const bool ok = validate_layer(M, up, "up") == SVDQ_OK && validate_layer(M, down, "down") == SVDQ_OK &&
+                  up->N == down->K && down->precision == SVDQ_NVFP4;
+  g_last_error = saved;
+  return ok ? mlp_workspace_bytes(M, up, down) : 0;
+}
+
+int svdq_w4a4_mlp_gelu_check(const void* x, int64_t M, const svdq_w4a4_layer* up, const svdq_w4a4_layer* down,
+                             const void* out, const void* workspace, size_t ws_bytes, const char* arch) {
+  g_last_error.clear();
+  int rc = validate_mlp(x, M, up, down, out, workspace, ws_bytes);
+  if (rc) return rc;
+  if (!arch_is_gfx950(arch)) return fail(SVDQ_EARCH, "device architecture is not gfx950");
+  return SVDQ_OK;
+}
+
+int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up, const svdq_w4a4_layer* down,
+                       void* out, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = validate_mlp(x, M, up, down, out, workspace, ws_bytes);
+  if (rc) return rc;
+  rc = check_device_arch();
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t H = up->N;
+  // up layer: kernel 1 into the first part of the workspace
+  rc = launch_quantize(x, M, up->K, up->smooth, up->lora_down, up->precision, up->rank, workspace, s);
+  if (rc) return rc;
+  const Carve cu = carve(workspace, M, up->K, up->precision);
+  void* ws_down = static_cast<uint8_t*>(workspace) + workspace_bytes(M, up->K, up->precision, up->rank);
+  const Carve cd = carve(ws_down, M, H, SVDQ_NVFP4);
+  if (down->rank > 0) {
+    rc = launch_status(svdq::launch_zero_f32(cd.lora_act, M * down->rank, s), "zero fill launch");
+    if (rc) return rc;
+  }
+  // up layer: kernel 2 with the GELU + nvfp4 epilogue writing the down
+  // layer's workspace (its bf16 output is not stored)
+  svdq::GemmArgs ga{cu.act_f16, cu.row_scale, cu.lora_act, up->packed_w, up->wscales, up->lora_up, up->bias,
+                    nullptr, nullptr, up->wtscale, M, up->K, H, up->precision, up->rank,
+                    down->smooth, down->lora_down, cd.act_f16, cd.lora_act, down->rank};
+  rc = launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up (GELU epilogue) launch");
+  if (rc) return rc;
+  // down layer: kernel 2 from its workspace
+  return launch_gemm(ws_down, M, H, down->N, down->packed_w, down->wscales, down->wtscale, down->lora_up,
+                     down->bias, SVDQ_NVFP4, down->rank, out, s);
 }
 
 }  // extern "C"

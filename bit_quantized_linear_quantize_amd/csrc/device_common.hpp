@@ -112,6 +112,35 @@ __device__ __forceinline__ f16x8 e2m1x8_to_f16_scaled(uint32_t w, _Float16 scale
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// nvfp4 activation quantizer for one group of 16 values x[0..15]: per-token
+// block scale s8 = E4M3(fl32(amax / 6)) (tensor scale 1; round to nearest
+// even, saturating at 448), codes = E2M1(fl32(x * fl32(1 / dec(s8)))) with
+// nibble i = value i; a group with amax < 2^-100 or dec(s8) == 0 gets codes
+// 0.  Returns the E4M3 byte (0 for such a group) and dec(s8) in S.
+__device__ __forceinline__ uint32_t nvfp4_quant16(const float* x, uint32_t& cw0, uint32_t& cw1, float& S) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float sf = __fdiv_rn(amax, 6.0f);
+  const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sf, 448.0f), 0.0f, 0, false) & 0xffu;
+  S = __builtin_amdgcn_cvt_f32_fp8((int)s8, 0);
+  const bool zero = !(amax >= kTiny) || S == 0.0f;
+  const float inv = zero ? 0.f : __fdiv_rn(1.0f, S);
+  cw0 = 0;
+  cw1 = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float t0 = __fmul_rn(x[2 * j], inv);
+    const float t1 = __fmul_rn(x[2 * j + 1], inv);
+    const uint32_t byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t0, t1, 1.0f, 0) & 0xffu;
+    if (j < 4) cw0 |= byte << (8 * j);
+    else cw1 |= byte << (8 * (j - 4));
+  }
+  cw0 = zero ? 0u : cw0;
+  cw1 = zero ? 0u : cw1;
+  return zero ? 0u : s8;
+}
+
 // Power-of-two exponent E of a positive normal float s such that s * 2^-E
 // lies in [2^12, 2^13): then |q| * s * 2^-E < 7 * 2^13 fits fp16 for |q| <= 7,
 // and every s' >= 2^-17 (within 2^29 of the largest) keeps all its bits.

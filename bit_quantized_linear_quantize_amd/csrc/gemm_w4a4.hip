@@ -116,7 +116,146 @@ __device__ __forceinline__ void tile_of(int bid, int nmt, int nnt, int& mt, int&
   nt = r / gsize;
 }
 
-template <int PREC, int RB, bool PARTIALS>
+// MLP fusion epilogue: wave-private LDS tile of GELU outputs, 64 rows x 96
+// bf16 columns, rows padded to 208 bytes (conflict-free row-wise and
+// operand-layout reads).
+constexpr int kGeluRow = 208;
+
+// GELU with the exact erf, y/2 (1 + erf(y / sqrt 2)), on an fp32 value,
+// evaluated as (y / 2) erfc(-y / sqrt 2): the same function without the
+// cancellation of 1 + erf for negative y.
+__device__ __forceinline__ float gelu_erf(float y) {
+  return __fmul_rn(__fmul_rn(y, 0.5f), erfcf(__fmul_rn(y, -0.70710678118654752f)));
+}
+
+// The MLP fusion epilogue of one wave ("Fused kernels" of the Nunchaku Lite
+// docs page: the MLP's GELU and the quantization for the down projection in
+// the up projection's epilogue).  acc holds this wave's 64 x 96 block of the
+// up projection before its bias.  Steps:
+//  1. g = bf16(GELU(bf16(acc + bias))) -- the values a bf16 up output followed
+//     by a bf16 GELU would give -- into the wave's LDS tile `tile_base`
+//     (+ 64 kGeluRow for odd waves);
+//  2. lane l takes tile row l: x = fl32(g * (1 / smooth_next)), nvfp4 per 16
+//     columns (nvfp4_quant16, the quantize kernel's reading), and stores the
+//     next layer's product operand e2m1 * dec(s8) as fp16;
+//  3. the next layer's low-rank activations: the same x in the 16x16x32 bf16
+//     operand layout, split hi + lo, times next_lora_down, added into
+//     next_lora_act with fp32 atomics (one partial per wave and tile).
+// Columns past N have 1/smooth 0 (x = 0) and are not stored; rows past M are
+// not stored.
+__device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16 (&acc)[kIB][kJB], int m0, int n0,
+                                                    int wave, int wm, int wn, int lane, int l32, int h,
+                                                    const float* nmu, uint8_t* tile_base) {
+  const int M = (int)args.M, N = (int)args.N;
+  uint8_t* gt = tile_base + (wave & 1) * (64 * kGeluRow);
+  // every wave has left the main loop (its LDS reads are done) and every
+  // direct-to-LDS load has landed before the buffers are reused
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // 1. the GELU tile
+  const uint16_t* bias = (const uint16_t*)args.bias;
+#pragma unroll
+  for (int j = 0; j < kJB; ++j) {
+    const int col = n0 + wn * (kJB * 32) + j * 32 + l32;
+    const float bv = (bias && col < N) ? bf16_bits_to_f32(bias[col]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < kIB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+        const float y = __uint_as_float(f32_to_bf16_bits(acc[i][j][e] + bv) << 16);
+        *(uint16_t*)(gt + r * kGeluRow + (j * 32 + l32) * 2) = (uint16_t)f32_to_bf16_bits(gelu_erf(y));
+      }
+  }
+  // (the wave's own LDS writes and reads execute in order)
+
+  // 2. quantization for the next layer, one tile row per lane
+  const float* mu = nmu + wn * (kJB * 32);
+  {
+    const int m = m0 + wm * 64 + lane;
+    const uint8_t* rowp = gt + lane * kGeluRow;
+    _Float16* dst = (_Float16*)args.next_act + (size_t)m * N + n0 + wn * (kJB * 32);
+#pragma unroll
+    for (int t = 0; t < 6; ++t) {
+      const u32x4 g0 = *(const u32x4*)(rowp + 32 * t);
+      const u32x4 g1 = *(const u32x4*)(rowp + 32 * t + 16);
+      float x[16];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        x[2 * p] = __fmul_rn(bf16_lo(g0[p]), mu[16 * t + 2 * p]);
+        x[2 * p + 1] = __fmul_rn(bf16_hi(g0[p]), mu[16 * t + 2 * p + 1]);
+        x[8 + 2 * p] = __fmul_rn(bf16_lo(g1[p]), mu[16 * t + 8 + 2 * p]);
+        x[8 + 2 * p + 1] = __fmul_rn(bf16_hi(g1[p]), mu[16 * t + 8 + 2 * p + 1]);
+      }
+      uint32_t cw0, cw1;
+      float S;
+      nvfp4_quant16(x, cw0, cw1, S);
+      // e2m1 * dec(s8) is an exact fp16 (|v| <= 2688, >= 2^-10)
+      const _Float16 S16 = (_Float16)S;
+      if (m < M && n0 + wn * (kJB * 32) + 16 * t < N) {
+        *(f16x8*)(dst + 16 * t) = e2m1x8_to_f16_scaled(cw0, S16);
+        *(f16x8*)(dst + 16 * t + 8) = e2m1x8_to_f16_scaled(cw1, S16);
+      }
+    }
+  }
+
+  // 3. the next layer's low-rank down projection of this tile's columns
+  const int nrank = args.next_rank;
+  if (nrank > 0) {
+    const int r16 = lane & 15, q = lane >> 4;
+    bf16x8 ahi[4][3], alo[4][3];
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      const f32x4 mu0 = *(const f32x4*)(mu + ks * 32 + 8 * q);
+      const f32x4 mu1 = *(const f32x4*)(mu + ks * 32 + 8 * q + 4);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const u32x4 g = *(const u32x4*)(gt + (rb * 16 + r16) * kGeluRow + (ks * 32 + 8 * q) * 2);
+        u32x4 hi4, lo4;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float a = __fmul_rn(bf16_lo(g[p]), p < 2 ? mu0[2 * p] : mu1[2 * p - 4]);
+          const float b = __fmul_rn(bf16_hi(g[p]), p < 2 ? mu0[2 * p + 1] : mu1[2 * p - 3]);
+          const uint32_t hh = bf16x2_rne(a, b);
+          hi4[p] = hh;
+          lo4[p] = bf16x2_rne(__fsub_rn(a, bf16_lo(hh)), __fsub_rn(b, bf16_hi(hh)));
+        }
+        ahi[rb][ks] = __builtin_bit_cast(bf16x8, hi4);
+        alo[rb][ks] = __builtin_bit_cast(bf16x8, lo4);
+      }
+    }
+    // next_lora_down [nrank, N]: reads past the end of the array return zero
+    const __amdgpu_buffer_rsrc_t ld_rs = make_rsrc(args.next_lora_down, (size_t)nrank * N * 2);
+    for (int rk = 0; rk < nrank; rk += 16) {
+      bf16x8 b[3];
+#pragma unroll
+      for (int ks = 0; ks < 3; ++ks)
+        b[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ld_rs, ((rk + r16) * N + n0 + wn * (kJB * 32) + ks * 32 + 8 * q) * 2,
+                                               0, 0));
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 3; ++ks) {
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[rb][ks], b[ks], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[rb][ks], b[ks], d, 0, 0, 0);
+        }
+        // D: lane (c, q) holds rows 4q + j of the row block, rank column c
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int m = m0 + wm * 64 + rb * 16 + 4 * q + j;
+          if (m < M) unsafeAtomicAdd(args.next_lora_act + (size_t)m * nrank + rk + r16, d[j]);
+        }
+      }
+    }
+  }
+}
+
+template <int PREC, int RB, bool PARTIALS, bool GELUQ = false>
 __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs args) {
   // separate LDS objects, selected at compile time, so that the compiler can
   // tell the buffers apart from those that direct-to-LDS loads are filling
@@ -127,6 +266,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   __shared__ __attribute__((aligned(16))) uint8_t lds_w1[kBN * kWRow];
   __shared__ float wexp[kBN];   // int4: 2^F[n] of this tile's weight rows
   __shared__ float wdown[kBN];  // int4: 2^-F[n]
+  __shared__ float nmu[kBN];    // MLP fusion: 1 / smooth of the next layer for this tile's columns
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -138,6 +278,13 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   tile_of(blockIdx.x, nmt, nnt, mt, nt);
   const int m0 = mt * kBM, n0 = nt * kBN;
   const int nstages = K / kBK;
+  if constexpr (GELUQ) {
+    // read before the first use by the main loop's barriers
+    if (tid < kBN) {
+      const int col = n0 + tid;
+      nmu[tid] = col < N ? __fdiv_rn(1.0f, bf16_bits_to_f32(((const uint16_t*)args.next_smooth)[col])) : 0.f;
+    }
+  }
   constexpr bool kRowExp = PREC == kInt4 && !PARTIALS;
 
   // ---- loaders ---------------------------------------------------------------
@@ -453,34 +600,39 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
           }
       }
     }
-    // ---- bias + bf16 store --------------------------------------------------
-    const uint16_t* bias = (const uint16_t*)args.bias;
-    uint16_t* out = (uint16_t*)args.out;
+    if constexpr (GELUQ) {
+      gelu_quant_epilogue(args, acc, m0, n0, wave, wm, wn, lane, l32, h, nmu,
+                          wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0);
+    } else {
+      // ---- bias + bf16 store ------------------------------------------------
+      const uint16_t* bias = (const uint16_t*)args.bias;
+      uint16_t* out = (uint16_t*)args.out;
 #pragma unroll
-    for (int j = 0; j < kJB; ++j) {
-      const int col = n0 + wn * (kJB * 32) + j * 32 + l32;
-      const float bv = (bias && col < N) ? bf16_bits_to_f32(bias[col]) : 0.f;
+      for (int j = 0; j < kJB; ++j) {
+        const int col = n0 + wn * (kJB * 32) + j * 32 + l32;
+        const float bv = (bias && col < N) ? bf16_bits_to_f32(bias[col]) : 0.f;
 #pragma unroll
-      for (int i = 0; i < kIB; ++i)
+        for (int i = 0; i < kIB; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = m0 + wm * (kIB * 32) + i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-          if (row < M && col < N) out[(size_t)row * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][e] + bv);
-        }
+          for (int e = 0; e < 16; ++e) {
+            const int row = m0 + wm * (kIB * 32) + i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+            if (row < M && col < N) out[(size_t)row * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][e] + bv);
+          }
+      }
     }
   }
 }
 
-template <int PREC, bool PARTIALS>
+template <int PREC, bool PARTIALS, bool GELUQ>
 static hipError_t dispatch_rank(const GemmArgs& a, hipStream_t s) {
   const unsigned tiles = (unsigned)(((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN));
   dim3 grid(tiles), block(kThreads);
   if constexpr (PARTIALS) {
     hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, 0, true>), grid, block, 0, s, a);
   } else {
-#define SVDQ_K2_CASE(rb)                                                                     \
-  case rb:                                                                                   \
-    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, rb, false>), grid, block, 0, s, a); \
+#define SVDQ_K2_CASE(rb)                                                                            \
+  case rb:                                                                                          \
+    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, rb, false, GELUQ>), grid, block, 0, s, a); \
     break;
     switch (a.rank / 16) {
       SVDQ_K2_CASE(0)
@@ -501,9 +653,25 @@ static hipError_t dispatch_rank(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream) {
   const bool partials = a.partials != nullptr;
-  if (a.precision == kInt4)
-    return partials ? dispatch_rank<kInt4, true>(a, stream) : dispatch_rank<kInt4, false>(a, stream);
-  return partials ? dispatch_rank<kNvfp4, true>(a, stream) : dispatch_rank<kNvfp4, false>(a, stream);
+  const bool geluq = a.next_act != nullptr;
+  if (a.precision == kInt4) {
+    if (partials) return dispatch_rank<kInt4, true, false>(a, stream);
+    return geluq ? dispatch_rank<kInt4, false, true>(a, stream) : dispatch_rank<kInt4, false, false>(a, stream);
+  }
+  if (partials) return dispatch_rank<kNvfp4, true, false>(a, stream);
+  return geluq ? dispatch_rank<kNvfp4, false, true>(a, stream) : dispatch_rank<kNvfp4, false, false>(a, stream);
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+// Clears n floats with a kernel (also inside a captured graph).
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
 }
 
 }  // namespace svdq

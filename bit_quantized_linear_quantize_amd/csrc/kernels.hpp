@@ -39,6 +39,14 @@ struct GemmArgs {
   float wtscale;
   int64_t M, K, N;
   int precision, rank;
+  // MLP fusion (null next_act: plain store of out).  The epilogue applies
+  // GELU to the bf16 output and quantizes it (nvfp4) for the next layer,
+  // whose input channels are this layer's N columns; out is not written.
+  const void* next_smooth;     // bf16 [N]
+  const void* next_lora_down;  // bf16 [next_rank, N] or null
+  void* next_act;              // f16 [M, N]: the next layer's product operand e2m1 * dec(s8)
+  float* next_lora_act;        // f32 [M, next_rank], zero on entry, accumulated with atomics
+  int next_rank;
 };
 
 struct AwqArgs {
@@ -54,5 +62,6 @@ struct AwqArgs {
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream);
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 
 }  // namespace svdq

@@ -202,24 +202,8 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
             if (row_ok && q == 0) ((uint16_t*)args.scales)[(size_t)row * (K >> 6) + c] = (uint16_t)sbits;
           }
         } else {
-          float amax = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-          const float sf = __fdiv_rn(amax, 6.0f);
-          const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sf, 448.0f), 0.0f, 0, false) & 0xffu;
-          const float S = __builtin_amdgcn_cvt_f32_fp8((int)s8, 0);
-          const bool zero = !(amax >= kTiny) || S == 0.0f;
-          const float inv = zero ? 0.f : __fdiv_rn(1.0f, S);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float t0 = __fmul_rn(xh[2 * j], inv);
-            const float t1 = __fmul_rn(xh[2 * j + 1], inv);
-            const uint32_t byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t0, t1, 1.0f, 0) & 0xffu;
-            if (j < 4) cw0 |= byte << (8 * j);
-            else cw1 |= byte << (8 * (j - 4));
-          }
-          cw0 = zero ? 0u : cw0;
-          cw1 = zero ? 0u : cw1;
+          float S;
+          const uint32_t s8 = nvfp4_quant16(xh, cw0, cw1, S);
           if constexpr (LINEAR) {
             // the product operand e2m1 * dec(s8): an exact fp16 (|v| <= 2688, >= 2^-10)
             if (row_ok) {
@@ -229,7 +213,7 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
               *(f16x8*)(dst + 8) = e2m1x8_to_f16_scaled(cw1, S16);
             }
           } else if (row_ok) {
-            ((uint8_t*)args.scales)[(size_t)row * (K >> 4) + 4 * c + q] = (uint8_t)(zero ? 0u : s8);
+            ((uint8_t*)args.scales)[(size_t)row * (K >> 4) + 4 * c + q] = (uint8_t)s8;
           }
         }
         if (row_ok && !LINEAR) *(u32x2*)(codes + (size_t)row * (K >> 1) + (k0 >> 1)) = u32x2{cw0, cw1};

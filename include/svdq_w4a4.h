@@ -126,6 +126,55 @@ int awq_w4a16_linear(const void* x, int64_t M, int64_t K, int64_t N,
                      const void* packed_w, const void* wscales, const void* wzeros,
                      const void* bias, int group_size, void* out, void* stream);
 
+/* One svdq_w4a4 layer's device tensors and sizes, with the meaning and rules
+ * of the svdq_w4a4_linear arguments of the same names (weights [N, K]).
+ * Plain C; the caller owns every buffer it points to. */
+typedef struct svdq_w4a4_layer {
+  const void* packed_w;   /* uint8 [N, K/2] */
+  const void* wscales;    /* int4: bf16 [N, K/64]; nvfp4: uint8 E4M3 [N, K/16] */
+  float wtscale;          /* nvfp4 weight tensor scale; 1.0f for int4 */
+  const void* smooth;     /* bf16 [K] */
+  const void* lora_down;  /* bf16 [rank, K]; NULL iff rank == 0 */
+  const void* lora_up;    /* bf16 [N, rank]; NULL iff rank == 0 */
+  const void* bias;       /* bf16 [N] or NULL */
+  int64_t K, N;
+  int precision, group_size, rank;
+} svdq_w4a4_layer;
+
+/* Bytes of scratch svdq_w4a4_mlp_gelu needs: the up layer's linear workspace
+ * (svdq_w4a4_workspace_bytes(M, up->K, up->N, ...)) followed by the down
+ * layer's (its fp16 product operand [M, H] and fp32 low-rank activations
+ * [M, down->rank]).  Returns 0 for arguments svdq_w4a4_mlp_gelu would reject. */
+size_t svdq_w4a4_mlp_workspace_bytes(int64_t M, const svdq_w4a4_layer* up,
+                                     const svdq_w4a4_layer* down);
+
+/* GELU MLP, Y = down(GELU(up(X))) with GELU(y) = y/2 (1 + erf(y / sqrt 2)),
+ * with the fusion of the "Fused kernels" section of the Nunchaku Lite docs
+ * page: the up projection's epilogue applies GELU to its bf16 output and
+ * quantizes the result for the down projection itself (the down layer's
+ * smoothing, nvfp4 group quantization and low-rank down projection), so the
+ * hidden [M, H] bf16 tensor is never written or read back.
+ *
+ * The values are those of svdq_w4a4_linear(up), a bf16 GELU of its output and
+ * svdq_w4a4_linear(down) on that, except that the down layer's low-rank
+ * activations are summed over the up projection's column tiles with fp32
+ * atomics: their rounding (and so the last bit of some outputs) may differ
+ * from run to run.
+ *
+ * x      bf16 [M, up->K]; H = up->N must equal down->K
+ * up     any svdq_w4a4 layer (int4 or nvfp4)
+ * down   an nvfp4 layer (group 16): int4 activations need one power of two
+ *        per row over the whole row, which a tile of the up projection does
+ *        not see, so int4 returns SVDQ_EUNSUPPORTED
+ * out    bf16 [M, down->N]; must not overlap x, the weights or the workspace
+ * workspace  at least svdq_w4a4_mlp_workspace_bytes(M, up, down) bytes
+ * Other rules (shapes, ranks, alignment, errors) as for svdq_w4a4_linear,
+ * for each layer.
+ */
+int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up,
+                       const svdq_w4a4_layer* down, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Parity export of the first svdq_w4a4 kernel (same kernel as the linear):
  * smoothing, activation quantization and the low-rank down projection.
  * codes_out  uint8 [M, K/2]; scales_out bf16 [M, K/64] (int4) or uint8 E4M3
@@ -157,6 +206,9 @@ int svdq_w4a4_check(const void* x, int64_t M, int64_t K, int64_t N, const void* 
 int awq_w4a16_check(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
                     const void* wscales, const void* wzeros, const void* bias,
                     int group_size, const void* out, const char* arch);
+int svdq_w4a4_mlp_gelu_check(const void* x, int64_t M, const svdq_w4a4_layer* up,
+                             const svdq_w4a4_layer* down, const void* out,
+                             const void* workspace, size_t workspace_bytes, const char* arch);
 
 /* Message for the last failure on the calling thread ("" if none). */
 const char* svdq_last_error(void);

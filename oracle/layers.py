@@ -194,6 +194,30 @@ def svdq_partials_ref(act_codes, w_codes, precision):
     return np.einsum("mgk,ngk->mng", a.reshape(M, K // G, G), w.reshape(N, K // G, G))
 
 
+def gelu_f64(y):
+    """GELU with the exact erf, y/2 (1 + erf(y / sqrt 2)), in fp64 (the
+    activation between the two linears of the DiT MLP), written as
+    y/2 erfc(-y / sqrt 2): the same function, without the cancellation of
+    1 + erf for negative y (scipy's erfc is the library routine)."""
+    from scipy.special import erfc
+    y = np.asarray(y, dtype=np.float64)
+    return 0.5 * y * erfc(-y / np.sqrt(2.0))
+
+
+def gelu_bf16(y_bits):
+    """A bf16 GELU of bf16 values: gelu_f64 of the values, rounded once to
+    bf16 (RNE).  Takes and returns bf16 bit patterns."""
+    return bf16_bits_f64(gelu_f64(bf16_to_f32(y_bits).astype(np.float64)))
+
+
+def mlp_gelu_ref(h_bits, down):
+    """Reference of the GELU MLP's second half, given the up projection's bf16
+    output h: the down linear (svdq_linear_ref) of gelu_bf16(h), in fp64.
+    (The fused MLP computes the same hidden values; h itself is the up
+    linear, checked on its own.)"""
+    return svdq_linear_ref(gelu_bf16(h_bits), down)
+
+
 def awq_dequant(layer):
     G = layer["group_size"]
     q = layer["q"].astype(np.float64)

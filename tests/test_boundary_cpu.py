@@ -191,3 +191,40 @@ def test_linear_rejects_before_touching_the_device(L):
                             1.0, _fake(0x4000_0000), None, None, None, 0, 32, 0, _fake(0x8000_0000),
                             _fake(0x9000_0000), 1 << 20, None)
     assert rc == EUNSUP
+
+
+# ------------------------------------------------------------------ fused GELU MLP
+def _layer(base, K, N, precision=1, rank=32, wt=None):
+    group = 16 if precision == 1 else 64
+    wt = (1.0 if precision == 0 else 0.01) if wt is None else wt
+    return bq.LayerStruct(base, base + 0x100_0000, wt, base + 0x200_0000,
+                          base + 0x300_0000 if rank else None, base + 0x400_0000 if rank else None,
+                          base + 0x500_0000, K, N, precision, group, rank)
+
+
+def test_mlp_rules(L):
+    M, K, H, N = 256, 512, 768, 256
+    x, out, ws = 0x3_0000_0000, 0x4_0000_0000, 0x5_0000_0000
+    up, down = _layer(0x1_0000_0000, K, H, precision=0), _layer(0x2_0000_0000, H, N, precision=1)
+    B = ctypes.byref
+    need = L.svdq_w4a4_mlp_workspace_bytes(M, B(up), B(down))
+    rnd = lambda v: (v + 255) // 256 * 256
+    # the up layer's linear workspace (int4: operand, row factors, lora_act), then the down layer's
+    assert need == (rnd(2 * M * K) + rnd(4 * M) + rnd(4 * M * 32)) + (rnd(2 * M * H) + rnd(4 * M * 32))
+
+    def call(x=x, M=M, up=up, down=down, out=out, ws=ws, wsb=need, arch=GFX950):
+        p = lambda v: None if v is None else _fake(v)
+        return L.svdq_w4a4_mlp_gelu_check(p(x), M, B(up) if up is not None else None,
+                                          B(down) if down is not None else None, p(out), p(ws), wsb, arch)
+    assert call() == OK
+    assert call(up=_layer(0x1_0000_0000, K, H, precision=1)) == OK
+    assert call(down=_layer(0x2_0000_0000, H, N, precision=0)) == EUNSUP  # int4 hidden activations
+    assert L.svdq_w4a4_mlp_workspace_bytes(M, B(up), B(_layer(0x2_0000_0000, H, N, precision=0))) == 0
+    assert call(down=_layer(0x2_0000_0000, H + 64, N)) == EINVAL     # up->N != down->K
+    assert call(up=None) == EINVAL
+    assert call(wsb=need - 1) == EWS
+    assert call(x=x + 8) == EINVAL
+    assert call(out=ws) == EINVAL                                     # out overlaps the workspace
+    assert call(down=_layer(0x2_0000_0000, H, N, rank=0)) == OK
+    assert call(down=_layer(0x2_0000_0000, H, N, rank=24)) == EUNSUP
+    assert call(arch=b"gfx942") == EARCH

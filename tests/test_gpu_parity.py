@@ -358,6 +358,48 @@ def test_mlp_pair_down_config2_sampled(mlp_up):
     assert_output(y[SAMPLE_ROWS], L.svdq_linear_ref(g[SAMPLE_ROWS], lay), "mlp down 12288->3072")
 
 
+def test_mlp_gelu_fused_config2_sampled(mlp_up):
+    # the fused MLP (GELU and the nvfp4 quantization for the down projection
+    # in the up projection's epilogue) at 3072 -> 12288 -> 3072, M = 4096,
+    # against the oracle's down half on the GPU's own up output h (the fused
+    # kernel computes the same h internally)
+    c, x, lay_up, h = mlp_up
+    hb = host_bits(h)
+    lay_down = prepared(L.gelu_bf16(hb), c["w_down"], c["b_down"], "nvfp4", 32, smooth="calibrated")
+    y = bq.svdq_w4a4_mlp_gelu(dev_bf16(x), bq.SVDQLinear.from_numpy(lay_up), bq.SVDQLinear.from_numpy(lay_down))
+    torch.cuda.synchronize()
+    assert_output(y[SAMPLE_ROWS], L.mlp_gelu_ref(hb[SAMPLE_ROWS], lay_down), "fused mlp 3072->12288->3072")
+
+
+@pytest.mark.parametrize("M,up_prec,ranks", [(1, "nvfp4", (32, 32)), (37, "int4", (32, 32)),
+                                             (300, "nvfp4", (0, 16)), (300, "int4", (16, 0)),
+                                             (257, "nvfp4", (128, 128))])
+def test_mlp_gelu_fused_ragged(M, up_prec, ranks):
+    # H = 640: the last 192-column tile of the up projection is partial; M
+    # ragged against the 256-row tiles; every rank block path of the epilogue
+    rng = np.random.default_rng(M + ranks[0])
+    K, H, N = 256, 640, 320
+    x = S.activations(M, K, 3, rng)
+    lay_up = prepared(x, S.weight(H, K, 0.02, rng, spike_rank=2), S.bias(H, rng), up_prec, ranks[0],
+                      smooth="calibrated")
+    hb = host_bits(run_linear(x, lay_up))
+    lay_down = prepared(L.gelu_bf16(hb), S.weight(N, H, 0.02, rng), S.bias(N, rng), "nvfp4", ranks[1],
+                        smooth="calibrated")
+    y = bq.svdq_w4a4_mlp_gelu(dev_bf16(x), bq.SVDQLinear.from_numpy(lay_up), bq.SVDQLinear.from_numpy(lay_down))
+    torch.cuda.synchronize()
+    assert_output(y, L.mlp_gelu_ref(hb, lay_down), f"fused mlp M={M} {up_prec} r{ranks}")
+
+
+def test_mlp_gelu_rejects_int4_down():
+    rng = np.random.default_rng(5)
+    x = S.activations(64, 256, 0, rng)
+    up = bq.SVDQLinear.from_numpy(prepared(x, S.weight(256, 256, 0.02, rng), None, "nvfp4", 16))
+    down = bq.SVDQLinear.from_numpy(prepared(x, S.weight(128, 256, 0.02, rng), None, "int4", 16))
+    with pytest.raises(bq.SvdqError) as e:
+        bq.svdq_w4a4_mlp_gelu(dev_bf16(x), up, down)
+    assert e.value.status == -2
+
+
 def test_stack_qkv_sampled():
     # the DiT stack's fused QKV shape, 3072 -> 9216 nvfp4 rank 32 at 4096 tokens
     x, w, b = S.svdq_problem(4096, 3072, 9216, seed=5, n_outliers=31)

@@ -226,3 +226,47 @@ def test_group_sizes_match_the_pages_table():
     ex = json.load(open(os.path.join(GOLDEN, "config_example.json")))
     assert ex["svdq"]["group_size"] == L.GROUP[ex["svdq"]["precision"]]
     assert ex["compute_dtype"] == "bfloat16"
+
+
+# ------------------------------------------------------------------ GELU (MLP fusion)
+def test_gelu_identities():
+    # gelu(y) - gelu(-y) = y (the erf term is odd), gelu(0) = 0, and
+    # gelu(y) -> y for large y, gelu(y) -> 0 for large negative y
+    y = np.linspace(-8, 8, 4001)
+    assert np.allclose(L.gelu_f64(y) - L.gelu_f64(-y), y, rtol=0, atol=1e-14)
+    assert L.gelu_f64(np.array([0.0]))[0] == 0.0
+    assert np.allclose(L.gelu_f64(np.array([30.0, -30.0])), [30.0, 0.0], rtol=0, atol=1e-12)
+    # closed form at y = sqrt(2): sqrt(2)/2 (1 + erf(1)), erf(1) = 0.8427007929497149
+    assert abs(L.gelu_f64(np.array([np.sqrt(2.0)]))[0] - np.sqrt(2.0) / 2 * (1 + 0.8427007929497149)) < 1e-15
+
+
+def test_gelu_matches_high_precision():
+    # the definition y/2 (1 + erf(y / sqrt 2)) evaluated with mpmath at 90
+    # digits (enough to survive the cancellation of 1 + erf down to y = -14),
+    # on every finite bf16 value with |y| < 14; beyond, the negative tail lies
+    # below the bf16 range and the positive one equals y
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 90
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    v = F.bf16_to_f32(bits)
+    bits = bits[np.isfinite(v) & (np.abs(v) < 14)]
+    y = F.bf16_to_f32(bits).astype(np.float64)
+    exact = np.array([float(mp.mpf(t) / 2 * (1 + mp.erf(mp.mpf(t) / mp.sqrt(2)))) for t in y])
+    got = L.gelu_f64(y)
+    scale = np.maximum(np.abs(exact), 1e-300)
+    assert np.max(np.abs(got - exact) / scale) < 1e-13  # scipy erfc: a few 1e-14 in the far tail
+    # bf16: one rounding of the correctly rounded value, equal bits (a tie
+    # between the two fp64 values and a bf16 boundary aside)
+    assert (L.gelu_bf16(bits) != F.bf16_bits_f64(exact)).sum() <= 1
+    tail = np.array([-14.0, -20.0, -63.5])
+    assert np.all(np.abs(L.gelu_f64(tail)) < 2.0 ** -130)
+    assert np.array_equal(L.gelu_f64(np.array([14.0, 20.0, 63.5])), [14.0, 20.0, 63.5])
+
+
+def test_gelu_matches_torch():
+    # torch's exact-erf GELU in float64 (a library routine), where its 1 + erf
+    # form keeps full accuracy (y >= -4)
+    torch = pytest.importorskip("torch")
+    y = np.random.default_rng(0).uniform(-4, 8, 20000)
+    ref = torch.nn.functional.gelu(torch.from_numpy(y), approximate="none").numpy()
+    assert np.allclose(L.gelu_f64(y), ref, rtol=1e-11, atol=1e-300)
