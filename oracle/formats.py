@@ -176,15 +176,17 @@ def unpack_nibbles(packed):
 def bf16_bits_f64(x):
     """float64 -> bfloat16 bits with a single round-to-nearest-even step.
 
-    Used for weight preparation, where values start in float64: the value is
-    written as m * 2^e with 0.5 <= |m| < 1, m is rounded to 8 significant bits
-    with ``np.rint`` (exact scaling by 256), and the result -- exactly
-    representable in float32 and bfloat16 -- is re-encoded.  Magnitudes below
-    the float32 normal range are flushed to signed zero (never reached by the
-    weights this is applied to).
+    Values start in float64 (weight preparation, the GELU reference).  A
+    normal value is written as m * 2^e with 0.5 <= |m| < 1 and m rounded to 8
+    significant bits with ``np.rint`` (exact scaling by 256); below the
+    normal range (|x| < 2^-126) bfloat16 has the fixed quantum 2^-133 of its
+    subnormals, and x / 2^-133 is rounded with ``np.rint``.  The result is
+    exactly representable in float32 and bfloat16 and is re-encoded.
     """
     x = np.asarray(x, dtype=np.float64)
     m, e = np.frexp(x)
     r = np.ldexp(np.rint(m * 256.0), e - 8)
-    r = np.where(np.abs(r) < 2.0 ** -126, np.copysign(0.0, x), r)
+    sub = np.abs(x) < 2.0 ** -126
+    r = np.where(sub, np.rint(x * 2.0 ** 133) * 2.0 ** -133, r)
+    r = np.where(r == 0, np.copysign(0.0, x), r)
     return bf16_bits(r.astype(F32))

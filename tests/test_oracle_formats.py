@@ -70,6 +70,21 @@ def test_bf16_from_f64_single_rounding_brute_force():
     assert np.all(k % 2 == 0)
 
 
+def test_bf16_from_f64_subnormals():
+    # below 2^-126 the bf16 grid has the fixed quantum 2^-133: values that are
+    # exactly float32 take the float32 route's rounding (bf16_bits, integer
+    # rounding of the bit pattern), and exact halfway points go to even
+    rng = np.random.default_rng(2)
+    x32 = (rng.integers(1, 2 ** 23, 5000).astype(np.uint32)).view(np.float32)  # float32 subnormals
+    x32 = np.concatenate([x32, -x32])
+    assert np.array_equal(F.bf16_bits_f64(x32.astype(np.float64)), F.bf16_bits(x32))
+    q = 2.0 ** -133
+    ties = (np.arange(1, 200) * 2 + 1) * q / 2   # halfway between k q and (k + 1) q
+    k = np.rint(F.bf16_to_f32(F.bf16_bits_f64(ties)).astype(np.float64) / q).astype(np.int64)
+    assert np.all(k % 2 == 0)
+    assert F.bf16_bits_f64(np.array([q / 4]))[0] == 0 and F.bf16_bits_f64(np.array([-q / 4]))[0] == 0x8000
+
+
 # ---------------------------------------------------------------- E4M3
 ALL_E4M3 = np.arange(256, dtype=np.uint32).astype(np.uint8)
 

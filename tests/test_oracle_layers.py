@@ -256,7 +256,8 @@ def test_gelu_matches_high_precision():
     scale = np.maximum(np.abs(exact), 1e-300)
     assert np.max(np.abs(got - exact) / scale) < 1e-13  # scipy erfc: a few 1e-14 in the far tail
     # bf16: one rounding of the correctly rounded value, equal bits (a tie
-    # between the two fp64 values and a bf16 boundary aside)
+    # between the two fp64 values and a bf16 boundary aside; mpmath's zero is
+    # unsigned, gelu(-0) = -0)
     assert (L.gelu_bf16(bits) != F.bf16_bits_f64(exact)).sum() <= 1
     tail = np.array([-14.0, -20.0, -63.5])
     assert np.all(np.abs(L.gelu_f64(tail)) < 2.0 ** -130)
