@@ -121,11 +121,32 @@ __device__ __forceinline__ void tile_of(int bid, int nmt, int nnt, int& mt, int&
 // operand-layout reads).
 constexpr int kGeluRow = 208;
 
+// erfc(z) for z >= 0 by the Chebyshev fit of Numerical Recipes in C (2nd
+// ed., section 6.2, "erfcc"): t = 1 / (1 + z/2), erfc(z) = t exp(-z^2 +
+// P(t)) with a 9th-degree P, fractional error below 1.2e-7 for every z >= 0.
+__device__ __forceinline__ float erfc_cheb(float z) {
+  const float t = __builtin_amdgcn_rcpf(__fmaf_rn(0.5f, z, 1.0f));
+  float q = 0.17087277f;
+  q = __fmaf_rn(t, q, -0.82215223f);
+  q = __fmaf_rn(t, q, 1.48851587f);
+  q = __fmaf_rn(t, q, -1.13520398f);
+  q = __fmaf_rn(t, q, 0.27886807f);
+  q = __fmaf_rn(t, q, -0.18628806f);
+  q = __fmaf_rn(t, q, 0.09678418f);
+  q = __fmaf_rn(t, q, 0.37409196f);
+  q = __fmaf_rn(t, q, 1.00002368f);
+  q = __fmaf_rn(t, q, -1.26551223f);
+  return __fmul_rn(t, __expf(__fmaf_rn(-z, z, q)));
+}
+
 // GELU with the exact erf, y/2 (1 + erf(y / sqrt 2)), on an fp32 value,
-// evaluated as (y / 2) erfc(-y / sqrt 2): the same function without the
-// cancellation of 1 + erf for negative y.
+// evaluated as (y / 2) erfc(-y / sqrt 2) -- no cancellation of 1 + erf for
+// negative y -- with erfc(-a) = 2 - erfc(a) for y > 0.  A float32 model of
+// this evaluation (exact exp in place of __expf), rounded to bf16, gives the
+// correctly rounded GELU of every bf16 input with a normal result.
 __device__ __forceinline__ float gelu_erf(float y) {
-  return __fmul_rn(__fmul_rn(y, 0.5f), erfcf(__fmul_rn(y, -0.70710678118654752f)));
+  const float e = erfc_cheb(__fmul_rn(fabsf(y), 0.70710678118654752f));
+  return __fmul_rn(__fmul_rn(y, 0.5f), y > 0.f ? __fsub_rn(2.0f, e) : e);
 }
 
 // The MLP fusion epilogue of one wave ("Fused kernels" of the Nunchaku Lite
@@ -135,12 +156,15 @@ __device__ __forceinline__ float gelu_erf(float y) {
 //  1. g = bf16(GELU(bf16(acc + bias))) -- the values a bf16 up output followed
 //     by a bf16 GELU would give -- into the wave's LDS tile `tile_base`
 //     (+ 64 kGeluRow for odd waves);
-//  2. lane l takes tile row l: x = fl32(g * (1 / smooth_next)), nvfp4 per 16
-//     columns (nvfp4_quant16, the quantize kernel's reading), and stores the
-//     next layer's product operand e2m1 * dec(s8) as fp16;
-//  3. the next layer's low-rank activations: the same x in the 16x16x32 bf16
-//     operand layout, split hi + lo, times next_lora_down, added into
-//     next_lora_act with fp32 atomics (one partial per wave and tile).
+//  2. the next layer's low-rank activations: x = fl32(g * (1 / smooth_next))
+//     in the 16x16x32 bf16 operand layout, split hi + lo, times
+//     next_lora_down, added into next_lora_act with fp32 atomics (one
+//     partial per wave and tile);
+//  3. lane l takes tile row l: the same x, nvfp4 per 16 columns
+//     (nvfp4_quant16, the quantize kernel's reading); the next layer's
+//     product operand e2m1 * dec(s8) as fp16 overwrites the lane's own tile
+//     row, and the wave then stores the tile with consecutive lanes on
+//     consecutive 16-byte pieces of a row.
 // Columns past N have 1/smooth 0 (x = 0) and are not stored; rows past M are
 // not stored.
 __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16 (&acc)[kIB][kJB], int m0, int n0,
@@ -172,37 +196,10 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
   }
   // (the wave's own LDS writes and reads execute in order)
 
-  // 2. quantization for the next layer, one tile row per lane
+  // 2 and 3 both read the next layer's 1 / smooth of this wave's columns
   const float* mu = nmu + wn * (kJB * 32);
-  {
-    const int m = m0 + wm * 64 + lane;
-    const uint8_t* rowp = gt + lane * kGeluRow;
-    _Float16* dst = (_Float16*)args.next_act + (size_t)m * N + n0 + wn * (kJB * 32);
-#pragma unroll
-    for (int t = 0; t < 6; ++t) {
-      const u32x4 g0 = *(const u32x4*)(rowp + 32 * t);
-      const u32x4 g1 = *(const u32x4*)(rowp + 32 * t + 16);
-      float x[16];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        x[2 * p] = __fmul_rn(bf16_lo(g0[p]), mu[16 * t + 2 * p]);
-        x[2 * p + 1] = __fmul_rn(bf16_hi(g0[p]), mu[16 * t + 2 * p + 1]);
-        x[8 + 2 * p] = __fmul_rn(bf16_lo(g1[p]), mu[16 * t + 8 + 2 * p]);
-        x[8 + 2 * p + 1] = __fmul_rn(bf16_hi(g1[p]), mu[16 * t + 8 + 2 * p + 1]);
-      }
-      uint32_t cw0, cw1;
-      float S;
-      nvfp4_quant16(x, cw0, cw1, S);
-      // e2m1 * dec(s8) is an exact fp16 (|v| <= 2688, >= 2^-10)
-      const _Float16 S16 = (_Float16)S;
-      if (m < M && n0 + wn * (kJB * 32) + 16 * t < N) {
-        *(f16x8*)(dst + 16 * t) = e2m1x8_to_f16_scaled(cw0, S16);
-        *(f16x8*)(dst + 16 * t + 8) = e2m1x8_to_f16_scaled(cw1, S16);
-      }
-    }
-  }
-
-  // 3. the next layer's low-rank down projection of this tile's columns
+  // 2. the next layer's low-rank down projection of this tile's columns (it
+  // reads the GELU values before step 3 replaces them)
   const int nrank = args.next_rank;
   if (nrank > 0) {
     const int r16 = lane & 15, q = lane >> 4;
@@ -251,6 +248,44 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
           if (m < M) unsafeAtomicAdd(args.next_lora_act + (size_t)m * nrank + rk + r16, d[j]);
         }
       }
+    }
+  }
+
+  // 3. quantization for the next layer, one tile row per lane; each group's
+  // fp16 operand replaces its GELU values in the lane's own tile row, then
+  // the wave copies the tile out with row-contiguous lanes
+  {
+    uint8_t* rowp = gt + lane * kGeluRow;
+#pragma unroll
+    for (int t = 0; t < 6; ++t) {
+      const u32x4 g0 = *(const u32x4*)(rowp + 32 * t);
+      const u32x4 g1 = *(const u32x4*)(rowp + 32 * t + 16);
+      float x[16];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        x[2 * p] = __fmul_rn(bf16_lo(g0[p]), mu[16 * t + 2 * p]);
+        x[2 * p + 1] = __fmul_rn(bf16_hi(g0[p]), mu[16 * t + 2 * p + 1]);
+        x[8 + 2 * p] = __fmul_rn(bf16_lo(g1[p]), mu[16 * t + 8 + 2 * p]);
+        x[8 + 2 * p + 1] = __fmul_rn(bf16_hi(g1[p]), mu[16 * t + 8 + 2 * p + 1]);
+      }
+      uint32_t cw0, cw1;
+      float S;
+      nvfp4_quant16(x, cw0, cw1, S);
+      // e2m1 * dec(s8) is an exact fp16 (|v| <= 2688, >= 2^-10)
+      const _Float16 S16 = (_Float16)S;
+      *(f16x8*)(rowp + 32 * t) = e2m1x8_to_f16_scaled(cw0, S16);
+      *(f16x8*)(rowp + 32 * t + 16) = e2m1x8_to_f16_scaled(cw1, S16);
+    }
+    // copy-out: 16-byte chunk c of the 64 x 192-byte tile, c = 64 i + lane,
+    // is row c / 12, bytes 16 (c % 12) of it
+    const int c0 = n0 + wn * (kJB * 32);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      const int c = 64 * i + lane;
+      const int r = c / 12, k = c - 12 * r;
+      const u32x4 v = *(const u32x4*)(gt + r * kGeluRow + 16 * k);
+      const int m = m0 + wm * 64 + r;
+      if (m < M && c0 + 8 * k < N) *(u32x4*)((_Float16*)args.next_act + (size_t)m * N + c0 + 8 * k) = v;
     }
   }
 }
