@@ -16,7 +16,9 @@ Also measured in the same run (reported under "extra"):
     timed as a captured graph of 48 launches replayed (a ~10 us kernel is
     close to the host's per-call launch cost, which the graph leaves out);
   * the nvfp4 MLP pair 3072 -> 12288 -> 3072 at M=4096 (exact-erf GELU on the
-    bf16 up output, a torch op, between the two library calls);
+    bf16 up output, a torch op, between the two library calls), and the same
+    pair fused (svdq_w4a4_mlp_gelu: GELU and the down projection's
+    quantization in the up projection's epilogue);
   * the DiT stack per pass: 24 blocks of QKV 3072->9216, out 3072->3072, MLP
     up/GELU/down (svdq nvfp4, rank 32, 4096 tokens) and the adaLN modulation
     linear 3072->18432 (awq_w4a16, one token; its 24 launches per pass are
@@ -91,15 +93,25 @@ def bench_mlp_pair(bq, S, torch, np, x, M, K, rank, stream, hidden=12288, reps=5
         f_up()
         f_gelu()
         f_dn()
+    # the fused MLP: GELU and the down projection's quantization in the up
+    # projection's epilogue (no [M, hidden] bf16 tensor)
+    ws_mlp = torch.empty(bq.mlp_workspace_bytes(M, up, down), dtype=torch.uint8, device="cuda")
+    y_f = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    f_fused = lambda: bq.svdq_w4a4_mlp_gelu(x, up, down, out=y_f, workspace=ws_mlp)
     for _ in range(10):
         pair()
+        f_fused()
     t_up, t_gelu, t_dn = (time_events(f, reps, stream) for f in (f_up, f_gelu, f_dn))
     t_pair = time_events(pair, reps, stream)
+    t_fused = time_events(f_fused, reps, stream)
     ops = 2.0 * M * hidden * K * 2
     return {"up_us": round(t_up * 1e3, 2), "gelu_us": round(t_gelu * 1e3, 2), "down_us": round(t_dn * 1e3, 2),
             "pair_us": round(t_pair * 1e3, 2),
             "svdq_TOPS": round(ops / ((t_up + t_dn) * 1e-3) / 1e12, 1),
-            "pair_TOPS_incl_gelu": round(ops / (t_pair * 1e-3) / 1e12, 1)}
+            "pair_TOPS_incl_gelu": round(ops / (t_pair * 1e-3) / 1e12, 1),
+            "fused_pair_us": round(t_fused * 1e3, 2),
+            "fused_pair_TOPS": round(ops / (t_fused * 1e-3) / 1e12, 1),
+            "fused_speedup": round(t_pair / t_fused, 3)}
 
 
 def bench_stack(bq, S, torch, np, M, rank, stream):
