@@ -19,6 +19,7 @@ import torch
 
 import synthetic as S
 from oracle import formats as F, layers as L
+from exact_mlp import exact_up_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -349,26 +350,35 @@ def test_mlp_pair_up_config2_sampled(mlp_up):
 
 
 def test_mlp_pair_down_config2_sampled(mlp_up):
-    # down-projection 12288 -> 3072 on GELU of the up output (exact erf on the
-    # bf16 tensor, a torch op between the two library calls)
-    c, _, _, h = mlp_up
-    g = host_bits(torch.nn.functional.gelu(h))
+    # down-projection 12288 -> 3072 at M = 4096 on post-GELU activations: the
+    # oracle's bf16 GELU of synthetic activations with outlier channels
+    c = mlp_up[0]
+    g = L.gelu_bf16(S.activations(4096, 12288, 123, np.random.default_rng(12288)))
     lay = prepared(g, c["w_down"], c["b_down"], "nvfp4", 32, smooth="calibrated")
     y = run_linear(g, lay)
     assert_output(y[SAMPLE_ROWS], L.svdq_linear_ref(g[SAMPLE_ROWS], lay), "mlp down 12288->3072")
 
 
+# The fused MLP never exposes its up output h; its parity tests use up layers
+# on which the fp32 product is exact (tests/exact_mlp.py), so that bf16(h) is
+# unique and the oracle computes the whole chain from x alone.  The fused
+# kernel's main loop is the plain linear's, checked on general inputs above.
+def fused_mlp_ref(x, lay_up, w_down, b_down, rank_down):
+    h = F.bf16_bits_f64(L.svdq_linear_ref(x, lay_up))
+    lay_down = prepared(L.gelu_bf16(h), w_down, b_down, "nvfp4", rank_down, smooth="calibrated")
+    return lay_down, L.mlp_gelu_ref(h, lay_down)
+
+
 def test_mlp_gelu_fused_config2_sampled(mlp_up):
     # the fused MLP (GELU and the nvfp4 quantization for the down projection
     # in the up projection's epilogue) at 3072 -> 12288 -> 3072, M = 4096,
-    # against the oracle's down half on the GPU's own up output h (the fused
-    # kernel computes the same h internally)
-    c, x, lay_up, h = mlp_up
-    hb = host_bits(h)
-    lay_down = prepared(L.gelu_bf16(hb), c["w_down"], c["b_down"], "nvfp4", 32, smooth="calibrated")
+    # rank 32 in both layers
+    c = mlp_up[0]
+    x, lay_up = exact_up_problem(4096, 3072, 12288, "nvfp4", 32, np.random.default_rng(77))
+    lay_down, y_ref = fused_mlp_ref(x[SAMPLE_ROWS], lay_up, c["w_down"], c["b_down"], 32)
     y = bq.svdq_w4a4_mlp_gelu(dev_bf16(x), bq.SVDQLinear.from_numpy(lay_up), bq.SVDQLinear.from_numpy(lay_down))
     torch.cuda.synchronize()
-    assert_output(y[SAMPLE_ROWS], L.mlp_gelu_ref(hb[SAMPLE_ROWS], lay_down), "fused mlp 3072->12288->3072")
+    assert_output(y[SAMPLE_ROWS], y_ref, "fused mlp 3072->12288->3072")
 
 
 @pytest.mark.parametrize("M,up_prec,ranks", [(1, "nvfp4", (32, 32)), (37, "int4", (32, 32)),
@@ -379,15 +389,11 @@ def test_mlp_gelu_fused_ragged(M, up_prec, ranks):
     # ragged against the 256-row tiles; every rank block path of the epilogue
     rng = np.random.default_rng(M + ranks[0])
     K, H, N = 256, 640, 320
-    x = S.activations(M, K, 3, rng)
-    lay_up = prepared(x, S.weight(H, K, 0.02, rng, spike_rank=2), S.bias(H, rng), up_prec, ranks[0],
-                      smooth="calibrated")
-    hb = host_bits(run_linear(x, lay_up))
-    lay_down = prepared(L.gelu_bf16(hb), S.weight(N, H, 0.02, rng), S.bias(N, rng), "nvfp4", ranks[1],
-                        smooth="calibrated")
+    x, lay_up = exact_up_problem(M, K, H, up_prec, ranks[0], rng)
+    lay_down, y_ref = fused_mlp_ref(x, lay_up, S.weight(N, H, 0.02, rng), S.bias(N, rng), ranks[1])
     y = bq.svdq_w4a4_mlp_gelu(dev_bf16(x), bq.SVDQLinear.from_numpy(lay_up), bq.SVDQLinear.from_numpy(lay_down))
     torch.cuda.synchronize()
-    assert_output(y, L.mlp_gelu_ref(hb, lay_down), f"fused mlp M={M} {up_prec} r{ranks}")
+    assert_output(y, y_ref, f"fused mlp M={M} {up_prec} r{ranks}")
 
 
 def test_mlp_gelu_rejects_int4_down():

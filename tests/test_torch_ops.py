@@ -60,32 +60,37 @@ def layers():
     lay = L.prepare_svdq_layer(w, L.smooth_factors(x, w), 32, "int4", S.bias(N, rng))
     wa = rng.standard_normal((Na, N)) * 0.02
     alay = L.prepare_awq_layer(wa, S.bias(Na, rng))
-    return x, lay, alay
+    xa = S.activations(M, N, 3, rng)
+    return x, lay, alay, xa
 
 
 @pytest.mark.gpu
 def test_custom_ops_match_binding_and_oracle(layers):
-    x, lay, alay = layers
+    x, lay, alay, xa = layers
     layer, alayer = bq.SVDQLinear.from_numpy(lay), bq.AWQLinear.from_numpy(alay)
-    xd = dev_bf16(x)
+    xd, xad = dev_bf16(x), dev_bf16(xa)
     y_op = T.svdq_linear(xd, layer)
     y_b = bq.svdq_w4a4_linear(xd, layer)
-    h_op = T.awq_linear(y_op, alayer)
-    h_b = bq.awq_w4a16_linear(y_b, alayer)
+    h_op = T.awq_linear(xad, alayer)
+    h_b = bq.awq_w4a16_linear(xad, alayer)
+    # chained, as a model calls them
+    c_op = T.awq_linear(y_op, alayer)
+    c_b = bq.awq_w4a16_linear(y_b, alayer)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(y_op), host_bits(y_b))
     assert np.array_equal(host_bits(h_op), host_bits(h_b))
+    assert np.array_equal(host_bits(c_op), host_bits(c_b))
     y = F.bf16_to_f32(host_bits(y_op)).astype(np.float64)
     _, excess, mre = L.output_errors(y, L.svdq_linear_ref(x, lay))
     assert excess <= 1e-2 and mre <= 2e-3
     h = F.bf16_to_f32(host_bits(h_op)).astype(np.float64)
-    _, excess, mre = L.output_errors(h, L.awq_linear_ref(host_bits(y_op), alay))
+    _, excess, mre = L.output_errors(h, L.awq_linear_ref(xa, alay))
     assert excess <= 1e-2 and mre <= 2e-3
 
 
 @pytest.mark.gpu
 def test_custom_ops_opcheck(layers):
-    x, lay, alay = layers
+    x, lay, alay, _ = layers
     layer, alayer = bq.SVDQLinear.from_numpy(lay), bq.AWQLinear.from_numpy(alay)
     xd = dev_bf16(x)
     torch.library.opcheck(torch.ops.svdq.w4a4_linear.default,
@@ -100,7 +105,7 @@ def test_custom_ops_opcheck(layers):
 @pytest.mark.parametrize("backend", ["aot_eager", "inductor"])
 def test_compile_fullgraph(layers, backend):
     # an elementwise op between the two linears, which Inductor generates itself
-    x, lay, alay = layers
+    x, lay, alay, _ = layers
     layer, alayer = bq.SVDQLinear.from_numpy(lay), bq.AWQLinear.from_numpy(alay)
     xd = dev_bf16(x)
 
