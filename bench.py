@@ -249,14 +249,15 @@ def time_graph(calls, reps, stream):
     return e0.elapsed_time(e1) / reps  # ms per replay
 
 
-ONLY_LEGS = {"quant_int4", "quant_nvfp4", "gemm_int4", "gemm_nvfp4", "awq_m1", "awq_m16", "copy"}
+ONLY_LEGS = {"quant_int4", "quant_nvfp4", "gemm_int4", "gemm_nvfp4", "awq_m1", "awq_m16", "mlp_fused", "copy"}
 
 
 def run_only(leg, steps):
     """Launch a single kernel of the headline workload `steps` times (after one
-    warm-up call), for per-kernel hardware-counter passes.  `copy` is a plain
-    device-to-device copy of 256 MiB, the reference for scaling HBM byte
-    counters."""
+    warm-up call), for per-kernel hardware-counter passes.  `mlp_fused` is the
+    fused GELU MLP pair (nvfp4, M=4096, 3072 -> 12288 -> 3072, rank 32).
+    `copy` is a plain device-to-device copy of 256 MiB, the reference for
+    scaling HBM byte counters."""
     import numpy as np
     import torch
 
@@ -281,6 +282,16 @@ def run_only(leg, steps):
         def fn():
             layers[it[0] % 12](xa, out=oa)
             it[0] += 1
+    elif leg == "mlp_fused":
+        H = 12288
+        r_up, r_dn = S.streams(11, 2)
+        rx = S.streams(0, 2)[0]
+        up = bq.SVDQLinear.from_numpy(S.random_svdq_layer(H, K, "nvfp4", rank, r_up))
+        down = bq.SVDQLinear.from_numpy(S.random_svdq_layer(K, H, "nvfp4", rank, r_dn))
+        x = torch.from_numpy(S.activations(M, K, round(0.01 * K), rx).view(np.int16).copy()).view(torch.bfloat16).cuda()
+        ws = torch.empty(bq.mlp_workspace_bytes(M, up, down), dtype=torch.uint8, device="cuda")
+        y = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: bq.svdq_w4a4_mlp_gelu(x, up, down, out=y, workspace=ws)
     else:
         precision = "int4" if leg.endswith("int4") else "nvfp4"
         rx, rl = S.streams(0, 2)

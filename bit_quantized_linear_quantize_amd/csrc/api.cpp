@@ -193,11 +193,14 @@ Carve carve(void* workspace, int64_t M, int64_t K, int precision) {
   return c;
 }
 
+// Kernel 1 into the workspace; `clear` (clear_n floats, optional) is set to
+// zero by the same launch.
 int launch_quantize(const void* x, int64_t M, int64_t K, const void* smooth, const void* lora_down,
-                    int precision, int rank, void* workspace, hipStream_t s) {
+                    int precision, int rank, void* workspace, hipStream_t s, float* clear = nullptr,
+                    int64_t clear_n = 0) {
   const Carve c = carve(workspace, M, K, precision);
   svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, c.lora_act, c.act_f16, c.row_scale,
-                        M, K, precision, rank};
+                        M, K, precision, rank, clear, clear_n};
   return launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
 }
 
@@ -462,16 +465,14 @@ int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up, cons
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t H = up->N;
-  // up layer: kernel 1 into the first part of the workspace
-  rc = launch_quantize(x, M, up->K, up->smooth, up->lora_down, up->precision, up->rank, workspace, s);
-  if (rc) return rc;
   const Carve cu = carve(workspace, M, up->K, up->precision);
   void* ws_down = static_cast<uint8_t*>(workspace) + workspace_bytes(M, up->K, up->precision, up->rank);
   const Carve cd = carve(ws_down, M, H, SVDQ_NVFP4);
-  if (down->rank > 0) {
-    rc = launch_status(svdq::launch_zero_f32(cd.lora_act, M * down->rank, s), "zero fill launch");
-    if (rc) return rc;
-  }
+  // up layer: kernel 1 into the first part of the workspace; the same launch
+  // clears the down layer's low-rank accumulator
+  rc = launch_quantize(x, M, up->K, up->smooth, up->lora_down, up->precision, up->rank, workspace, s,
+                       cd.lora_act, M * down->rank);
+  if (rc) return rc;
   // up layer: kernel 2 with the GELU + nvfp4 epilogue writing the down
   // layer's workspace (its bf16 output is not stored)
   svdq::GemmArgs ga{cu.act_f16, cu.row_scale, cu.lora_act, up->packed_w, up->wscales, up->lora_up, up->bias,

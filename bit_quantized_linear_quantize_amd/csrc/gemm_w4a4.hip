@@ -697,16 +697,4 @@ hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream) {
   return geluq ? dispatch_rank<kNvfp4, false, true>(a, stream) : dispatch_rank<kNvfp4, false, false>(a, stream);
 }
 
-__global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
-}
-
-// Clears n floats with a kernel (also inside a captured graph).
-hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n);
-  return hipGetLastError();
-}
-
 }  // namespace svdq

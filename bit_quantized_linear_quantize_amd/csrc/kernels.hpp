@@ -20,6 +20,8 @@ struct QuantActArgs {
   float* row_scale;       // linear int4 only: f32 [M] power-of-two factor of each row of act_f16
   int64_t M, K;
   int precision, rank;
+  float* clear = nullptr;  // optional: f32 [clear_n] set to zero by the same launch (the fused
+  int64_t clear_n = 0;     // MLP's accumulator for the next layer's low-rank activations)
 };
 
 // act_f16 holds the dequantized activations exactly: int4 q * s * 2^-E[m]
@@ -62,6 +64,5 @@ struct AwqArgs {
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream);
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream);
-hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 
 }  // namespace svdq

@@ -74,6 +74,12 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
+  // optional side job: clear args.clear (grid-stride over all workgroups)
+  if constexpr (LINEAR) {
+    for (int64_t i = (int64_t)blockIdx.x * kK1Threads + tid; i < args.clear_n; i += (int64_t)gridDim.x * kK1Threads)
+      args.clear[i] = 0.f;
+  }
+
   // 1 / smooth for every input channel (IEEE division, one per channel).
   for (int k = tid; k < K; k += kK1Threads) lds[k] = __fdiv_rn(1.0f, bf16_bits_to_f32(smooth[k]));
   __syncthreads();
