@@ -218,6 +218,58 @@ def mlp_gelu_ref(h_bits, down):
     return svdq_linear_ref(gelu_bf16(h_bits), down)
 
 
+# ----------------------------------------------------------------------------
+# fused QKV projection with RMSNorm and RoPE ("Fused kernels" section of the
+# Nunchaku Lite docs: the original engine merges the Q, K and V projections
+# with RMSNorm and RoPE).  Readings: the layout is one [M, 3 H D] output
+# q | k | v, heads of D consecutive columns; q and k get a per-head RMSNorm
+# with their own learned weights [D], then the rotary embedding on interleaved
+# pairs (2i, 2i+1) with per-token angle tables; v is the projection itself.
+# The value chain is that of separate bf16 ops: h = bf16(linear), n =
+# bf16(RMSNorm(h)), out = bf16(RoPE(n)).
+# ----------------------------------------------------------------------------
+def rmsnorm_bf16(h_bits, w_bits, eps):
+    """RMSNorm over the last axis of bf16 values: h / sqrt(mean(h^2) + eps) * w,
+    in fp64, rounded once to bf16.  Takes and returns bf16 bit patterns."""
+    h = bf16_to_f32(h_bits).astype(np.float64)
+    w = bf16_to_f32(w_bits).astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + float(eps))
+    return bf16_bits_f64(h * r * w)
+
+
+def rope_f64(n, cos, sin):
+    """Rotary embedding on interleaved pairs of the last axis, in fp64:
+    (a, b) at columns (2i, 2i+1) -> (a cos_i - b sin_i, a sin_i + b cos_i).
+    n [..., D] float; cos, sin [..., D/2] broadcast against n's leading axes."""
+    n = np.asarray(n, dtype=np.float64)
+    a, b = n[..., 0::2], n[..., 1::2]
+    c, s = np.asarray(cos, np.float64), np.asarray(sin, np.float64)
+    out = np.empty_like(n)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
+def qkv_norm_rope_ref(x_bits, layer, heads, q_norm_bits, k_norm_bits, eps, cos, sin):
+    """Reference of the fused QKV projection + RMSNorm + RoPE, fp64.
+
+    x [M, K] bf16 bits; ``layer`` a prepared svdq layer with N = 3 heads D;
+    q_norm / k_norm bf16 bits [D]; cos, sin float32 [M, D/2] (per token).
+    Returns [M, N] float64: q and k columns are RoPE(RMSNorm(bf16(h))) before
+    the final bf16 rounding, v columns are the linear's own fp64 output."""
+    h64 = svdq_linear_ref(x_bits, layer)
+    M, N = h64.shape
+    D = N // (3 * heads)
+    h = bf16_bits_f64(h64)
+    out = h64.copy()
+    for part, wb in ((0, q_norm_bits), (1, k_norm_bits)):
+        cols = slice(part * heads * D, (part + 1) * heads * D)
+        hp = h[:, cols].reshape(M, heads, D)
+        n = bf16_to_f32(rmsnorm_bf16(hp, wb, eps)).astype(np.float64)
+        out[:, cols] = rope_f64(n, np.asarray(cos)[:, None, :], np.asarray(sin)[:, None, :]).reshape(M, heads * D)
+    return out
+
+
 def awq_dequant(layer):
     G = layer["group_size"]
     q = layer["q"].astype(np.float64)

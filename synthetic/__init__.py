@@ -63,6 +63,22 @@ def bias(N, rng, std=0.01):
     return to_bf16_bits(rng.standard_normal(N) * std)
 
 
+def rope_tables(M, D, base=10000.0, offset=0):
+    """Rotary-embedding angle tables for M tokens at positions offset ..
+    offset + M - 1 and head dim D: angle[m, i] = pos_m * base^(-2i/D),
+    returned as float32 (cos, sin) [M, D/2].  The model's positional input,
+    not part of the layer."""
+    pos = np.arange(offset, offset + M, dtype=np.float64)[:, None]
+    inv = base ** (-np.arange(0, D, 2, dtype=np.float64) / D)[None, :]
+    ang = pos * inv
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def norm_weight(D, rng):
+    """A learned RMSNorm weight [D] as bf16 bits, around 1."""
+    return to_bf16_bits(1.0 + 0.1 * rng.standard_normal(D))
+
+
 # ----------------------------------------------------------------------------
 # the five workloads
 # ----------------------------------------------------------------------------

@@ -271,3 +271,79 @@ def test_gelu_matches_torch():
     y = np.random.default_rng(0).uniform(-4, 8, 20000)
     ref = torch.nn.functional.gelu(torch.from_numpy(y), approximate="none").numpy()
     assert np.allclose(L.gelu_f64(y), ref, rtol=1e-11, atol=1e-300)
+
+
+# ------------------------------------------------------------------ QKV + RMSNorm + RoPE
+def test_rope_matches_complex_rotation():
+    # interleaved pairs as complex numbers a + ib times e^{i theta}
+    rng = np.random.default_rng(3)
+    n = rng.standard_normal((5, 4, 16))
+    th = rng.uniform(-40, 40, (5, 1, 8))
+    got = L.rope_f64(n, np.cos(th), np.sin(th))
+    z = (n[..., 0::2] + 1j * n[..., 1::2]) * np.exp(1j * th)
+    assert np.allclose(got[..., 0::2], z.real, rtol=0, atol=1e-12)
+    assert np.allclose(got[..., 1::2], z.imag, rtol=0, atol=1e-12)
+
+
+def test_rope_identities():
+    rng = np.random.default_rng(4)
+    n = rng.standard_normal((3, 8))
+    assert np.array_equal(L.rope_f64(n, np.ones((3, 4)), np.zeros((3, 4))), n)
+    # quarter turn: (a, b) -> (-b, a)
+    q = L.rope_f64(n, np.zeros((3, 4)), np.ones((3, 4)))
+    assert np.array_equal(q[:, 0::2], -n[:, 1::2]) and np.array_equal(q[:, 1::2], n[:, 0::2])
+    # pair norms are kept; rotations compose
+    a, b = rng.uniform(-3, 3, (3, 4)), rng.uniform(-3, 3, (3, 4))
+    r1 = L.rope_f64(L.rope_f64(n, np.cos(a), np.sin(a)), np.cos(b), np.sin(b))
+    r2 = L.rope_f64(n, np.cos(a + b), np.sin(a + b))
+    assert np.allclose(r1, r2, atol=1e-12)
+    assert np.allclose(r1[:, 0::2] ** 2 + r1[:, 1::2] ** 2, n[:, 0::2] ** 2 + n[:, 1::2] ** 2, atol=1e-12)
+
+
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(5)
+    one = np.full(64, 0x3F80, np.uint16)
+    h = S.to_bf16_bits(rng.standard_normal((6, 64)) * 3.0)
+    n = F.bf16_to_f32(L.rmsnorm_bf16(h, one, 0.0)).astype(np.float64)
+    # unit weight: every row has mean square 1, up to the bf16 rounding
+    assert np.allclose(np.mean(n * n, axis=1), 1.0, atol=2 * 2.0 ** -8)
+    # scale invariance (eps = 0): powers of two change nothing, bit for bit
+    h4 = F.bf16_bits_f64(F.bf16_to_f32(h).astype(np.float64) * 4.0)
+    assert np.array_equal(L.rmsnorm_bf16(h4, one, 0.0), L.rmsnorm_bf16(h, one, 0.0))
+    # a constant row c gives c / sqrt(c^2 + eps) * w
+    w = S.to_bf16_bits(rng.uniform(0.5, 1.5, 64))
+    c = F.bf16_bits_f64(np.full((1, 64), -0.375))
+    got = F.bf16_to_f32(L.rmsnorm_bf16(c, w, 1e-6)).astype(np.float64)
+    want = F.bf16_to_f32(F.bf16_bits_f64(-0.375 / np.sqrt(0.375 ** 2 + 1e-6) * F.bf16_to_f32(w))).astype(np.float64)
+    assert np.array_equal(got[0], want)
+
+
+def test_qkv_norm_rope_brute_force():
+    # per token, head and pair with scalar math on a tiny layer
+    import math
+    rng = np.random.default_rng(6)
+    M, K, H, D = 3, 128, 2, 8
+    x = S.activations(M, K, 1, rng)
+    lay = L.prepare_svdq_layer(S.weight(3 * H * D, K, 0.05, rng), np.full(K, 0x3F80, np.uint16), 16, "nvfp4",
+                               S.bias(3 * H * D, rng))
+    qw, kw = S.norm_weight(D, rng), S.norm_weight(D, rng)
+    cos, sin = S.rope_tables(M, D, offset=7)
+    eps = 1e-6
+    got = L.qkv_norm_rope_ref(x, lay, H, qw, kw, eps, cos, sin)
+    h64 = L.svdq_linear_ref(x, lay)
+    hb = F.bf16_to_f32(F.bf16_bits_f64(h64)).astype(np.float64)
+    f = lambda bits: float(F.bf16_to_f32(np.array([bits], np.uint16))[0])
+    rnd = lambda v: f(F.bf16_bits_f64(np.array([v]))[0])
+    for m in range(M):
+        for part, wb in ((0, qw), (1, kw)):
+            for hd in range(H):
+                c0 = (part * H + hd) * D
+                vals = [hb[m, c0 + d] for d in range(D)]
+                ms = sum(v * v for v in vals) / D
+                nv = [rnd(vals[d] / math.sqrt(ms + eps) * f(wb[d])) for d in range(D)]
+                for i in range(D // 2):
+                    a, b = nv[2 * i], nv[2 * i + 1]
+                    cs, sn = float(cos[m, i]), float(sin[m, i])
+                    assert math.isclose(got[m, c0 + 2 * i], a * cs - b * sn, rel_tol=0, abs_tol=1e-12)
+                    assert math.isclose(got[m, c0 + 2 * i + 1], a * sn + b * cs, rel_tol=0, abs_tol=1e-12)
+        assert np.array_equal(got[m, 2 * H * D:], h64[m, 2 * H * D:])
