@@ -26,7 +26,8 @@ STATUS = {0: "SVDQ_OK", -1: "SVDQ_EINVAL", -2: "SVDQ_EUNSUPPORTED", -3: "SVDQ_EA
 EXPORTS = ("svdq_w4a4_workspace_bytes", "svdq_w4a4_linear", "svdq_w4a4_quantize", "svdq_w4a4_gemm",
            "awq_w4a16_linear", "svdq_w4a4_mlp_workspace_bytes", "svdq_w4a4_mlp_gelu",
            "svdq_w4a4_quantize_act", "svdq_w4a4_gemm_partials", "svdq_w4a4_check",
-           "awq_w4a16_check", "svdq_w4a4_mlp_gelu_check", "svdq_last_error")
+           "awq_w4a16_check", "svdq_w4a4_mlp_gelu_check", "svdq_w4a4_qkv_rmsnorm_rope",
+           "svdq_w4a4_qkv_rmsnorm_rope_check", "svdq_last_error")
 
 
 class LayerStruct(ctypes.Structure):
@@ -84,6 +85,12 @@ def lib():
         L.svdq_w4a4_mlp_gelu.restype = I
         L.svdq_w4a4_mlp_gelu_check.argtypes = [P, I64, LP, LP, P, P, ctypes.c_size_t, ctypes.c_char_p]
         L.svdq_w4a4_mlp_gelu_check.restype = I
+        F = ctypes.c_float
+        L.svdq_w4a4_qkv_rmsnorm_rope.argtypes = [P, I64, LP, I, I, P, P, F, P, P, P, P, ctypes.c_size_t, P]
+        L.svdq_w4a4_qkv_rmsnorm_rope.restype = I
+        L.svdq_w4a4_qkv_rmsnorm_rope_check.argtypes = [P, I64, LP, I, I, P, P, F, P, P, P, P, ctypes.c_size_t,
+                                                       ctypes.c_char_p]
+        L.svdq_w4a4_qkv_rmsnorm_rope_check.restype = I
         L.svdq_last_error.argtypes = []
         L.svdq_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -229,6 +236,30 @@ def svdq_w4a4_mlp_gelu(x, up, down, out=None, workspace=None, stream=None):
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().svdq_w4a4_mlp_gelu(_ptr(x), M, ctypes.byref(u), ctypes.byref(d), _ptr(out), _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
+    return out
+
+
+def svdq_w4a4_qkv_rmsnorm_rope(x, qkv, heads, q_norm, k_norm, rope_cos, rope_sin, eps=1e-6, out=None,
+                               workspace=None, stream=None):
+    """Fused QKV projection: q | k | v = qkv(x) with per-head RMSNorm (weights
+    q_norm / k_norm, bf16 [128]) and RoPE (rope_cos / rope_sin, fp32 [M, 64],
+    interleaved pairs) applied to the q and k heads in the projection's
+    epilogue; returns bf16 [M, 3 heads 128]."""
+    x = _contig(x, torch.bfloat16, "x")
+    M = x.shape[0]
+    q = layer_struct(qkv)
+    q_norm = _contig(q_norm, torch.bfloat16, "q_norm")
+    k_norm = _contig(k_norm, torch.bfloat16, "k_norm")
+    rope_cos = _contig(rope_cos, torch.float32, "rope_cos")
+    rope_sin = _contig(rope_sin, torch.float32, "rope_sin")
+    head_dim = q_norm.numel()
+    if out is None:
+        out = torch.empty((M, qkv.N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(qkv.workspace_bytes(M), 1), dtype=torch.uint8, device=x.device)
+    _check(lib().svdq_w4a4_qkv_rmsnorm_rope(
+        _ptr(x), M, ctypes.byref(q), heads, head_dim, _ptr(q_norm), _ptr(k_norm), float(eps), _ptr(rope_cos),
+        _ptr(rope_sin), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -276,6 +276,49 @@ int validate_mlp(const void* x, int64_t M, const svdq_w4a4_layer* up, const svdq
   return SVDQ_OK;
 }
 
+// QKV fusion: heads of 128 columns (the epilogue's column order needs two
+// heads' v columns per head: 2 * (192 - 128) == 128)
+constexpr int kQkvHeadDim = 128;
+constexpr int kQkvMaxHeads = 256;
+
+int validate_qkv(const void* x, int64_t M, const svdq_w4a4_layer* qkv, int heads, int head_dim,
+                 const void* q_norm, const void* k_norm, float eps, const float* rope_cos,
+                 const float* rope_sin, const void* out, const void* workspace, size_t ws_bytes) {
+  int rc = validate_layer(M, qkv, "qkv");
+  if (rc) return rc;
+  if (head_dim != kQkvHeadDim) return fail(SVDQ_EUNSUPPORTED, "head_dim must be 128");
+  if (heads < 1 || heads > kQkvMaxHeads) return fail(SVDQ_EINVAL, "heads must be in [1, 256]");
+  if (qkv->N != int64_t(3) * heads * head_dim) return fail(SVDQ_EINVAL, "qkv->N must equal 3 * heads * head_dim");
+  if (!(std::isfinite(eps) && eps > 0.f)) return fail(SVDQ_EINVAL, "eps must be finite and positive");
+  if (!x || !out || !workspace || !q_norm || !k_norm || !rope_cos || !rope_sin)
+    return fail(SVDQ_EINVAL, "null pointer argument");
+  const void* ptrs[] = {x, out, workspace, q_norm, k_norm, rope_cos, rope_sin};
+  for (const void* p : ptrs)
+    if (!aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  const int64_t K = qkv->K, N = qkv->N;
+  const size_t need = workspace_bytes(M, K, qkv->precision, qkv->rank);
+  const size_t table = size_t(M) * size_t(head_dim / 2) * 4;
+  const Range o{out, size_t(M) * size_t(N) * 2};
+  const Range ins[] = {{x, size_t(M) * size_t(K) * 2},
+                       {workspace, need},
+                       {qkv->packed_w, size_t(N) * size_t(K / 2)},
+                       {qkv->wscales, w_scale_bytes(N, K, qkv->precision)},
+                       {qkv->smooth, size_t(K) * 2},
+                       {qkv->lora_down, size_t(qkv->rank) * size_t(K) * 2},
+                       {qkv->lora_up, size_t(N) * size_t(qkv->rank) * 2},
+                       {qkv->bias, size_t(N) * 2},
+                       {q_norm, size_t(head_dim) * 2},
+                       {k_norm, size_t(head_dim) * 2},
+                       {rope_cos, table},
+                       {rope_sin, table}};
+  for (const Range& r : ins)
+    if (overlaps(o, r)) return fail(SVDQ_EINVAL, "out overlaps an input or the workspace");
+  if (overlaps(Range{x, size_t(M) * size_t(K) * 2}, Range{workspace, need}))
+    return fail(SVDQ_EINVAL, "workspace overlaps x");
+  if (ws_bytes < need) return fail(SVDQ_EWORKSPACE, "workspace too small");
+  return SVDQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -483,6 +526,43 @@ int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up, cons
   // down layer: kernel 2 from its workspace
   return launch_gemm(ws_down, M, H, down->N, down->packed_w, down->wscales, down->wtscale, down->lora_up,
                      down->bias, SVDQ_NVFP4, down->rank, out, s);
+}
+
+int svdq_w4a4_qkv_rmsnorm_rope_check(const void* x, int64_t M, const svdq_w4a4_layer* qkv, int heads,
+                                     int head_dim, const void* q_norm, const void* k_norm, float eps,
+                                     const float* rope_cos, const float* rope_sin, const void* out,
+                                     const void* workspace, size_t ws_bytes, const char* arch) {
+  g_last_error.clear();
+  int rc = validate_qkv(x, M, qkv, heads, head_dim, q_norm, k_norm, eps, rope_cos, rope_sin, out, workspace,
+                        ws_bytes);
+  if (rc) return rc;
+  if (!arch_is_gfx950(arch)) return fail(SVDQ_EARCH, "device architecture is not gfx950");
+  return SVDQ_OK;
+}
+
+int svdq_w4a4_qkv_rmsnorm_rope(const void* x, int64_t M, const svdq_w4a4_layer* qkv, int heads, int head_dim,
+                               const void* q_norm, const void* k_norm, float eps, const float* rope_cos,
+                               const float* rope_sin, void* out, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  g_last_error.clear();
+  int rc = validate_qkv(x, M, qkv, heads, head_dim, q_norm, k_norm, eps, rope_cos, rope_sin, out, workspace,
+                        ws_bytes);
+  if (rc) return rc;
+  rc = check_device_arch();
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = launch_quantize(x, M, qkv->K, qkv->smooth, qkv->lora_down, qkv->precision, qkv->rank, workspace, s);
+  if (rc) return rc;
+  const Carve c = carve(workspace, M, qkv->K, qkv->precision);
+  svdq::GemmArgs ga{c.act_f16, c.row_scale, c.lora_act, qkv->packed_w, qkv->wscales, qkv->lora_up, qkv->bias,
+                    out, nullptr, qkv->wtscale, M, qkv->K, qkv->N, qkv->precision, qkv->rank};
+  ga.q_norm = q_norm;
+  ga.k_norm = k_norm;
+  ga.rope_cos = rope_cos;
+  ga.rope_sin = rope_sin;
+  ga.eps = eps;
+  ga.heads = heads;
+  return launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up (RMSNorm + RoPE epilogue) launch");
 }
 
 }  // extern "C"

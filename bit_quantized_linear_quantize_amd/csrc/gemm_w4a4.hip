@@ -71,6 +71,23 @@ static_assert(kAP % 4 == 0 && kWP == 3 && kThreads >= kBN && kADma * kThreads ==
 template <int I>
 using IC = std::integral_constant<int, I>;
 
+// Epilogues: plain bias + bf16 store; the MLP fusion (GELU and nvfp4
+// quantization for the next layer); the QKV fusion (RMSNorm and RoPE).
+constexpr int kEpiStore = 0;
+constexpr int kEpiGelu = 1;
+constexpr int kEpiQk = 2;
+
+// QKV fusion column order.  The output is q | k | v with heads of 128
+// columns; a 192-column tile cannot hold whole heads of q or k in the natural
+// order, so column tile t of the 2 H tiles takes the 128 columns of head t
+// of q | k and 64 columns of v (two tiles' v columns make one head), and
+// RMSNorm needs no data from another workgroup.
+constexpr int kHeadDim = 128;
+static_assert(2 * (kBN - kHeadDim) == kHeadDim, "the v columns of two tiles make one head");
+__device__ __forceinline__ int qk_col(int nt, int c, int qk_cols) {
+  return c < kHeadDim ? nt * kHeadDim + c : qk_cols + nt * (kBN - kHeadDim) + (c - kHeadDim);
+}
+
 // Workgroup barrier for the main loop: this wave's LDS reads and writes are
 // complete (lgkmcnt 0), and the compiler moves no memory access across it.
 // Unlike a release fence it does not wait for the wave's direct-to-LDS loads
@@ -290,7 +307,116 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
   }
 }
 
-template <int PREC, int RB, bool PARTIALS, bool GELUQ = false>
+// The QKV fusion epilogue of one wave ("Fused kernels" of the Nunchaku Lite
+// docs page: the Q, K and V projections merged with RMSNorm and RoPE).  acc
+// holds this wave's 64 x 96 block before the bias; tile columns 0..127 are
+// head nt of q | k (q for nt < heads), 128..191 v columns (qk_col).  Wave
+// column group wn = 0 holds head dims 0..95, wn = 1 head dims 96..127 and
+// the 64 v columns.  Steps:
+//  1. h = bf16(acc + bias) into the wave's LDS tile (rows of kGeluRow bytes);
+//  2. lane l takes tile row l: the sum of squares of its head columns; the
+//     two waves of a row block add theirs through LDS (`ssq`, in a fixed
+//     order) and r = 1 / sqrt(sum / 128 + eps);
+//  3. each head pair (2i, 2i+1): n = bf16(fl32(fl32(h r) w_d)), then
+//     (n_a cos - n_b sin, n_a sin + n_b cos) in fp32, rounded to bf16 in
+//     place; v columns keep h;
+//  4. the wave stores the tile with consecutive lanes on consecutive 16-byte
+//     pieces of a row.
+__device__ __forceinline__ void qk_norm_rope_epilogue(const GemmArgs& args, f32x16 (&acc)[kIB][kJB], int m0, int nt,
+                                                      int wave, int wm, int wn, int lane, int l32, int h,
+                                                      uint8_t* tile_base, float* ssq) {
+  const int M = (int)args.M, N = (int)args.N;
+  const int heads = args.heads;
+  const int qk_cols = 2 * heads * kHeadDim;
+  uint8_t* gt = tile_base + (wave & 1) * (64 * kGeluRow);
+  // every wave has left the main loop and every direct-to-LDS load has landed
+  // before the stage buffers are reused
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // 1. the bf16 projection
+  const uint16_t* bias = (const uint16_t*)args.bias;
+#pragma unroll
+  for (int j = 0; j < kJB; ++j) {
+    const int col = qk_col(nt, wn * (kJB * 32) + j * 32 + l32, qk_cols);
+    const float bv = bias ? bf16_bits_to_f32(bias[col]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < kIB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+        *(uint16_t*)(gt + r * kGeluRow + (j * 32 + l32) * 2) = (uint16_t)f32_to_bf16_bits(acc[i][j][e] + bv);
+      }
+  }
+  // (the wave's own LDS writes and reads execute in order)
+
+  // 2. RMSNorm factor of the lane's row
+  uint8_t* rowp = gt + lane * kGeluRow;
+  const int nhead = wn == 0 ? kJB * 32 : kHeadDim - kJB * 32;  // head columns of this wave (96 | 32)
+  float ss = 0.f;
+#pragma unroll
+  for (int t = 0; t < 12; ++t) {
+    if (8 * t < nhead) {
+      const u32x4 v = *(const u32x4*)(rowp + 16 * t);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float a = bf16_lo(v[p]), b = bf16_hi(v[p]);
+        ss = __fmaf_rn(a, a, ss);
+        ss = __fmaf_rn(b, b, ss);
+      }
+    }
+  }
+  const int trow = wm * 64 + lane;  // row of the workgroup tile
+  ssq[wn * kBM + trow] = ss;
+  lds_barrier();
+  const float tot = __fadd_rn(ssq[trow], ssq[kBM + trow]);
+  const float rr = __fdiv_rn(1.0f, __fsqrt_rn(__fmaf_rn(tot, 1.0f / kHeadDim, args.eps)));
+
+  // 3. normalize and rotate the head columns in place
+  const uint32_t* nw = (const uint32_t*)(nt < heads ? args.q_norm : args.k_norm);  // bf16 pairs
+  const int m = m0 + trow;
+  const size_t trow_off = (size_t)min(m, M - 1) * (kHeadDim / 2);
+  const float* cs = args.rope_cos + trow_off;
+  const float* sn = args.rope_sin + trow_off;
+  const int d0 = wn * (kJB * 32);  // head dim of the wave's first column
+#pragma unroll
+  for (int t = 0; t < 12; ++t) {
+    if (8 * t < nhead) {
+      const u32x4 v = *(const u32x4*)(rowp + 16 * t);
+      const int pr = (d0 + 8 * t) >> 1;  // first pair of the piece
+      const f32x4 c4 = *(const f32x4*)(cs + pr);
+      const f32x4 s4 = *(const f32x4*)(sn + pr);
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t wp = nw[pr + p];
+        const float na = __uint_as_float(f32_to_bf16_bits(__fmul_rn(__fmul_rn(bf16_lo(v[p]), rr), bf16_lo(wp))) << 16);
+        const float nb = __uint_as_float(f32_to_bf16_bits(__fmul_rn(__fmul_rn(bf16_hi(v[p]), rr), bf16_hi(wp))) << 16);
+        const float oa = __fsub_rn(__fmul_rn(na, c4[p]), __fmul_rn(nb, s4[p]));
+        const float ob = __fadd_rn(__fmul_rn(na, s4[p]), __fmul_rn(nb, c4[p]));
+        o[p] = bf16x2_rne(oa, ob);
+      }
+      *(u32x4*)(rowp + 16 * t) = o;
+    }
+  }
+
+  // 4. copy-out: 16-byte chunk c of the 64 x 192-byte tile, c = 64 i + lane,
+  // is row c / 12, bytes 16 (c % 12) of it; a piece never crosses a head edge
+  uint16_t* out = (uint16_t*)args.out;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    const int c = 64 * i + lane;
+    const int r = c / 12, k = c - 12 * r;
+    const u32x4 v = *(const u32x4*)(gt + r * kGeluRow + 16 * k);
+    const int mr = m0 + wm * 64 + r;
+    const int col = qk_col(nt, wn * (kJB * 32) + 8 * k, qk_cols);
+    if (mr < M) *(u32x4*)(out + (size_t)mr * N + col) = v;
+  }
+}
+
+template <int PREC, int RB, bool PARTIALS, int EPI = kEpiStore>
 __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs args) {
   // separate LDS objects, selected at compile time, so that the compiler can
   // tell the buffers apart from those that direct-to-LDS loads are filling
@@ -313,7 +439,14 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   tile_of(blockIdx.x, nmt, nnt, mt, nt);
   const int m0 = mt * kBM, n0 = nt * kBN;
   const int nstages = K / kBK;
-  if constexpr (GELUQ) {
+  // physical column of tile column c (the QKV fusion reorders columns)
+  constexpr bool kQk = EPI == kEpiQk;
+  const int qk_cols = kQk ? 2 * args.heads * kHeadDim : 0;
+  auto pcol = [&](int c) -> int {
+    if constexpr (kQk) return qk_col(nt, c, qk_cols);
+    else return n0 + c;
+  };
+  if constexpr (EPI == kEpiGelu) {
     // read before the first use by the main loop's barriers
     if (tid < kBN) {
       const int col = n0 + tid;
@@ -332,18 +465,22 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   const size_t a_row_bytes = PARTIALS ? (size_t)K2 : (size_t)K * 2;
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc((const uint8_t*)args.act + (size_t)m0 * a_row_bytes,
                                                 (size_t)(M - m0) * a_row_bytes);
-  const __amdgpu_buffer_rsrc_t w_rs = make_rsrc((const uint8_t*)args.w_codes + (size_t)n0 * K2,
-                                                (size_t)(N - n0) * K2);
+  // (the QKV fusion addresses W rows from the matrix start: its tile rows
+  // are not contiguous)
+  const int w_base = kQk ? 0 : n0;
+  const __amdgpu_buffer_rsrc_t w_rs = make_rsrc((const uint8_t*)args.w_codes + (size_t)w_base * K2,
+                                                (size_t)(N - w_base) * K2);
   const size_t ws_row_bytes = PREC == kInt4 ? (size_t)(K >> 6) * 2 : (size_t)(K >> 4);
-  const __amdgpu_buffer_rsrc_t ws_rs = make_rsrc((const uint8_t*)args.w_scales + (size_t)n0 * ws_row_bytes,
-                                                 PARTIALS ? 0 : (size_t)(N - n0) * ws_row_bytes);
+  const __amdgpu_buffer_rsrc_t ws_rs = make_rsrc((const uint8_t*)args.w_scales + (size_t)w_base * ws_row_bytes,
+                                                 PARTIALS ? 0 : (size_t)(N - w_base) * ws_row_bytes);
   // stages past the last read through an empty descriptor: all zeros
   const __amdgpu_buffer_rsrc_t zero_rs = make_rsrc(args.w_codes, 0);
   int w_off[kWP], ws_off[kWP], pa_off[kAP];
 #pragma unroll
   for (int j = 0; j < kWP; ++j) {
-    w_off[j] = (lr + kRP * j) * K2 + lc * 4;
-    ws_off[j] = (lr + kRP * j) * (int)ws_row_bytes + (PREC == kNvfp4 ? (lc >> 1) : 0);
+    const int wrow = kQk ? pcol(lr + kRP * j) : lr + kRP * j;  // row from the descriptor base
+    w_off[j] = wrow * K2 + lc * 4;
+    ws_off[j] = wrow * (int)ws_row_bytes + (PREC == kNvfp4 ? (lc >> 1) : 0);
   }
 #pragma unroll
   for (int i = 0; i < kAP; ++i) pa_off[i] = (lr + kRP * i) * K2 + lc * 4;
@@ -541,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   if constexpr (kRowExp) {
     if (tid < kBN) {
       // the row's scales, two per load (G64 is even: rows are 4-byte aligned)
-      const uint16_t* srow = (const uint16_t*)args.w_scales + (size_t)min(n0 + tid, N - 1) * G64;
+      const uint16_t* srow = (const uint16_t*)args.w_scales + (size_t)(kQk ? pcol(tid) : min(n0 + tid, N - 1)) * G64;
       float m = 0.f;
       for (int g0 = 0; g0 < G64; g0 += 16) {
         uint32_t v[8];
@@ -623,7 +760,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
         }
 #pragma unroll
         for (int j = 0; j < kJB; ++j) {
-          const int col = min(n0 + wn * (kJB * 32) + j * 32 + l32, N - 1);
+          const int tc = wn * (kJB * 32) + j * 32 + l32;
+          const int col = kQk ? pcol(tc) : min(n0 + tc, N - 1);
           bo[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(lu + (size_t)col * rank + rs16 * 16 + h * 8));
         }
 #pragma unroll
@@ -635,9 +773,12 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
           }
       }
     }
-    if constexpr (GELUQ) {
+    if constexpr (EPI == kEpiGelu) {
       gelu_quant_epilogue(args, acc, m0, n0, wave, wm, wn, lane, l32, h, nmu,
                           wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0);
+    } else if constexpr (kQk) {
+      qk_norm_rope_epilogue(args, acc, m0, nt, wave, wm, wn, lane, l32, h,
+                            wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, (float*)lds_w1);
     } else {
       // ---- bias + bf16 store ------------------------------------------------
       const uint16_t* bias = (const uint16_t*)args.bias;
@@ -658,16 +799,16 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   }
 }
 
-template <int PREC, bool PARTIALS, bool GELUQ>
+template <int PREC, bool PARTIALS, int EPI>
 static hipError_t dispatch_rank(const GemmArgs& a, hipStream_t s) {
   const unsigned tiles = (unsigned)(((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN));
   dim3 grid(tiles), block(kThreads);
   if constexpr (PARTIALS) {
-    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, 0, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, 0, true, kEpiStore>), grid, block, 0, s, a);
   } else {
 #define SVDQ_K2_CASE(rb)                                                                            \
   case rb:                                                                                          \
-    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, rb, false, GELUQ>), grid, block, 0, s, a); \
+    hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, rb, false, EPI>), grid, block, 0, s, a);   \
     break;
     switch (a.rank / 16) {
       SVDQ_K2_CASE(0)
@@ -688,13 +829,17 @@ static hipError_t dispatch_rank(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream) {
   const bool partials = a.partials != nullptr;
-  const bool geluq = a.next_act != nullptr;
+  const int epi = a.next_act != nullptr ? kEpiGelu : a.heads > 0 ? kEpiQk : kEpiStore;
   if (a.precision == kInt4) {
-    if (partials) return dispatch_rank<kInt4, true, false>(a, stream);
-    return geluq ? dispatch_rank<kInt4, false, true>(a, stream) : dispatch_rank<kInt4, false, false>(a, stream);
+    if (partials) return dispatch_rank<kInt4, true, kEpiStore>(a, stream);
+    if (epi == kEpiGelu) return dispatch_rank<kInt4, false, kEpiGelu>(a, stream);
+    if (epi == kEpiQk) return dispatch_rank<kInt4, false, kEpiQk>(a, stream);
+    return dispatch_rank<kInt4, false, kEpiStore>(a, stream);
   }
-  if (partials) return dispatch_rank<kNvfp4, true, false>(a, stream);
-  return geluq ? dispatch_rank<kNvfp4, false, true>(a, stream) : dispatch_rank<kNvfp4, false, false>(a, stream);
+  if (partials) return dispatch_rank<kNvfp4, true, kEpiStore>(a, stream);
+  if (epi == kEpiGelu) return dispatch_rank<kNvfp4, false, kEpiGelu>(a, stream);
+  if (epi == kEpiQk) return dispatch_rank<kNvfp4, false, kEpiQk>(a, stream);
+  return dispatch_rank<kNvfp4, false, kEpiStore>(a, stream);
 }
 
 }  // namespace svdq

@@ -44,11 +44,20 @@ struct GemmArgs {
   // MLP fusion (null next_act: plain store of out).  The epilogue applies
   // GELU to the bf16 output and quantizes it (nvfp4) for the next layer,
   // whose input channels are this layer's N columns; out is not written.
-  const void* next_smooth;     // bf16 [N]
-  const void* next_lora_down;  // bf16 [next_rank, N] or null
-  void* next_act;              // f16 [M, N]: the next layer's product operand e2m1 * dec(s8)
-  float* next_lora_act;        // f32 [M, next_rank], zero on entry, accumulated with atomics
-  int next_rank;
+  const void* next_smooth = nullptr;     // bf16 [N]
+  const void* next_lora_down = nullptr;  // bf16 [next_rank, N] or null
+  void* next_act = nullptr;              // f16 [M, N]: the next layer's product operand e2m1 * dec(s8)
+  float* next_lora_act = nullptr;        // f32 [M, next_rank], zero on entry, accumulated with atomics
+  int next_rank = 0;
+  // QKV fusion (heads > 0): N = 3 heads 128 columns q | k | v.  Column tile t
+  // of the 2 heads tiles computes head t of q | k and v columns 64 t ..
+  // 64 t + 63; the epilogue applies RMSNorm and RoPE to the head's columns.
+  const void* q_norm = nullptr;     // bf16 [128]
+  const void* k_norm = nullptr;     // bf16 [128]
+  const float* rope_cos = nullptr;  // f32 [M, 64]
+  const float* rope_sin = nullptr;  // f32 [M, 64]
+  float eps = 0.f;
+  int heads = 0;
 };
 
 struct AwqArgs {

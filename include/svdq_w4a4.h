@@ -175,6 +175,37 @@ int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up,
                        const svdq_w4a4_layer* down, void* out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Fused QKV projection with RMSNorm and RoPE, the fusion of the "Fused
+ * kernels" section of the Nunchaku Lite docs page (the Q, K and V
+ * projections merged with RMSNorm and RoPE): one svdq_w4a4 linear whose
+ * epilogue normalizes and rotates the q and k heads before they are stored.
+ *
+ *   h = svdq_w4a4_linear(qkv, x)  (bf16 [M, 3 heads 128]: q | k | v, heads of
+ *                                  128 consecutive columns)
+ *   for each token m and q or k head: n = bf16(h / sqrt(mean(h^2) + eps) * w)
+ *     with w = q_norm or k_norm; out pair (2i, 2i+1) =
+ *     bf16(n_2i cos[m,i] - n_2i+1 sin[m,i], n_2i sin[m,i] + n_2i+1 cos[m,i])
+ *   v columns: out = h.
+ * The GPU computes the norm and rotation in fp32 (the sum of squares in its
+ * own order), so a value can differ from an fp64 evaluation by one bf16 ulp.
+ *
+ * x       bf16 [M, qkv->K]
+ * qkv     an svdq_w4a4 layer with N = 3 * heads * head_dim
+ * heads   1..256; head_dim must be 128 (else SVDQ_EUNSUPPORTED)
+ * q_norm, k_norm  bf16 [head_dim] RMSNorm weights
+ * eps     finite, > 0
+ * rope_cos, rope_sin  fp32 [M, head_dim / 2]: the rotation of pair i at token m
+ * out     bf16 [M, N]; must not overlap x, the weights, the tables or the
+ *         workspace
+ * workspace  at least svdq_w4a4_workspace_bytes(M, K, N, precision,
+ *         group_size, rank) bytes (the linear's)
+ * Pointers 16-byte aligned; other rules as for svdq_w4a4_linear.
+ */
+int svdq_w4a4_qkv_rmsnorm_rope(const void* x, int64_t M, const svdq_w4a4_layer* qkv, int heads,
+                               int head_dim, const void* q_norm, const void* k_norm, float eps,
+                               const float* rope_cos, const float* rope_sin, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Parity export of the first svdq_w4a4 kernel (same kernel as the linear):
  * smoothing, activation quantization and the low-rank down projection.
  * codes_out  uint8 [M, K/2]; scales_out bf16 [M, K/64] (int4) or uint8 E4M3
@@ -209,6 +240,12 @@ int awq_w4a16_check(const void* x, int64_t M, int64_t K, int64_t N, const void* 
 int svdq_w4a4_mlp_gelu_check(const void* x, int64_t M, const svdq_w4a4_layer* up,
                              const svdq_w4a4_layer* down, const void* out,
                              const void* workspace, size_t workspace_bytes, const char* arch);
+int svdq_w4a4_qkv_rmsnorm_rope_check(const void* x, int64_t M, const svdq_w4a4_layer* qkv,
+                                     int heads, int head_dim, const void* q_norm,
+                                     const void* k_norm, float eps, const float* rope_cos,
+                                     const float* rope_sin, const void* out,
+                                     const void* workspace, size_t workspace_bytes,
+                                     const char* arch);
 
 /* Message for the last failure on the calling thread ("" if none). */
 const char* svdq_last_error(void);

@@ -228,3 +228,37 @@ def test_mlp_rules(L):
     assert call(down=_layer(0x2_0000_0000, H, N, rank=0)) == OK
     assert call(down=_layer(0x2_0000_0000, H, N, rank=24)) == EUNSUP
     assert call(arch=b"gfx942") == EARCH
+
+
+def test_qkv_rules(L):
+    M, K, H = 256, 512, 4
+    N = 3 * H * 128
+    x, out, ws = 0x3_0000_0000, 0x4_0000_0000, 0x5_0000_0000
+    qn, kn, cs, sn = 0x6_0000_0000, 0x6_0001_0000, 0x7_0000_0000, 0x8_0000_0000
+    qkv = _layer(0x1_0000_0000, K, N, precision=1)
+    B = ctypes.byref
+    need = L.svdq_w4a4_workspace_bytes(M, K, N, 1, 16, 32)
+
+    def call(x=x, M=M, qkv=qkv, heads=H, hd=128, qn=qn, kn=kn, eps=1e-6, cs=cs, sn=sn, out=out, ws=ws,
+             wsb=need, arch=GFX950):
+        p = lambda v: None if v is None else _fake(v)
+        return L.svdq_w4a4_qkv_rmsnorm_rope_check(p(x), M, B(qkv) if qkv is not None else None, heads, hd, p(qn),
+                                                  p(kn), eps, p(cs), p(sn), p(out), p(ws), wsb, arch)
+    assert call() == OK
+    assert call(qkv=_layer(0x1_0000_0000, K, N, precision=0), wsb=L.svdq_w4a4_workspace_bytes(M, K, N, 0, 64, 32)) == OK
+    assert call(hd=64) == EUNSUP                    # head_dim 128 only
+    assert call(heads=3) == EINVAL                  # N != 3 heads head_dim
+    assert call(heads=0) == EINVAL
+    big = 257
+    assert call(heads=big, qkv=_layer(0x1_0000_0000, K, 3 * big * 128)) == EINVAL
+    for e in (0.0, -1e-6, float("nan"), float("inf")):
+        assert call(eps=e) == EINVAL
+    assert call(qn=None) == EINVAL and call(kn=None) == EINVAL
+    assert call(cs=None) == EINVAL and call(sn=None) == EINVAL
+    assert call(cs=cs + 8) == EINVAL                # alignment
+    assert call(out=sn) == EINVAL                   # out overlaps a table
+    assert call(out=ws) == EINVAL                   # out overlaps the workspace
+    assert call(wsb=need - 1) == EWS
+    assert call(qkv=_layer(0x1_0000_0000, K, N, rank=24)) == EUNSUP
+    assert call(qkv=None) == EINVAL
+    assert call(arch=b"gfx942") == EARCH

@@ -430,3 +430,85 @@ def test_awq_no_bias_and_extreme_codes():
     lay = L.prepare_awq_layer(w, None)
     x = S.activations(4, K, 0, rng)
     assert_output(run_awq(x, lay), L.awq_linear_ref(x, lay), "awq extremes")
+
+
+# ------------------------------------------------------------------ QKV + RMSNorm + RoPE
+def bf16_ulp(v):
+    return 2.0 * L.bf16_half_ulp(v)
+
+
+def check_qkv(x, lay, heads, qn, kn, cos, sin, eps, label, rows=None):
+    """The fused QKV call against the oracle.  v: bit for bit the plain
+    linear's output, and the r14 bar.  q | k pass through two bf16 roundings
+    (n = bf16(RMSNorm(h)), then the rotation's); the GPU's fp32 chain and the
+    oracle's fp64 one can round n differently, and h itself can differ in its
+    last place, so each output may also differ by two ulps of each n it
+    combines: |err| <= half-ulp(out) + 2 (ulp(n_a) |c| + ulp(n_b) |s|) +
+    1e-2 RMS, with MRE <= 2e-3."""
+    layer = bq.SVDQLinear.from_numpy(lay)
+    xd = dev_bf16(x)
+    y = bq.svdq_w4a4_qkv_rmsnorm_rope(xd, layer, heads, dev_bf16(qn), dev_bf16(kn),
+                                      torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda(), eps)
+    plain = layer(xd)
+    torch.cuda.synchronize()
+    rows = np.arange(x.shape[0]) if rows is None else rows
+    ref = L.qkv_norm_rope_ref(x[rows], lay, heads, qn, kn, eps, cos[rows], sin[rows])
+    qk = 2 * heads * 128
+    yb = host_bits(y)[rows]
+    assert np.array_equal(yb[:, qk:], host_bits(plain)[rows][:, qk:]), label
+    assert_output(torch.from_numpy(yb[:, qk:].view(np.int16).copy()).view(torch.bfloat16), ref[:, qk:], label + " v")
+    # q | k with the allowance for the intermediate rounding
+    R = len(rows)
+    h = F.bf16_bits_f64(L.svdq_linear_ref(x[rows], lay))[:, :qk].reshape(R, 2, heads, 128)
+    n = np.stack([F.bf16_to_f32(L.rmsnorm_bf16(h[:, p], w, eps)).astype(np.float64) for p, w in ((0, qn), (1, kn))],
+                 axis=1)
+    c, s_ = np.abs(cos[rows])[:, None, None, :], np.abs(sin[rows])[:, None, None, :]
+    ua, ub = bf16_ulp(n[..., 0::2]), bf16_ulp(n[..., 1::2])
+    allow = np.empty_like(n)
+    allow[..., 0::2] = 2 * (ua * c + ub * s_)
+    allow[..., 1::2] = 2 * (ua * s_ + ub * c)
+    allow = allow.reshape(R, qk)
+    got = F.bf16_to_f32(yb[:, :qk]).astype(np.float64)
+    want = ref[:, :qk]
+    err = np.abs(got - want)
+    rms = np.sqrt(np.mean(want ** 2))
+    excess = np.max(err - L.bf16_half_ulp(want) - allow) / rms
+    mre = err.sum() / np.abs(want).sum()
+    print(f"[{label} q|k] max|err|/RMS={err.max() / rms:.3e} (beyond the allowance {excess:.3e}) MRE={mre:.3e} "
+          f"elements beyond half-ulp + 1e-2 RMS: {int(np.sum(err - L.bf16_half_ulp(want) > 1e-2 * rms))}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert excess <= 1e-2 and mre <= 2e-3, label
+
+
+@pytest.mark.parametrize("M,heads,precision,rank", [(1, 1, "nvfp4", 32), (37, 2, "int4", 16), (300, 3, "nvfp4", 0),
+                                                    (257, 2, "int4", 32), (300, 1, "nvfp4", 128)])
+def test_qkv_rmsnorm_rope_ragged(M, heads, precision, rank):
+    # M ragged against the 256-row tiles; 2 heads column tiles per call
+    rng = np.random.default_rng(M * 7 + heads)
+    K, N = 256, 3 * heads * 128
+    x = S.activations(M, K, 3, rng)
+    lay = prepared(x, S.weight(N, K, 0.05, rng, spike_rank=2), S.bias(N, rng), precision, rank, smooth="calibrated")
+    qn, kn = S.norm_weight(128, rng), S.norm_weight(128, rng)
+    cos, sin = S.rope_tables(M, 128, offset=M)
+    check_qkv(x, lay, heads, qn, kn, cos, sin, 1e-6, f"qkv M={M} H={heads} {precision} r{rank}")
+
+
+def test_qkv_rmsnorm_rope_dit_sampled():
+    # the DiT attention projection: 4096 tokens, 24 heads of 128 (3072 -> 9216), nvfp4 rank 32
+    x, w, b = S.svdq_problem(4096, 3072, 9216, seed=5, n_outliers=31)
+    lay = prepared(x, w, b, "nvfp4", 32, smooth="calibrated")
+    rng = np.random.default_rng(24)
+    qn, kn = S.norm_weight(128, rng), S.norm_weight(128, rng)
+    cos, sin = S.rope_tables(4096, 128)
+    check_qkv(x, lay, 24, qn, kn, cos, sin, 1e-6, "qkv dit 3072->9216", rows=SAMPLE_ROWS)
+
+
+def test_qkv_rejects_head_dim():
+    rng = np.random.default_rng(1)
+    x = S.activations(8, 256, 0, rng)
+    lay = bq.SVDQLinear.from_numpy(prepared(x, S.weight(384, 256, 0.05, rng), None, "nvfp4", 16))
+    cos, sin = (torch.from_numpy(t).cuda() for t in S.rope_tables(8, 64))
+    q = dev_bf16(S.norm_weight(64, rng))
+    with pytest.raises(bq.SvdqError) as e:
+        bq.svdq_w4a4_qkv_rmsnorm_rope(dev_bf16(x), lay, 2, q, q, cos, sin)
+    assert e.value.status == -2
