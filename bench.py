@@ -19,10 +19,15 @@ Also measured in the same run (reported under "extra"):
     bf16 up output, a torch op, between the two library calls), and the same
     pair fused (svdq_w4a4_mlp_gelu: GELU and the down projection's
     quantization in the up projection's epilogue);
+  * the attention QKV projection 3072 -> 9216 (24 heads of 128, nvfp4) with
+    per-head RMSNorm and RoPE on q and k, as the linear plus torch ops and
+    fused (svdq_w4a4_qkv_rmsnorm_rope);
   * the DiT stack per pass: 24 blocks of QKV 3072->9216, out 3072->3072, MLP
     up/GELU/down (svdq nvfp4, rank 32, 4096 tokens) and the adaLN modulation
     linear 3072->18432 (awq_w4a16, one token; its 24 launches per pass are
-    timed from a replayed graph), 8 passes (--no-stack skips it).
+    timed from a replayed graph), 8 passes (--no-stack skips it); also with
+    the per-head RMSNorm and RoPE of q and k as torch ops, and with the QKV
+    and MLP fusions.
 The weights of the timed legs are random but valid packed layers (prepared
 weight values do not change the work); parity with the oracle is the job of
 tests/.  The cpu_baseline leg times the CPU oracle on the same inputs.
@@ -114,6 +119,59 @@ def bench_mlp_pair(bq, S, torch, np, x, M, K, rank, stream, hidden=12288, reps=5
             "fused_speedup": round(t_pair / t_fused, 3)}
 
 
+def torch_norm_rope(y, heads, qn, kn, cos, sin, eps=1e-6):
+    """The unfused form of the QKV epilogue as separate torch ops on the bf16
+    projection (per-head RMSNorm in fp32 with a bf16 weight, then RoPE on
+    interleaved pairs in fp32), as a bf16 DiT attention block runs them."""
+    import torch
+    M = y.shape[0]
+    q, k, v = y.view(M, 3, heads, 128).unbind(1)
+
+    def norm(t, w):
+        tf = t.float()
+        tf = tf * torch.rsqrt(tf.pow(2).mean(-1, keepdim=True) + eps)
+        return tf.to(torch.bfloat16) * w
+
+    def rope(t):
+        tf = t.float().view(M, heads, 64, 2)
+        a, b = tf[..., 0], tf[..., 1]
+        c, s = cos[:, None, :], sin[:, None, :]
+        return torch.stack((a * c - b * s, a * s + b * c), -1).view(M, heads, 128).to(torch.bfloat16)
+    return rope(norm(q, qn)), rope(norm(k, kn)), v
+
+
+def bench_qkv(bq, S, torch, np, M, K, rank, stream, heads=24, reps=50):
+    """The DiT attention projection 3072 -> 9216 (24 heads of 128, nvfp4, rank
+    32) with per-head RMSNorm and RoPE on q and k: the linear followed by the
+    torch ops, against svdq_w4a4_qkv_rmsnorm_rope (the same in the linear's
+    epilogue)."""
+    log("timing the fused QKV projection ...")
+    N = 3 * heads * 128
+    rl, rx, rn = S.streams(17, 3)
+    layer = bq.SVDQLinear.from_numpy(S.random_svdq_layer(N, K, "nvfp4", rank, rl))
+    x = torch.from_numpy(S.activations(M, K, round(0.01 * K), rx).view(np.int16).copy()).view(torch.bfloat16).cuda()
+    qn, kn = (torch.from_numpy(S.norm_weight(128, rn).view(np.int16).copy()).view(torch.bfloat16).cuda()
+              for _ in range(2))
+    cos, sin = (torch.from_numpy(t).cuda() for t in S.rope_tables(M, 128))
+    ws = torch.empty(layer.workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    yf = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    keep = [None]
+    f_lin = lambda: layer(x, out=y, workspace=ws)
+    f_ops = lambda: keep.__setitem__(0, torch_norm_rope(y, heads, qn, kn, cos, sin))
+    f_unfused = lambda: (f_lin(), f_ops())
+    f_fused = lambda: bq.svdq_w4a4_qkv_rmsnorm_rope(x, layer, heads, qn, kn, cos, sin, out=yf, workspace=ws)
+    for _ in range(10):
+        f_unfused()
+        f_fused()
+    t_lin, t_ops, t_unf, t_fus = (time_events(f, reps, stream) for f in (f_lin, f_ops, f_unfused, f_fused))
+    ops = 2.0 * M * N * K
+    return {"linear_us": round(t_lin * 1e3, 2), "torch_norm_rope_us": round(t_ops * 1e3, 2),
+            "unfused_us": round(t_unf * 1e3, 2), "fused_us": round(t_fus * 1e3, 2),
+            "fused_TOPS": round(ops / (t_fus * 1e-3) / 1e12, 1),
+            "epilogue_cost_us": round((t_fus - t_lin) * 1e3, 2), "fused_speedup": round(t_unf / t_fus, 3)}
+
+
 def bench_stack(bq, S, torch, np, M, rank, stream):
     """DiT stack per pass: every block runs QKV, out, MLP up, GELU, MLP down (svdq
     nvfp4, rank 32, M tokens, each linear on its own pre-generated activation,
@@ -166,9 +224,42 @@ def bench_stack(bq, S, torch, np, M, rank, stream):
             layers["up"][b](xu, out=outs["up"], workspace=ws[k_of["up"]])
             g[0] = Fn.gelu(outs["up"])
             layers["down"][b](g[0], out=outs["down"], workspace=ws[k_of["down"]])
+
+    # the same blocks with the attention's per-head RMSNorm and RoPE on q and k:
+    # as torch ops after the QKV linear, and with both fusions
+    heads = hid // 128
+    rq = rs[len(shapes) + 5]
+    qn, kn = (torch.from_numpy(S.norm_weight(128, rq).view(np.int16).copy()).view(torch.bfloat16).cuda()
+              for _ in range(2))
+    cos, sin = (torch.from_numpy(t).cuda() for t in S.rope_tables(M, 128))
+    ws_mlp = torch.empty(bq.mlp_workspace_bytes(M, layers["up"][0], layers["down"][0]), dtype=torch.uint8,
+                         device="cuda")
+    keep = [None]
+
+    def unfused_pass():
+        for b in range(blocks):
+            ada[b](xa, out=oa)
+            layers["qkv"][b](xq, out=outs["qkv"], workspace=ws[k_of["qkv"]])
+            keep[0] = torch_norm_rope(outs["qkv"], heads, qn, kn, cos, sin)
+            layers["out"][b](xo, out=outs["out"], workspace=ws[k_of["out"]])
+            layers["up"][b](xu, out=outs["up"], workspace=ws[k_of["up"]])
+            g[0] = Fn.gelu(outs["up"])
+            layers["down"][b](g[0], out=outs["down"], workspace=ws[k_of["down"]])
+
+    def fused_pass():
+        for b in range(blocks):
+            ada[b](xa, out=oa)
+            bq.svdq_w4a4_qkv_rmsnorm_rope(xq, layers["qkv"][b], heads, qn, kn, cos, sin, out=outs["qkv"],
+                                          workspace=ws[k_of["qkv"]])
+            layers["out"][b](xo, out=outs["out"], workspace=ws[k_of["out"]])
+            bq.svdq_w4a4_mlp_gelu(xu, layers["up"][b], layers["down"][b], out=outs["down"], workspace=ws_mlp)
     full_pass()
+    unfused_pass()
+    fused_pass()
     t_full = time_events(full_pass, passes, stream)
     t_svdq = time_events(svdq_pass, passes, stream)
+    t_unf = time_events(unfused_pass, passes, stream)
+    t_fus = time_events(fused_pass, passes, stream)
     t_awq = time_graph(awq_pass, passes, stream)
     if t_awq is None:
         t_awq = time_events(awq_pass, passes, stream)
@@ -178,6 +269,8 @@ def bench_stack(bq, S, torch, np, M, rank, stream):
             "svdq_and_gelu_pass_ms": round(t_svdq, 3), "awq_pass_ms": round(t_awq, 3),
             "svdq_TOPS_incl_gelu": round(svdq_ops / (t_svdq * 1e-3) / 1e12, 1),
             "awq_GBps": round(awq_bytes / (t_awq * 1e-3) / 1e9, 1),
+            "with_norm_rope_pass_ms": round(t_unf, 3), "fused_pass_ms": round(t_fus, 3),
+            "fused_speedup": round(t_unf / t_fus, 3),
             "svdq_ops_per_pass": svdq_ops, "awq_bytes_per_pass": awq_bytes}
 
 
@@ -447,6 +540,7 @@ def main():
             roofline["measured_instruction_peak"] = peak["measured_TFLOPs"]
             roofline["frac_of_measured_peak"] = round(k2_tops / peak["measured_TFLOPs"], 4)
         extra["mlp_pair_nvfp4_3072_12288_3072"] = bench_mlp_pair(bq, S, torch, np, x, M, K, rank, stream)
+        extra["qkv_rmsnorm_rope_nvfp4_3072_9216"] = bench_qkv(bq, S, torch, np, M, K, rank, stream)
         torch.cuda.empty_cache()
         if not args.no_stack:
             extra["dit_stack_nvfp4"] = bench_stack(bq, S, torch, np, M, rank, stream)
