@@ -22,6 +22,7 @@ Also measured in the same run (reported under "extra"):
   * the attention QKV projection 3072 -> 9216 (24 heads of 128, nvfp4) with
     per-head RMSNorm and RoPE on q and k, as the linear plus torch ops and
     fused (svdq_w4a4_qkv_rmsnorm_rope);
+  * offline weight preparation of a 9216 x 3072 nvfp4 layer on the GPU;
   * the DiT stack per pass: 24 blocks of QKV 3072->9216, out 3072->3072, MLP
     up/GELU/down (svdq nvfp4, rank 32, 4096 tokens) and the adaLN modulation
     linear 3072->18432 (awq_w4a16, one token; its 24 launches per pass are
@@ -170,6 +171,30 @@ def bench_qkv(bq, S, torch, np, M, K, rank, stream, heads=24, reps=50):
             "unfused_us": round(t_unf * 1e3, 2), "fused_us": round(t_fus * 1e3, 2),
             "fused_TOPS": round(ops / (t_fus * 1e-3) / 1e12, 1),
             "epilogue_cost_us": round((t_fus - t_lin) * 1e3, 2), "fused_speedup": round(t_unf / t_fus, 3)}
+
+
+def bench_weight_prep(bq, S, torch, np, stream, N=9216, K=3072, M=4096, rank=32, reps=20):
+    """Offline preparation of the QKV-shaped nvfp4 layer on the GPU: the
+    smoothing factors and the residual packing (this library's kernels), and
+    the whole prepare_layer call (with torch's randomized SVD)."""
+    import time as _t
+    log("timing the GPU weight preparation ...")
+    rx, rw = S.streams(19, 2)
+    x = torch.from_numpy(S.activations(M, K, round(0.01 * K), rx).view(np.int16).copy()).view(torch.bfloat16).cuda()
+    w = torch.from_numpy(S.weight(N, K, 0.02, rw, spike_rank=8).astype(np.float32)).cuda()
+    ws = torch.empty(bq.lib().svdq_w4a4_prep_workspace_bytes(K), dtype=torch.uint8, device="cuda")
+    t_smooth = time_events(lambda: bq.smooth_factors(x, w, workspace=ws), reps, stream)
+    t_pack = time_events(lambda: bq.pack_weight(w, "nvfp4", workspace=ws), reps, stream)
+    bq.prepare_layer(w, x, rank, "nvfp4")
+    torch.cuda.synchronize()
+    t0 = _t.perf_counter()
+    for _ in range(3):
+        bq.prepare_layer(w, x, rank, "nvfp4")
+    torch.cuda.synchronize()
+    t_prep = (_t.perf_counter() - t0) / 3
+    return {"shape": f"{N}x{K} nvfp4 rank {rank}, {M} calibration tokens",
+            "smooth_factors_us": round(t_smooth * 1e3, 2), "pack_weight_us": round(t_pack * 1e3, 2),
+            "prepare_layer_ms": round(t_prep * 1e3, 2)}
 
 
 def bench_stack(bq, S, torch, np, M, rank, stream):
@@ -541,6 +566,7 @@ def main():
             roofline["frac_of_measured_peak"] = round(k2_tops / peak["measured_TFLOPs"], 4)
         extra["mlp_pair_nvfp4_3072_12288_3072"] = bench_mlp_pair(bq, S, torch, np, x, M, K, rank, stream)
         extra["qkv_rmsnorm_rope_nvfp4_3072_9216"] = bench_qkv(bq, S, torch, np, M, K, rank, stream)
+        extra["weight_prep"] = bench_weight_prep(bq, S, torch, np, stream)
         torch.cuda.empty_cache()
         if not args.no_stack:
             extra["dit_stack_nvfp4"] = bench_stack(bq, S, torch, np, M, rank, stream)

@@ -27,7 +27,8 @@ EXPORTS = ("svdq_w4a4_workspace_bytes", "svdq_w4a4_linear", "svdq_w4a4_quantize"
            "awq_w4a16_linear", "svdq_w4a4_mlp_workspace_bytes", "svdq_w4a4_mlp_gelu",
            "svdq_w4a4_quantize_act", "svdq_w4a4_gemm_partials", "svdq_w4a4_check",
            "awq_w4a16_check", "svdq_w4a4_mlp_gelu_check", "svdq_w4a4_qkv_rmsnorm_rope",
-           "svdq_w4a4_qkv_rmsnorm_rope_check", "svdq_last_error")
+           "svdq_w4a4_qkv_rmsnorm_rope_check", "svdq_w4a4_prep_workspace_bytes", "svdq_w4a4_smooth_factors",
+           "svdq_w4a4_pack_weight", "svdq_last_error")
 
 
 class LayerStruct(ctypes.Structure):
@@ -91,6 +92,12 @@ def lib():
         L.svdq_w4a4_qkv_rmsnorm_rope_check.argtypes = [P, I64, LP, I, I, P, P, F, P, P, P, P, ctypes.c_size_t,
                                                        ctypes.c_char_p]
         L.svdq_w4a4_qkv_rmsnorm_rope_check.restype = I
+        L.svdq_w4a4_prep_workspace_bytes.argtypes = [I64]
+        L.svdq_w4a4_prep_workspace_bytes.restype = ctypes.c_size_t
+        L.svdq_w4a4_smooth_factors.argtypes = [P, I64, P, I64, I64, P, P, ctypes.c_size_t, P]
+        L.svdq_w4a4_smooth_factors.restype = I
+        L.svdq_w4a4_pack_weight.argtypes = [P, I64, I64, I, I, P, P, P, P, ctypes.c_size_t, P]
+        L.svdq_w4a4_pack_weight.restype = I
         L.svdq_last_error.argtypes = []
         L.svdq_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -261,6 +268,62 @@ def svdq_w4a4_qkv_rmsnorm_rope(x, qkv, heads, q_norm, k_norm, rope_cos, rope_sin
         _ptr(x), M, ctypes.byref(q), heads, head_dim, _ptr(q_norm), _ptr(k_norm), float(eps), _ptr(rope_cos),
         _ptr(rope_sin), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+# ---- offline weight preparation on the GPU -----------------------------------------
+def _prep_ws(K, workspace, device):
+    if workspace is None:
+        workspace = torch.empty(max(lib().svdq_w4a4_prep_workspace_bytes(K), 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def smooth_factors(x_calib, w, workspace=None, stream=None):
+    """bf16 [K] smoothing factors sqrt(max|x| / max|w|) per input channel of a
+    weight w (fp32 [N, K]) from calibration activations x_calib (bf16 [M, K])."""
+    x_calib = _contig(x_calib, torch.bfloat16, "x_calib")
+    w = _contig(w, torch.float32, "w")
+    (M, K), N = x_calib.shape, w.shape[0]
+    out = torch.empty(K, dtype=torch.bfloat16, device=w.device)
+    workspace = _prep_ws(K, workspace, w.device)
+    _check(lib().svdq_w4a4_smooth_factors(_ptr(x_calib), M, _ptr(w), N, K, _ptr(out), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)))
+    return out
+
+
+def pack_weight(resid, precision, workspace=None, stream=None):
+    """Quantize and pack a residual weight (fp32 [N, K]): returns (packed_w
+    uint8 [N, K/2], wscales, wtscale as a 1-element fp32 device tensor)."""
+    resid = _contig(resid, torch.float32, "resid")
+    N, K = resid.shape
+    G = GROUP_SIZE[precision]
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=resid.device)
+    wscales = torch.empty((N, K // G), dtype=torch.bfloat16 if precision == "int4" else torch.uint8,
+                          device=resid.device)
+    wt = torch.empty(4, dtype=torch.float32, device=resid.device)
+    workspace = _prep_ws(K, workspace, resid.device)
+    _check(lib().svdq_w4a4_pack_weight(_ptr(resid), N, K, PRECISIONS[precision], G, _ptr(packed), _ptr(wscales),
+                                       _ptr(wt), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return packed, wscales, wt[:1]
+
+
+def prepare_layer(w, x_calib, rank, precision, bias=None, niter=6, oversample=16):
+    """A ready SVDQLinear from a weight (fp32 [N, K] CUDA tensor) and
+    calibration activations, prepared on the GPU: smoothing factors and the
+    residual's quantization and packing by this library's kernels; the rank-r
+    split of the smoothed weight by torch's randomized SVD (fp64), its factors
+    rounded to bf16, the residual formed in fp64.  Offline: it synchronizes
+    once to read the nvfp4 tensor scale."""
+    smooth = smooth_factors(x_calib, w)
+    w_hat = w.double() * smooth.double()[None, :]
+    down = up = None
+    resid = w_hat
+    if rank:
+        U, S_, V = torch.svd_lowrank(w_hat, q=min(rank + oversample, min(w_hat.shape)), niter=niter)
+        down = (S_[:rank, None] * V[:, :rank].T).to(torch.bfloat16).contiguous()
+        up = U[:, :rank].to(torch.bfloat16).contiguous()
+        resid = w_hat - up.double() @ down.double()
+    packed, wscales, wt = pack_weight(resid.float().contiguous(), precision)
+    return SVDQLinear(packed, wscales, smooth, down, up, bias, precision, float(wt.item()))
 
 
 class AWQLinear:

@@ -39,6 +39,7 @@ int fail(int code, const std::string& msg) {
 
 constexpr int64_t kMaxM = int64_t(1) << 24;
 constexpr int64_t kMaxK = 16384;
+constexpr int64_t kMaxPrepRows = int64_t(1) << 22;  // calibration rows and weight rows of the smoothing call
 constexpr size_t kAlign = 16;
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
@@ -563,6 +564,66 @@ int svdq_w4a4_qkv_rmsnorm_rope(const void* x, int64_t M, const svdq_w4a4_layer* 
   ga.eps = eps;
   ga.heads = heads;
   return launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up (RMSNorm + RoPE epilogue) launch");
+}
+
+// ---- offline weight preparation ------------------------------------------------
+size_t svdq_w4a4_prep_workspace_bytes(int64_t K) {
+  if (K < 1 || K > kMaxK) return 0;
+  return round_up(size_t(K) * 8);
+}
+
+int svdq_w4a4_smooth_factors(const void* x_calib, int64_t M, const float* w, int64_t N, int64_t K,
+                             void* smooth_out, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (M < 1 || M > kMaxPrepRows || N < 1 || N > kMaxPrepRows)
+    return fail(SVDQ_EINVAL, "M and N must be in [1, 2^22]");
+  if (K < 128 || K > kMaxK || K % 128) return fail(SVDQ_EINVAL, "K must be a multiple of 128 in [128, 16384]");
+  if (!x_calib || !w || !smooth_out || !workspace) return fail(SVDQ_EINVAL, "null pointer argument");
+  const void* ptrs[] = {x_calib, w, smooth_out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  const size_t need = svdq_w4a4_prep_workspace_bytes(K);
+  const Range o{smooth_out, size_t(K) * 2};
+  const Range ins[] = {{x_calib, size_t(M) * size_t(K) * 2}, {w, size_t(N) * size_t(K) * 4}, {workspace, need}};
+  for (const Range& r : ins)
+    if (overlaps(o, r)) return fail(SVDQ_EINVAL, "smooth_out overlaps an input or the workspace");
+  if (ws_bytes < need) return fail(SVDQ_EWORKSPACE, "workspace too small");
+  int rc = check_device_arch();
+  if (rc) return rc;
+  svdq::SmoothArgs a{x_calib, w, smooth_out, static_cast<uint32_t*>(workspace), M, N, K};
+  return launch_status(svdq::launch_smooth_factors(a, static_cast<hipStream_t>(stream)), "smooth factors launch");
+}
+
+int svdq_w4a4_pack_weight(const float* resid, int64_t N, int64_t K, int precision, int group_size,
+                          void* packed_w_out, void* wscales_out, float* wtscale_out, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_svdq_kind(precision, group_size, 0);
+  if (rc) return rc;
+  if (N < 1 || N > (int64_t(1) << 24)) return fail(SVDQ_EINVAL, "N must be in [1, 2^24]");
+  if (K < 128 || K > kMaxK || K % 128) return fail(SVDQ_EINVAL, "K must be a multiple of 128 in [128, 16384]");
+  if (!resid || !packed_w_out || !wscales_out || !workspace) return fail(SVDQ_EINVAL, "null pointer argument");
+  if (precision == SVDQ_NVFP4 && !wtscale_out) return fail(SVDQ_EINVAL, "nvfp4 needs wtscale_out");
+  const void* ptrs[] = {resid, packed_w_out, wscales_out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(wtscale_out) % 4) return fail(SVDQ_EINVAL, "wtscale_out must be 4-byte aligned");
+  const size_t need = svdq_w4a4_prep_workspace_bytes(K);
+  const Range outs[] = {{packed_w_out, size_t(N) * size_t(K / 2)},
+                        {wscales_out, w_scale_bytes(N, K, precision)},
+                        {wtscale_out, 4}};
+  const Range ins[] = {{resid, size_t(N) * size_t(K) * 4}, {workspace, need}};
+  for (const Range& o : outs)
+    for (const Range& r : ins)
+      if (overlaps(o, r)) return fail(SVDQ_EINVAL, "an output overlaps the residual or the workspace");
+  if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2]))
+    return fail(SVDQ_EINVAL, "outputs overlap");
+  if (ws_bytes < need) return fail(SVDQ_EWORKSPACE, "workspace too small");
+  rc = check_device_arch();
+  if (rc) return rc;
+  svdq::PackArgs a{resid, packed_w_out, wscales_out, wtscale_out, static_cast<uint32_t*>(workspace), N, K,
+                   precision};
+  return launch_status(svdq::launch_pack_weight(a, static_cast<hipStream_t>(stream)), "pack weight launch");
 }
 
 }  // extern "C"

@@ -70,6 +70,27 @@ struct AwqArgs {
   int64_t M, K, N;
 };
 
+// Offline weight preparation (weight_prep.hip).
+struct SmoothArgs {
+  const void* x;   // bf16 [M, K] calibration activations
+  const float* w;  // f32 [N, K] weight
+  void* smooth;    // out: bf16 [K]
+  uint32_t* amax;  // scratch: u32 [2 K]
+  int64_t M, N, K;
+};
+
+struct PackArgs {
+  const float* resid;  // f32 [N, K] residual weight
+  void* packed;        // out: u8 [N, K/2]
+  void* scales;        // out: bf16 [N, K/64] | u8 [N, K/16]
+  float* wtscale;      // out: f32 [1] (1 for int4); may be null
+  uint32_t* amax;      // scratch: u32 [1]
+  int64_t N, K;
+  int precision;
+};
+
+hipError_t launch_smooth_factors(const SmoothArgs& a, hipStream_t stream);
+hipError_t launch_pack_weight(const PackArgs& a, hipStream_t stream);
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream);
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream);

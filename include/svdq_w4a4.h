@@ -206,6 +206,43 @@ int svdq_w4a4_qkv_rmsnorm_rope(const void* x, int64_t M, const svdq_w4a4_layer* 
                                const float* rope_cos, const float* rope_sin, void* out,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Offline weight preparation on the GPU (what the diffuse-compressor tool the
+ * Nunchaku Lite pages name under "Resources" does before a checkpoint is
+ * saved), bit-identical to the CPU reference packer.  The low-rank split (an
+ * SVD of smooth-scaled W) is not part of it: the caller computes the
+ * residual R = W * smooth - lora_up lora_down between the two calls.
+ *
+ * Scratch for both calls: svdq_w4a4_prep_workspace_bytes(K) bytes (0 for an
+ * invalid K). */
+size_t svdq_w4a4_prep_workspace_bytes(int64_t K);
+
+/* Per-channel smoothing factors for svdq_w4a4 weights:
+ *   smooth[k] = bf16_rne(sqrt(max_m |x[m, k]| / max_n |w[n, k]|))
+ * with the ratio and the root in fp64 and one rounding to bf16; 1 where the
+ * result is not finite or not positive (a zero column of x or of w).
+ * x_calib  bf16 [M, K] calibration activations, 1 <= M <= 2^22
+ * w        fp32 [N, K] weight, 1 <= N <= 2^22; K as for svdq_w4a4_linear
+ * smooth_out  bf16 [K]
+ * Pointers 16-byte aligned; the output may not overlap an input. */
+int svdq_w4a4_smooth_factors(const void* x_calib, int64_t M, const float* w, int64_t N, int64_t K,
+                             void* smooth_out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Quantize and pack a residual weight R (fp32 [N, K]) for svdq_w4a4_linear:
+ *   int4 (group 64):  s = bf16(fl32(amax / 7)), q = rne(fl32(r * fl32(1/s))),
+ *                     sign-magnitude nibbles; wscales bf16 [N, K/64];
+ *                     *wtscale_out = 1 (wtscale_out may be NULL)
+ *   nvfp4 (group 16): t = fl32(amax_R / 2688), s8 = E4M3(fl32(amax / fl32(6 t))),
+ *                     S = fl32(dec(s8) t), code = E2M1(fl32(r * fl32(1/S)));
+ *                     wscales uint8 E4M3 [N, K/16]; *wtscale_out = t (1 for an
+ *                     all-zero R), a device fp32
+ * Groups with amax < 2^-100 (or a zero scale) get scale 0 and codes 0.
+ * packed_w_out uint8 [N, K/2], low nibble = even column.  Outputs may not
+ * overlap each other, R or the workspace; errors as for svdq_w4a4_linear. */
+int svdq_w4a4_pack_weight(const float* resid, int64_t N, int64_t K, int precision, int group_size,
+                          void* packed_w_out, void* wscales_out, float* wtscale_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Parity export of the first svdq_w4a4 kernel (same kernel as the linear):
  * smoothing, activation quantization and the low-rank down projection.
  * codes_out  uint8 [M, K/2]; scales_out bf16 [M, K/64] (int4) or uint8 E4M3

@@ -262,3 +262,33 @@ def test_qkv_rules(L):
     assert call(qkv=_layer(0x1_0000_0000, K, N, rank=24)) == EUNSUP
     assert call(qkv=None) == EINVAL
     assert call(arch=b"gfx942") == EARCH
+
+
+def test_prep_rules(L):
+    K, M, N = 1024, 64, 384
+    x, w, sm, ws = 0x1_0000_0000, 0x2_0000_0000, 0x3_0000_0000, 0x4_0000_0000
+    need = L.svdq_w4a4_prep_workspace_bytes(K)
+    assert need == 8 * K and L.svdq_w4a4_prep_workspace_bytes(0) == 0
+    p = lambda v: None if v is None else _fake(v)
+
+    def smooth(x=x, M=M, w=w, N=N, K=K, sm=sm, ws=ws, wsb=need):
+        return L.svdq_w4a4_smooth_factors(p(x), M, p(w), N, K, p(sm), p(ws), wsb, None)
+    # (argument errors are found before the device is queried)
+    assert smooth(M=0) == EINVAL and smooth(N=(1 << 22) + 1) == EINVAL
+    assert smooth(K=1000) == EINVAL
+    assert smooth(x=None) == EINVAL and smooth(sm=None) == EINVAL
+    assert smooth(w=w + 4) == EINVAL
+    assert smooth(sm=w + 64) == EINVAL                 # output inside w
+    assert smooth(wsb=need - 1) == EWS
+
+    r, pk, sc, wt = 0x5_0000_0000, 0x6_0000_0000, 0x7_0000_0000, 0x8_0000_0000
+
+    def pack(r=r, N=N, K=K, prec=1, G=16, pk=pk, sc=sc, wt=wt, ws=ws, wsb=need):
+        return L.svdq_w4a4_pack_weight(p(r), N, K, prec, G, p(pk), p(sc), p(wt), p(ws), wsb, None)
+    assert pack(G=64) == EUNSUP and pack(prec=0, G=16) == EUNSUP and pack(prec=2) == EUNSUP
+    assert pack(K=100) == EINVAL and pack(N=0) == EINVAL
+    assert pack(wt=None) == EINVAL                     # nvfp4 needs the tensor scale output
+    assert pack(wt=wt + 2) == EINVAL
+    assert pack(pk=r) == EINVAL                        # output overlaps the residual
+    assert pack(sc=pk + 16) == EINVAL                  # outputs overlap
+    assert pack(wsb=0) == EWS
