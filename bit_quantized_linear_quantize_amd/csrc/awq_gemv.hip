@@ -283,7 +283,161 @@ static hipError_t launch_awq_mt(const AwqArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---- one token: a VALU GEMV ----------------------------------------------------
+// M = 1 and K a multiple of 1024 (P = K / 1024 pieces per row): the matrix
+// instructions would be mostly padding, and the LDS staging they need
+// lengthens every step's latency.  Each wave owns R weight rows:
+// * instruction i (i < P) of a row reads its bytes 512 i .. 512 i + 511,
+//   8 per lane (fully coalesced), so lane l holds codes k = 1024 i + 16 l ..
+//   1024 i + 16 l + 15 of every row: one piece of one group (16 i + l / 4);
+// * all R rows' codes, scales and zero-points are requested at once, so a
+//   wave keeps R * P * 512 bytes of weights in flight;
+// * x is loaded once per wave (the same k for every row), put in the operand
+//   pair order, and summed per piece (sum_k x, for the zero-point term);
+// * codes become bf16 128 + q (awq_operand) and v_dot2_f32_bf16 accumulates
+//   sum_k x (128 + q) in fp32 per piece; per piece and row
+//   acc += s * dot - s (128 + z) * sum_k x;
+// * the R per-lane partials are reduced over the 64 lanes with a butterfly
+//   (every exchange halves the rows a lane keeps), fixed order.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
+}
+
+template <int R, int P>
+__global__ __launch_bounds__(256) void awq_gemv1_kernel(AwqArgs args) {
+  static_assert(R * 16 * P / 4 <= 64, "one 8-byte scale load per lane and table");
+  // per wave: (s, z) bf16 pairs of its R rows x 16 P groups
+  __shared__ uint32_t sz[4][R * 16 * P];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int K = (int)args.K, N = (int)args.N;
+  const int K2 = K >> 1, G = K >> 6;
+  const int row0 = (blockIdx.x * 4 + wave) * R;
+  const uint16_t* x = (const uint16_t*)args.x;
+  const uint8_t* codes = (const uint8_t*)args.w_codes;
+
+  // x first (cached: every wave reads it), then the scales and zero-points,
+  // then this wave's weights, all rows at once
+  u32x4 xr[P][2];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const u32x4* xp = (const u32x4*)(x + 1024 * i + 16 * lane);
+    xr[i][0] = xp[0];
+    xr[i][1] = xp[1];
+  }
+  // the scales and zero-points of the R rows are contiguous (R G values
+  // each): lane l loads 4 of each (8 bytes), for lanes below R G / 4
+  constexpr int kSzLanes = R * 16 * P / 4;
+  const int nvals = (min(row0 + R, N) - row0) * G;  // values that exist
+  const int sl = min(lane, kSzLanes - 1);
+  u32x2 s4 = {0u, 0u}, z4 = {0u, 0u};
+  if (4 * sl < nvals) {
+    s4 = *(const u32x2*)((const uint16_t*)args.scales + (size_t)row0 * G + 4 * sl);
+    z4 = *(const u32x2*)((const uint16_t*)args.zeros + (size_t)row0 * G + 4 * sl);
+  }
+  u32x2 w[R][P];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(row0 + r, N - 1);
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      w[r][i] = __builtin_nontemporal_load((const u32x2*)(codes + (size_t)row * K2 + 512 * i + 8 * lane));
+  }
+  // every load above is issued before any arithmetic (the scheduler would
+  // otherwise interleave them and keep only a few in flight)
+  __builtin_amdgcn_sched_barrier(0);
+  // interleave into (s, z) pairs in the wave's table
+  if (lane < kSzLanes) {
+    u32x4 v;
+    v[0] = __builtin_amdgcn_perm(z4[0], s4[0], 0x05040100u);
+    v[1] = __builtin_amdgcn_perm(z4[0], s4[0], 0x07060302u);
+    v[2] = __builtin_amdgcn_perm(z4[1], s4[1], 0x05040100u);
+    v[3] = __builtin_amdgcn_perm(z4[1], s4[1], 0x07060302u);
+    *(u32x4*)&sz[wave][4 * lane] = v;
+  }
+  // x in operand order, and its sum per piece
+  u32x4 xo[P][2];
+  float xs[P];
+  constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    xo[i][0] = awq_x_order(xr[i][0]);
+    xo[i][1] = awq_x_order(xr[i][1]);
+    float t = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) t = dot2_bf16(xo[i][h][d], kOnes, t);
+    xs[i] = t;
+  }
+  float part[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      float d = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 op = __builtin_bit_cast(u32x4, awq_operand(w[r][i][h]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d = dot2_bf16(op[e], xo[i][h][e], d);
+      }
+      // (the wave's own LDS write precedes this read)
+      const uint32_t p = sz[wave][r * 16 * P + 16 * i + (lane >> 2)];
+      const float s = bf16_lo(p);
+      const float cz = -s * (128.0f + bf16_hi(p));  // exact
+      acc = __fmaf_rn(s, d, acc);
+      acc = __fmaf_rn(cz, xs[i], acc);
+    }
+    part[r] = acc;
+  }
+  // butterfly over the lanes: after it lane l holds the sum of row
+  // l >> (6 - log2 R)
+  int bit = 32;
+#pragma unroll
+  for (int n = R; n > 1; n >>= 1, bit >>= 1) {
+    const bool up = (lane & bit) != 0;
+#pragma unroll
+    for (int j = 0; j < n / 2; ++j) {
+      const float send = up ? part[j] : part[n / 2 + j];
+      const float keep = up ? part[n / 2 + j] : part[j];
+      part[j] = keep + __shfl_xor(send, bit, 64);
+    }
+  }
+  for (; bit >= 1; bit >>= 1) part[0] += __shfl_xor(part[0], bit, 64);
+  const int per = 64 / R;
+  const int row = row0 + lane / per;
+  if (lane % per == 0 && row < N) {
+    const float b = args.bias ? bf16_bits_to_f32(((const uint16_t*)args.bias)[row]) : 0.f;
+    ((uint16_t*)args.out)[row] = (uint16_t)f32_to_bf16_bits(part[0] + b);
+  }
+}
+
+template <int R, int P>
+static hipError_t launch_awq_gemv1(const AwqArgs& a, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((a.N + 4 * R - 1) / (4 * R));
+  hipLaunchKernelGGL((awq_gemv1_kernel<R, P>), dim3(blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+#ifndef AWQ_V1_ROWS
+#define AWQ_V1_ROWS 4
+#endif
+
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream) {
+#ifndef AWQ_NO_VALU
+  if (a.M == 1 && a.K % 1024 == 0 && a.K <= 4096) {
+    switch (a.K / 1024) {
+      case 1: return launch_awq_gemv1<AWQ_V1_ROWS, 1>(a, stream);
+      case 2: return launch_awq_gemv1<AWQ_V1_ROWS, 2>(a, stream);
+      case 3: return launch_awq_gemv1<AWQ_V1_ROWS, 3>(a, stream);
+      default: return launch_awq_gemv1<AWQ_V1_ROWS, 4>(a, stream);
+    }
+  }
+#endif
   if (a.M <= 2) return launch_awq_mt<2, 1>(a, stream);
   if (a.M <= 4) return launch_awq_mt<4, 1>(a, stream);
   return launch_awq_mt<16, 1>(a, stream);
