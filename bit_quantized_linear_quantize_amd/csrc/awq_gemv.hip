@@ -284,19 +284,23 @@ static hipError_t launch_awq_mt(const AwqArgs& a, hipStream_t stream) {
 }
 
 // ---- one token: a VALU GEMV ----------------------------------------------------
-// M = 1 and K a multiple of 1024 (P = K / 1024 pieces per row): the matrix
-// instructions would be mostly padding, and the LDS staging they need
-// lengthens every step's latency.  Each wave owns R weight rows:
-// * instruction i (i < P) of a row reads its bytes 512 i .. 512 i + 511,
-//   8 per lane (fully coalesced), so lane l holds codes k = 1024 i + 16 l ..
-//   1024 i + 16 l + 15 of every row: one piece of one group (16 i + l / 4);
-// * all R rows' codes, scales and zero-points are requested at once, so a
-//   wave keeps R * P * 512 bytes of weights in flight;
-// * x is loaded once per wave (the same k for every row), put in the operand
-//   pair order, and summed per piece (sum_k x, for the zero-point term);
+// M = 1 and K a multiple of 1024 (P = K / 1024): the matrix instructions would
+// be mostly padding, and the LDS staging they need lengthens every step's
+// latency.  Each wave owns R weight rows (R even):
+// * the rows come in pairs, 2 K/2 = 1024 P contiguous bytes; instruction i
+//   of a pair reads its bytes 1024 i .. 1024 i + 1023, 16 per lane (fully
+//   coalesced), so lane l holds 32 codes -- half a group -- of row
+//   (1024 i + 16 l) / (K/2) of the pair, the same k for every pair;
+// * all of the wave's codes are requested before any arithmetic (R * 512 P
+//   bytes in flight per wave), behind x and the scales;
+// * the workgroup stages x once in LDS, in the operand pair order; each lane
+//   reads the k it holds per use, and sums it once per piece (sum_k x, for
+//   the zero-point term);
+// * the R rows' scales and zero-points (contiguous) arrive as two 8-byte
+//   loads per lane and are interleaved into a wave-private LDS table of
+//   (s, z) pairs;
 // * codes become bf16 128 + q (awq_operand) and v_dot2_f32_bf16 accumulates
-//   sum_k x (128 + q) in fp32 per piece; per piece and row
-//   acc += s * dot - s (128 + z) * sum_k x;
+//   sum_k x (128 + q) in fp32 per piece; acc += s dot - s (128 + z) sum_k x;
 // * the R per-lane partials are reduced over the 64 lanes with a butterfly
 //   (every exchange halves the rows a lane keeps), fixed order.
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -307,29 +311,27 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 template <int R, int P>
 __global__ __launch_bounds__(256) void awq_gemv1_kernel(AwqArgs args) {
-  static_assert(R * 16 * P / 4 <= 64, "one 8-byte scale load per lane and table");
-  // per wave: (s, z) bf16 pairs of its R rows x 16 P groups
-  __shared__ uint32_t sz[4][R * 16 * P];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int K = (int)args.K, N = (int)args.N;
-  const int K2 = K >> 1, G = K >> 6;
+  static_assert(R % 2 == 0 && R * 16 * P / 4 <= 64, "row pairs; one 8-byte scale load per lane and table");
+  constexpr int K2 = 512 * P, G = 16 * P;
+  __shared__ __attribute__((aligned(16))) uint16_t xsh[1024 * P];  // x [K] bf16
+  __shared__ uint32_t sz[4][R * G];                                // per wave: (s, z) per row and group
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int N = (int)args.N;
   const int row0 = (blockIdx.x * 4 + wave) * R;
-  const uint16_t* x = (const uint16_t*)args.x;
   const uint8_t* codes = (const uint8_t*)args.w_codes;
 
-  // x first (cached: every wave reads it), then the scales and zero-points,
-  // then this wave's weights, all rows at once
-  u32x4 xr[P][2];
+  // x: 16-byte pieces 256 t + tid of the workgroup
+  constexpr int kXPieces = (2 * 1024 * P / 16 + 255) / 256;
+  u32x4 xv[kXPieces];
 #pragma unroll
-  for (int i = 0; i < P; ++i) {
-    const u32x4* xp = (const u32x4*)(x + 1024 * i + 16 * lane);
-    xr[i][0] = xp[0];
-    xr[i][1] = xp[1];
+  for (int t = 0; t < kXPieces; ++t) {
+    const int q = min(256 * t + tid, 2 * 1024 * P / 16 - 1);
+    xv[t] = *(const u32x4*)((const uint16_t*)args.x + 8 * q);
   }
-  // the scales and zero-points of the R rows are contiguous (R G values
-  // each): lane l loads 4 of each (8 bytes), for lanes below R G / 4
-  constexpr int kSzLanes = R * 16 * P / 4;
+  // the R rows' scales and zero-points: lane l loads 4 of each
+  constexpr int kSzLanes = R * G / 4;
   const int nvals = (min(row0 + R, N) - row0) * G;  // values that exist
   const int sl = min(lane, kSzLanes - 1);
   u32x2 s4 = {0u, 0u}, z4 = {0u, 0u};
@@ -337,62 +339,76 @@ __global__ __launch_bounds__(256) void awq_gemv1_kernel(AwqArgs args) {
     s4 = *(const u32x2*)((const uint16_t*)args.scales + (size_t)row0 * G + 4 * sl);
     z4 = *(const u32x2*)((const uint16_t*)args.zeros + (size_t)row0 * G + 4 * sl);
   }
-  u32x2 w[R][P];
+  // the codes, all pairs at once
+  u32x4 w[R / 2][P];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row = min(row0 + r, N - 1);
+  for (int p = 0; p < R / 2; ++p) {
+    const int pr = min(row0 + 2 * p, N - 2);
 #pragma unroll
     for (int i = 0; i < P; ++i)
-      w[r][i] = __builtin_nontemporal_load((const u32x2*)(codes + (size_t)row * K2 + 512 * i + 8 * lane));
+      w[p][i] = __builtin_nontemporal_load((const u32x4*)(codes + (size_t)pr * K2 + 1024 * i + 16 * lane));
   }
   // every load above is issued before any arithmetic (the scheduler would
   // otherwise interleave them and keep only a few in flight)
   __builtin_amdgcn_sched_barrier(0);
-  // interleave into (s, z) pairs in the wave's table
+
+  // x in LDS, each 8 values in operand order
+#pragma unroll
+  for (int t = 0; t < kXPieces; ++t)
+    if (256 * t + tid < 2 * 1024 * P / 16) *(u32x4*)(xsh + 8 * (256 * t + tid)) = awq_x_order(xv[t]);
   if (lane < kSzLanes) {
     u32x4 v;
-    v[0] = __builtin_amdgcn_perm(z4[0], s4[0], 0x05040100u);
+    v[0] = __builtin_amdgcn_perm(z4[0], s4[0], 0x05040100u);  // (s, z) of value 4 lane
     v[1] = __builtin_amdgcn_perm(z4[0], s4[0], 0x07060302u);
     v[2] = __builtin_amdgcn_perm(z4[1], s4[1], 0x05040100u);
     v[3] = __builtin_amdgcn_perm(z4[1], s4[1], 0x07060302u);
     *(u32x4*)&sz[wave][4 * lane] = v;
   }
-  // x in operand order, and its sum per piece
-  u32x4 xo[P][2];
+  lds_barrier();
+
+  // the lane's pieces: byte b_i of row r_i of each pair, codes k = 2 b_i ..
+  // 2 b_i + 31 (group b_i / 32), and sum_k x over them
   float xs[P];
+  int prow[P], pb[P];
   constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
 #pragma unroll
   for (int i = 0; i < P; ++i) {
-    xo[i][0] = awq_x_order(xr[i][0]);
-    xo[i][1] = awq_x_order(xr[i][1]);
+    const int o = 1024 * i + 16 * lane;
+    prow[i] = o >= K2 ? 1 : 0;
+    pb[i] = o - prow[i] * K2;
     float t = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 xq = *(const u32x4*)(xsh + 2 * pb[i] + 8 * h);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) t = dot2_bf16(xo[i][h][d], kOnes, t);
+      for (int d = 0; d < 4; ++d) t = dot2_bf16(xq[d], kOnes, t);
+    }
     xs[i] = t;
   }
   float part[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float acc = 0.f;
+  for (int r = 0; r < R; ++r) part[r] = 0.f;
+#pragma unroll
+  for (int p = 0; p < R / 2; ++p) {
 #pragma unroll
     for (int i = 0; i < P; ++i) {
       float d = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 op = __builtin_bit_cast(u32x4, awq_operand(w[r][i][h]));
+      for (int h = 0; h < 4; ++h) {
+        const u32x4 xq = *(const u32x4*)(xsh + 2 * pb[i] + 8 * h);
+        const u32x4 op = __builtin_bit_cast(u32x4, awq_operand(w[p][i][h]));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d = dot2_bf16(op[e], xo[i][h][e], d);
+        for (int e = 0; e < 4; ++e) d = dot2_bf16(op[e], xq[e], d);
       }
-      // (the wave's own LDS write precedes this read)
-      const uint32_t p = sz[wave][r * 16 * P + 16 * i + (lane >> 2)];
-      const float s = bf16_lo(p);
-      const float cz = -s * (128.0f + bf16_hi(p));  // exact
-      acc = __fmaf_rn(s, d, acc);
-      acc = __fmaf_rn(cz, xs[i], acc);
+      const int r = 2 * p + prow[i];
+      const uint32_t sp = sz[wave][r * G + (pb[i] >> 5)];
+      const float s = bf16_lo(sp);
+      const float cz = -s * (128.0f + bf16_hi(sp));  // exact
+      // the lane's two rows of the pair get their pieces in a fixed order
+      const float add = __fmaf_rn(cz, xs[i], s * d);
+      if (prow[i]) part[2 * p + 1] += add;
+      else part[2 * p] += add;
     }
-    part[r] = acc;
   }
   // butterfly over the lanes: after it lane l holds the sum of row
   // l >> (6 - log2 R)
@@ -411,8 +427,8 @@ __global__ __launch_bounds__(256) void awq_gemv1_kernel(AwqArgs args) {
   const int per = 64 / R;
   const int row = row0 + lane / per;
   if (lane % per == 0 && row < N) {
-    const float b = args.bias ? bf16_bits_to_f32(((const uint16_t*)args.bias)[row]) : 0.f;
-    ((uint16_t*)args.out)[row] = (uint16_t)f32_to_bf16_bits(part[0] + b);
+    const float bv = args.bias ? bf16_bits_to_f32(((const uint16_t*)args.bias)[row]) : 0.f;
+    ((uint16_t*)args.out)[row] = (uint16_t)f32_to_bf16_bits(part[0] + bv);
   }
 }
 
