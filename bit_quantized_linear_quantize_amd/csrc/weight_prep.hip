@@ -75,11 +75,15 @@ __global__ __launch_bounds__(256) void prep_smooth_kernel(const uint32_t* amax, 
   smooth[k] = bf16_from_f64(lam);
 }
 
-// tensor maximum of |r| (fp32, n values) into *amax
+// tensor maximum of |r| (fp32, n values, n a multiple of 4, 16-byte
+// aligned) into *amax: 16-byte loads, grid-stride
 __global__ __launch_bounds__(256) void prep_absmax_kernel(const float* __restrict__ r, int64_t n, uint32_t* amax) {
   uint32_t m = 0u;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    m = max(m, __float_as_uint(r[i]) & 0x7fffffffu);
+  const int64_t n4 = n >> 2;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const u32x4 v = *(const u32x4*)(r + 4 * i);
+    m = max(m, max(max(v[0] & 0x7fffffffu, v[1] & 0x7fffffffu), max(v[2] & 0x7fffffffu, v[3] & 0x7fffffffu)));
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
   if ((threadIdx.x & 63) == 0) atomicMax(amax, m);
@@ -183,8 +187,8 @@ hipError_t launch_pack_weight(const PackArgs& a, hipStream_t s) {
   const int64_t groups = a.N * (a.K / G);
   if (a.precision == kNvfp4) {
     hipLaunchKernelGGL(prep_zero_u32_kernel, dim3(1), dim3(256), 0, s, a.amax, (int64_t)1);
-    hipLaunchKernelGGL(prep_absmax_kernel, dim3(grid_for(a.N * a.K, 2048)), dim3(256), 0, s, a.resid, a.N * a.K,
-                       a.amax);
+    hipLaunchKernelGGL(prep_absmax_kernel, dim3(grid_for(a.N * a.K / 4, 4096)), dim3(256), 0, s, a.resid,
+                       a.N * a.K, a.amax);
     hipLaunchKernelGGL(prep_pack_kernel<kNvfp4>, dim3(grid_for(groups, 1 << 30)), dim3(256), 0, s, a.resid, a.N,
                        a.K, (uint8_t*)a.packed, a.scales, (const uint32_t*)a.amax, a.wtscale);
   } else {
