@@ -367,13 +367,15 @@ def time_graph(calls, reps, stream):
     return e0.elapsed_time(e1) / reps  # ms per replay
 
 
-ONLY_LEGS = {"quant_int4", "quant_nvfp4", "gemm_int4", "gemm_nvfp4", "awq_m1", "awq_m16", "mlp_fused", "copy"}
+ONLY_LEGS = {"quant_int4", "quant_nvfp4", "gemm_int4", "gemm_nvfp4", "awq_m1", "awq_m16", "mlp_fused", "qkv_fused",
+             "copy"}
 
 
 def run_only(leg, steps):
     """Launch a single kernel of the headline workload `steps` times (after one
     warm-up call), for per-kernel hardware-counter passes.  `mlp_fused` is the
-    fused GELU MLP pair (nvfp4, M=4096, 3072 -> 12288 -> 3072, rank 32).
+    fused GELU MLP pair (nvfp4, M=4096, 3072 -> 12288 -> 3072, rank 32);
+    `qkv_fused` the QKV projection 3072 -> 9216 with RMSNorm + RoPE (nvfp4).
     `copy` is a plain device-to-device copy of 256 MiB, the reference for
     scaling HBM byte counters."""
     import numpy as np
@@ -410,6 +412,17 @@ def run_only(leg, steps):
         ws = torch.empty(bq.mlp_workspace_bytes(M, up, down), dtype=torch.uint8, device="cuda")
         y = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
         fn = lambda: bq.svdq_w4a4_mlp_gelu(x, up, down, out=y, workspace=ws)
+    elif leg == "qkv_fused":
+        heads, Nq = 24, 9216
+        rl, rx, rn = S.streams(17, 3)
+        layer = bq.SVDQLinear.from_numpy(S.random_svdq_layer(Nq, K, "nvfp4", rank, rl))
+        x = torch.from_numpy(S.activations(M, K, round(0.01 * K), rx).view(np.int16).copy()).view(torch.bfloat16).cuda()
+        qn, kn = (torch.from_numpy(S.norm_weight(128, rn).view(np.int16).copy()).view(torch.bfloat16).cuda()
+                  for _ in range(2))
+        cos, sin = (torch.from_numpy(t).cuda() for t in S.rope_tables(M, 128))
+        ws = torch.empty(layer.workspace_bytes(M), dtype=torch.uint8, device="cuda")
+        y = torch.empty((M, Nq), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: bq.svdq_w4a4_qkv_rmsnorm_rope(x, layer, heads, qn, kn, cos, sin, out=y, workspace=ws)
     else:
         precision = "int4" if leg.endswith("int4") else "nvfp4"
         rx, rl = S.streams(0, 2)
