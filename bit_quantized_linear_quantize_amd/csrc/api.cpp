@@ -8,6 +8,7 @@
 //   (int4, 64) and (nvfp4, 16) only; AWQ group 64      -> SVDQ_EUNSUPPORTED
 //   rank in 0..128, multiple of 16                      -> SVDQ_EUNSUPPORTED
 //   M >= 1, K % 128 == 0, 128 <= K <= 16384, N % 64 == 0 -> SVDQ_EINVAL
+//   svdq: at most 2^23 - 1 output tiles of 256 x 192     -> SVDQ_EINVAL
 //   null / non-16-byte-aligned pointers, out overlapping an input or the
 //   workspace, wtscale != 1 for int4                      -> SVDQ_EINVAL
 //   workspace too small                                 -> SVDQ_EWORKSPACE
@@ -87,6 +88,16 @@ int check_shape(int64_t M, int64_t K, int64_t N) {
   return SVDQ_OK;
 }
 
+// The product kernel launches one 512-thread workgroup per 256 x 192 output
+// tile: the grid must stay below 2^32 work-items.
+constexpr int64_t kMaxGemmTiles = (int64_t(1) << 23) - 1;
+
+int check_gemm_tiles(int64_t M, int64_t N) {
+  if (((M + 255) / 256) * ((N + 191) / 192) > kMaxGemmTiles)
+    return fail(SVDQ_EINVAL, "M x N too large: more than 2^23 - 1 output tiles of 256 x 192");
+  return SVDQ_OK;
+}
+
 int check_svdq_kind(int precision, int group_size, int rank) {
   if (precision == SVDQ_INT4) {
     if (group_size != 64) return fail(SVDQ_EUNSUPPORTED, "int4 requires group_size 64");
@@ -120,6 +131,8 @@ int validate_svdq(const void* x, int64_t M, int64_t K, int64_t N, const void* pa
   int rc = check_svdq_kind(precision, group_size, rank);
   if (rc) return rc;
   rc = check_shape(M, K, N);
+  if (rc) return rc;
+  rc = check_gemm_tiles(M, N);
   if (rc) return rc;
   if (!x || !packed_w || !wscales || !smooth || !out || !workspace)
     return fail(SVDQ_EINVAL, "null pointer argument");
@@ -225,6 +238,8 @@ int validate_layer(int64_t M, const svdq_w4a4_layer* L, const char* which) {
   if (rc) return rc;
   rc = check_shape(M, L->K, L->N);
   if (rc) return rc;
+  rc = check_gemm_tiles(M, L->N);
+  if (rc) return rc;
   if (!L->packed_w || !L->wscales || !L->smooth) return fail(SVDQ_EINVAL, w + " layer: null pointer");
   if ((L->rank > 0) != (L->lora_down != nullptr) || (L->rank > 0) != (L->lora_up != nullptr))
     return fail(SVDQ_EINVAL, w + " layer: lora_down / lora_up must be non-null exactly when rank > 0");
@@ -329,7 +344,8 @@ const char* svdq_last_error(void) { return g_last_error.c_str(); }
 size_t svdq_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision, int group_size,
                                  int rank) {
   const std::string saved = g_last_error;
-  const bool ok = check_svdq_kind(precision, group_size, rank) == SVDQ_OK && check_shape(M, K, N) == SVDQ_OK;
+  const bool ok = check_svdq_kind(precision, group_size, rank) == SVDQ_OK && check_shape(M, K, N) == SVDQ_OK &&
+                  check_gemm_tiles(M, N) == SVDQ_OK;
   g_last_error = saved;
   return ok ? workspace_bytes(M, K, precision, rank) : 0;
 }
@@ -387,6 +403,8 @@ int svdq_w4a4_gemm(const void* workspace, size_t ws_bytes, int64_t M, int64_t K,
   int rc = check_svdq_kind(precision, group_size, rank);
   if (rc) return rc;
   rc = check_shape(M, K, N);
+  if (rc) return rc;
+  rc = check_gemm_tiles(M, N);
   if (rc) return rc;
   if (!workspace || !packed_w || !wscales || !out) return fail(SVDQ_EINVAL, "null pointer argument");
   if ((rank > 0) != (lora_up != nullptr))
@@ -470,6 +488,8 @@ int svdq_w4a4_gemm_partials(const void* act_codes, const void* w_codes, int64_t 
   int rc = check_svdq_kind(precision, group_size, 0);
   if (rc) return rc;
   rc = check_shape(M, K, N);
+  if (rc) return rc;
+  rc = check_gemm_tiles(M, N);
   if (rc) return rc;
   if (!act_codes || !w_codes || !partials_out) return fail(SVDQ_EINVAL, "null pointer argument");
   const void* ptrs[] = {act_codes, w_codes, partials_out};

@@ -29,17 +29,18 @@ __global__ __launch_bounds__(256) void prep_zero_u32_kernel(uint32_t* p, int64_t
 
 // column maxima of |x| (bf16 [M, K]) and |w| (fp32 [N, K]) into amax[0 .. K)
 // and amax[K .. 2K); block (bx, by) covers columns 256 bx .. and rows
-// kPrepRows by ..
+// rows_per_block by ..
 constexpr int kPrepRows = 64;
+constexpr int64_t kMaxGridY = 65535;
 
 __global__ __launch_bounds__(256) void prep_colmax_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                           const float* __restrict__ w, int64_t N, int64_t K,
-                                                          uint32_t* amax) {
+                                                          int64_t rows_per_block, uint32_t* amax) {
   const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (k >= K) return;
-  const int64_t r0 = (int64_t)blockIdx.y * kPrepRows;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   uint32_t mx = 0u, mw = 0u;
-  for (int64_t r = r0; r < r0 + kPrepRows; ++r) {
+  for (int64_t r = r0; r < r0 + rows_per_block; ++r) {
     if (r < M) mx = max(mx, (uint32_t)(x[r * K + k] & 0x7fffu) << 16);
     if (r < N) mw = max(mw, __float_as_uint(w[r * K + k]) & 0x7fffffffu);
   }
@@ -175,8 +176,11 @@ static unsigned grid_for(int64_t n, int64_t cap) {
 hipError_t launch_smooth_factors(const SmoothArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prep_zero_u32_kernel, dim3(grid_for(2 * a.K, 1024)), dim3(256), 0, s, a.amax, 2 * a.K);
   const int64_t rows = a.M > a.N ? a.M : a.N;
-  const dim3 grid((unsigned)((a.K + 255) / 256), (unsigned)((rows + kPrepRows - 1) / kPrepRows));
-  hipLaunchKernelGGL(prep_colmax_kernel, grid, dim3(256), 0, s, (const uint16_t*)a.x, a.M, a.w, a.N, a.K, a.amax);
+  int64_t rpb = kPrepRows;
+  if ((rows + rpb - 1) / rpb > kMaxGridY) rpb = (rows + kMaxGridY - 1) / kMaxGridY;
+  const dim3 grid((unsigned)((a.K + 255) / 256), (unsigned)((rows + rpb - 1) / rpb));
+  hipLaunchKernelGGL(prep_colmax_kernel, grid, dim3(256), 0, s, (const uint16_t*)a.x, a.M, a.w, a.N, a.K, rpb,
+                     a.amax);
   hipLaunchKernelGGL(prep_smooth_kernel, dim3(grid_for(a.K, 1 << 20)), dim3(256), 0, s, (const uint32_t*)a.amax,
                      a.K, (uint16_t*)a.smooth);
   return hipGetLastError();

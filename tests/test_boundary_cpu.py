@@ -114,6 +114,12 @@ def test_shape_rules(L):
     assert Args().call(L, K=64) == EINVAL
     assert Args().call(L, N=96) == EINVAL
     assert Args().call(L, K=32768) == EINVAL
+    # the product kernel's grid: at most 2^23 - 1 tiles of 256 x 192
+    M = 1 << 24
+    assert L.svdq_w4a4_workspace_bytes(M, 512, 127 * 192, 0, 64, 32) > 0
+    assert L.svdq_w4a4_workspace_bytes(M, 512, 128 * 192, 0, 64, 32) == 0
+    assert Args().call(L, M=M, N=128 * 192, wsb=1 << 62) == EINVAL
+    assert b"output tiles" in L.svdq_last_error()
 
 
 def test_null_and_alignment(L):
