@@ -318,11 +318,12 @@ def test_awq_ragged(M):
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 64), (3, 640, 128), (4, 1152, 192), (5, 8192, 64),
                                    (2, 16384, 64), (17, 3200, 128), (1, 1024, 64), (1, 2048, 192),
-                                   (1, 4096, 320), (1, 8192, 64)])
+                                   (1, 4096, 320), (1, 8192, 64), (2, 2048, 192), (2, 4096, 320)])
 def test_awq_shapes(M, K, N):
     # X-row tiles of 1, 2, 4 and 16 rows; K from one group pair to the maximum
     # (a scale table wider than one load batch); partial 4-group steps; the
-    # one-token VALU path for K = 1024 .. 4096 (and K = 8192 past it)
+    # the one-token VALU path for K = 1024 .. 4096 (and K = 8192 past it);
+    # two tokens at the same K on the matrix-instruction kernel
     rng = np.random.default_rng(K + M)
     w = rng.standard_normal((N, K)) * 0.02
     lay = L.prepare_awq_layer(w, S.bias(N, rng))
