@@ -28,7 +28,7 @@ EXPORTS = ("svdq_w4a4_workspace_bytes", "svdq_w4a4_linear", "svdq_w4a4_quantize"
            "svdq_w4a4_quantize_act", "svdq_w4a4_gemm_partials", "svdq_w4a4_check",
            "awq_w4a16_check", "svdq_w4a4_mlp_gelu_check", "svdq_w4a4_qkv_rmsnorm_rope",
            "svdq_w4a4_qkv_rmsnorm_rope_check", "svdq_w4a4_prep_workspace_bytes", "svdq_w4a4_smooth_factors",
-           "svdq_w4a4_pack_weight", "svdq_last_error")
+           "svdq_w4a4_pack_weight", "svdq_w4a4_gelu_table", "svdq_last_error")
 
 
 class LayerStruct(ctypes.Structure):
@@ -98,6 +98,8 @@ def lib():
         L.svdq_w4a4_smooth_factors.restype = I
         L.svdq_w4a4_pack_weight.argtypes = [P, I64, I64, I, I, P, P, P, P, ctypes.c_size_t, P]
         L.svdq_w4a4_pack_weight.restype = I
+        L.svdq_w4a4_gelu_table.argtypes = [P, P]
+        L.svdq_w4a4_gelu_table.restype = I
         L.svdq_last_error.argtypes = []
         L.svdq_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -267,6 +269,14 @@ def svdq_w4a4_qkv_rmsnorm_rope(x, qkv, heads, q_norm, k_norm, rope_cos, rope_sin
     _check(lib().svdq_w4a4_qkv_rmsnorm_rope(
         _ptr(x), M, ctypes.byref(q), heads, head_dim, _ptr(q_norm), _ptr(k_norm), float(eps), _ptr(rope_cos),
         _ptr(rope_sin), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def gelu_table(stream=None):
+    """Parity export: the fused MLP epilogue's bf16 GELU table, uint16 [65536]
+    (entry b = bf16 bits of GELU of the bf16 value with bits b)."""
+    out = torch.empty(1 << 16, dtype=torch.int16, device="cuda")
+    _check(lib().svdq_w4a4_gelu_table(_ptr(out), _stream(stream)))
     return out
 
 

@@ -37,11 +37,15 @@ def _run(cmd):
 def build(verbose=False):
     os.makedirs(LIBDIR, exist_ok=True)
     os.makedirs(BUILD, exist_ok=True)
+    # generated sources (the bf16 GELU table of the fused MLP epilogue)
+    sys.path.insert(0, HERE)
+    import gelu_bf16_gen
+    gelu_bf16_gen.write(os.path.join(BUILD, "gelu_bf16_table.inc"))
 
     def compile_one(src):
         obj = os.path.join(BUILD, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        _run([HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
+        _run([HIPCC] + FLAGS + ["-I", BUILD] + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:

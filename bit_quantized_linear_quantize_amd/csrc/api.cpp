@@ -646,4 +646,14 @@ int svdq_w4a4_pack_weight(const float* resid, int64_t N, int64_t K, int precisio
   return launch_status(svdq::launch_pack_weight(a, static_cast<hipStream_t>(stream)), "pack weight launch");
 }
 
+int svdq_w4a4_gelu_table(void* out, void* stream) {
+  g_last_error.clear();
+  if (!out) return fail(SVDQ_EINVAL, "null pointer argument");
+  if (!aligned(out)) return fail(SVDQ_EINVAL, "out must be 16-byte aligned");
+  int rc = check_device_arch();
+  if (rc) return rc;
+  return launch_status(svdq::launch_gelu_table_copy(static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)),
+                       "GELU table copy launch");
+}
+
 }  // extern "C"

@@ -138,41 +138,18 @@ __device__ __forceinline__ void tile_of(int bid, int nmt, int nnt, int& mt, int&
 // operand-layout reads).
 constexpr int kGeluRow = 208;
 
-// erfc(z) for z >= 0 by the Chebyshev fit of Numerical Recipes in C (2nd
-// ed., section 6.2, "erfcc"): t = 1 / (1 + z/2), erfc(z) = t exp(-z^2 +
-// P(t)) with a 9th-degree P, fractional error below 1.2e-7 for every z >= 0.
-__device__ __forceinline__ float erfc_cheb(float z) {
-  const float t = __builtin_amdgcn_rcpf(__fmaf_rn(0.5f, z, 1.0f));
-  float q = 0.17087277f;
-  q = __fmaf_rn(t, q, -0.82215223f);
-  q = __fmaf_rn(t, q, 1.48851587f);
-  q = __fmaf_rn(t, q, -1.13520398f);
-  q = __fmaf_rn(t, q, 0.27886807f);
-  q = __fmaf_rn(t, q, -0.18628806f);
-  q = __fmaf_rn(t, q, 0.09678418f);
-  q = __fmaf_rn(t, q, 0.37409196f);
-  q = __fmaf_rn(t, q, 1.00002368f);
-  q = __fmaf_rn(t, q, -1.26551223f);
-  return __fmul_rn(t, __expf(__fmaf_rn(-z, z, q)));
-}
-
-// GELU with the exact erf, y/2 (1 + erf(y / sqrt 2)), on an fp32 value,
-// evaluated as (y / 2) erfc(-y / sqrt 2) -- no cancellation of 1 + erf for
-// negative y -- with erfc(-a) = 2 - erfc(a) for y > 0.  A float32 model of
-// this evaluation (exact exp in place of __expf), rounded to bf16, gives the
-// correctly rounded GELU of every bf16 input with a normal result.
-__device__ __forceinline__ float gelu_erf(float y) {
-  const float e = erfc_cheb(__fmul_rn(fabsf(y), 0.70710678118654752f));
-  return __fmul_rn(__fmul_rn(y, 0.5f), y > 0.f ? __fsub_rn(2.0f, e) : e);
-}
+// GELU with the exact erf of every bf16 value, rounded to bf16 (the table is
+// generated at build time in double precision: gelu_bf16_gen.py).  The epilogue's
+// GELU input is a bf16 value, so one lookup gives the correctly rounded result.
+#include "gelu_bf16_table.inc"
 
 // The MLP fusion epilogue of one wave ("Fused kernels" of the Nunchaku Lite
 // docs page: the MLP's GELU and the quantization for the down projection in
 // the up projection's epilogue).  acc holds this wave's 64 x 96 block of the
 // up projection before its bias.  Steps:
 //  1. g = bf16(GELU(bf16(acc + bias))) -- the values a bf16 up output followed
-//     by a bf16 GELU would give -- into the wave's LDS tile `tile_base`
-//     (+ 64 kGeluRow for odd waves);
+//     by a bf16 GELU would give; GELU by the table kGeluBf16 -- into the
+//     wave's LDS tile `tile_base` (+ 64 kGeluRow for odd waves);
 //  2. the next layer's low-rank activations: x = fl32(g * (1 / smooth_next))
 //     in the 16x16x32 bf16 operand layout, split hi + lo, times
 //     next_lora_down, added into next_lora_act with fp32 atomics (one
@@ -207,8 +184,7 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-        const float y = __uint_as_float(f32_to_bf16_bits(acc[i][j][e] + bv) << 16);
-        *(uint16_t*)(gt + r * kGeluRow + (j * 32 + l32) * 2) = (uint16_t)f32_to_bf16_bits(gelu_erf(y));
+        *(uint16_t*)(gt + r * kGeluRow + (j * 32 + l32) * 2) = kGeluBf16[f32_to_bf16_bits(acc[i][j][e] + bv)];
       }
   }
   // (the wave's own LDS writes and reads execute in order)
@@ -824,6 +800,17 @@ static hipError_t dispatch_rank(const GemmArgs& a, hipStream_t s) {
     }
 #undef SVDQ_K2_CASE
   }
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void gelu_table_copy_kernel(uint16_t* out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  out[i] = kGeluBf16[i];
+}
+
+// Parity export: the 65536-entry bf16 GELU table.
+hipError_t launch_gelu_table_copy(uint16_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(gelu_table_copy_kernel, dim3(256), dim3(256), 0, stream, out);
   return hipGetLastError();
 }
 

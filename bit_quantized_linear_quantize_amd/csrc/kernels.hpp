@@ -93,6 +93,7 @@ hipError_t launch_smooth_factors(const SmoothArgs& a, hipStream_t stream);
 hipError_t launch_pack_weight(const PackArgs& a, hipStream_t stream);
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream);
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gelu_table_copy(uint16_t* out, hipStream_t stream);
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream);
 
 }  // namespace svdq

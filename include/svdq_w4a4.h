@@ -243,6 +243,12 @@ int svdq_w4a4_pack_weight(const float* resid, int64_t N, int64_t K, int precisio
                           void* packed_w_out, void* wscales_out, float* wtscale_out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Parity export of the fused MLP's GELU: out (bf16 [65536]) receives, for
+ * every bf16 bit pattern b, the bits of GELU(h) = h/2 (1 + erf(h / sqrt 2))
+ * of the value h with bits b, rounded once to bf16 -- the table the epilogue
+ * of svdq_w4a4_mlp_gelu looks its GELU up in. */
+int svdq_w4a4_gelu_table(void* out, void* stream);
+
 /* Parity export of the first svdq_w4a4 kernel (same kernel as the linear):
  * smoothing, activation quantization and the low-rank down projection.
  * codes_out  uint8 [M, K/2]; scales_out bf16 [M, K/64] (int4) or uint8 E4M3
