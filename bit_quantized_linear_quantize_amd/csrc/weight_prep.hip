@@ -77,8 +77,10 @@ __global__ __launch_bounds__(256) void prep_smooth_kernel(const uint32_t* amax, 
 }
 
 // tensor maximum of |r| (fp32, n values, n a multiple of 4, 16-byte
-// aligned) into *amax: 16-byte loads, grid-stride
+// aligned) into *amax: 16-byte loads, grid-stride, one atomic per workgroup
+// (atomics on one address serialize)
 __global__ __launch_bounds__(256) void prep_absmax_kernel(const float* __restrict__ r, int64_t n, uint32_t* amax) {
+  __shared__ uint32_t wmax[4];
   uint32_t m = 0u;
   const int64_t n4 = n >> 2;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
@@ -87,7 +89,9 @@ __global__ __launch_bounds__(256) void prep_absmax_kernel(const float* __restric
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(amax, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(amax, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
 }
 
 // One thread per group: G fp32 values of row n -> G/2 code bytes and a scale.
@@ -191,7 +195,7 @@ hipError_t launch_pack_weight(const PackArgs& a, hipStream_t s) {
   const int64_t groups = a.N * (a.K / G);
   if (a.precision == kNvfp4) {
     hipLaunchKernelGGL(prep_zero_u32_kernel, dim3(1), dim3(256), 0, s, a.amax, (int64_t)1);
-    hipLaunchKernelGGL(prep_absmax_kernel, dim3(grid_for(a.N * a.K / 4, 4096)), dim3(256), 0, s, a.resid,
+    hipLaunchKernelGGL(prep_absmax_kernel, dim3(grid_for(a.N * a.K / 4, 1024)), dim3(256), 0, s, a.resid,
                        a.N * a.K, a.amax);
     hipLaunchKernelGGL(prep_pack_kernel<kNvfp4>, dim3(grid_for(groups, 1 << 30)), dim3(256), 0, s, a.resid, a.N,
                        a.K, (uint8_t*)a.packed, a.scales, (const uint32_t*)a.amax, a.wtscale);
