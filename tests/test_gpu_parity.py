@@ -233,6 +233,17 @@ def test_linear_full_size(cfg1_layers, which):
     assert_output(y, L.svdq_linear_ref(c["x"], lay), f"linear cfg1 {which}")
 
 
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+@pytest.mark.parametrize("M,K,N,rank", [(33, 16384, 320, 32), (70, 128, 64, 16), (5, 128, 448, 0)])
+def test_linear_k_extremes(precision, M, K, N, rank):
+    # K = 16384 (the largest accepted: 256 stages, not a multiple of the
+    # loop's six) and K = 128 (two stages); N with a partial 192-column tile
+    rng = np.random.default_rng(K + N + M)
+    x = S.activations(M, K, 3, rng)
+    lay = prepared(x, S.weight(N, K, 0.02, rng, spike_rank=2), S.bias(N, rng), precision, rank, smooth="calibrated")
+    assert_output(run_linear(x, lay), L.svdq_linear_ref(x, lay), f"linear {precision} M={M} K={K} N={N} r{rank}")
+
+
 def test_linear_int4_row_exponents():
     # int4 activations enter the product as fp16 q * s * 2^-E[row]; E = 0 when
     # every group scale s of the row is in [2^-17, 2^13), else the row is
