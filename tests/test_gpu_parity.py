@@ -129,6 +129,16 @@ def test_quantize_act_ragged(ragged, precision, rank):
     check_quantize_act(x, lay, f"k1 ragged {precision} r{rank}")
 
 
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+@pytest.mark.parametrize("M,K,rank", [(33, 16384, 32), (70, 128, 16), (17, 16384, 128)])
+def test_quantize_act_k_extremes(precision, M, K, rank):
+    # codes and scales bit-exact at the largest and smallest K
+    rng = np.random.default_rng(M + K + rank)
+    x = S.activations(M, K, 3, rng)
+    lay = prepared(x, S.weight(128, K, 0.02, rng), None, precision, rank, smooth="calibrated")
+    check_quantize_act(x, lay, f"k1 {precision} M={M} K={K} r{rank}")
+
+
 @pytest.mark.parametrize("which", ["int4", "nvfp4"])
 def test_quantize_act_full_size(cfg1_layers, which):
     c, lay4, layfp4 = cfg1_layers
