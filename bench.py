@@ -8,6 +8,8 @@ resident in HBM.  value = effective TOPS = 2 M N K / step time.
 
 Also measured in the same run (reported under "extra"):
   * the nvfp4 variant of the same layer;
+  * the same int4 layer on one GPU's share of the tokens when 8 GPUs split
+    them (M = 512);
   * per-kernel durations (HIP events on the launch stream) of
     quantize_act_lora_down and gemm_w4a4_lora_up, from which the roofline
     object of the dominant kernel (gemm_w4a4_lora_up) is computed;
@@ -540,6 +542,22 @@ def main():
                           "gemm_w4a4_lora_up_TOPS": round(k2n, 1),
                           "gemm_frac_of_f16_peak": round(k2n / PEAK["f16"], 4),
                           "instruction": "v_mfma_f32_32x32x16_f16 (exactly dequantized E2M1 x E4M3)"}
+        # one GPU's share of the same layer when 8 GPUs split the tokens (M = 512):
+        # 32 of the 256 x 192 tiles, so 1/8 of the CUs get work
+        log("timing the M=512 token shard ...")
+        xs = x[:512].contiguous()
+        lay_s = bq.SVDQLinear.from_numpy(r4["lay"])
+        ws_s = torch.empty(lay_s.workspace_bytes(512), dtype=torch.uint8, device="cuda")
+        out_s = torch.empty((512, N), dtype=torch.bfloat16, device="cuda")
+        f_s = lambda: lay_s(xs, out=out_s, workspace=ws_s)
+        for _ in range(50):
+            f_s()
+        t_s = time_graph(f_s, 200, stream)
+        if t_s is None:
+            t_s = time_events(f_s, 200, stream)
+        extra["int4_token_shard_M512"] = {"step_us": round(t_s * 1e3, 2),
+                                          "TOPS": round(2.0 * 512 * N * K / (t_s * 1e-3) / 1e12, 1),
+                                          "tiles": 2 * 16}
         log("timing awq_w4a16 ...")
         Na, Ka, copies = 18432, 3072, 12
         ra = S.streams(7, copies + 1)

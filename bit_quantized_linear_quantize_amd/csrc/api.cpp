@@ -114,7 +114,7 @@ size_t w_scale_bytes(int64_t N, int64_t K, int precision) {
   return precision == SVDQ_INT4 ? size_t(N) * size_t(K / 64) * 2 : size_t(N) * size_t(K / 16);
 }
 
-// Workspace of svdq_w4a4_linear (each part 256-byte aligned):
+// Base workspace of one layer (each part 256-byte aligned):
 //   act_f16    f16 [M, K]   dequantized activations, the product operand
 //   row_scale  int4 only: f32 [M], the power of two factored out of each row
 //   lora_act   f32 [M, rank]
@@ -122,6 +122,32 @@ size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
   size_t b = round_up(size_t(M) * size_t(K) * 2);
   if (precision == SVDQ_INT4) b += round_up(size_t(M) * 4);
   return b + round_up(size_t(M) * size_t(rank) * 4);
+}
+
+// Split K for the plain linear: when the 256 x 192 tiles would occupy less
+// than half of the 256 compute units, each tile's stages are shared by up to
+// 8 workgroups (at least 2 stages each) that write fp32 partials, summed in a
+// fixed order by a second kernel.
+int choose_ksplit(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 191) / 192);
+  const int nst = int(K / 64);
+  if (tiles >= 128) return 1;
+  int s = int(std::min<int64_t>(8, 256 / tiles));
+  s = std::min(s, nst / 2);
+  s = std::max(s, 1);
+  while (s > 1 && ((nst + s - 1) / s) * (s - 1) >= nst) --s;  // every split gets stages
+  return s;
+}
+
+size_t split_bytes(int64_t M, int64_t K, int64_t N) {
+  const int s = choose_ksplit(M, N, K);
+  return s > 1 ? round_up(size_t(s) * size_t(M) * size_t(N) * 4) : 0;
+}
+
+// Workspace of svdq_w4a4_linear / svdq_w4a4_gemm: workspace_bytes, then the
+// split-K partials fp32 [ksplit, M, N] when K is split.
+size_t linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision, int rank) {
+  return workspace_bytes(M, K, precision, rank) + split_bytes(M, K, N);
 }
 
 int validate_svdq(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
@@ -144,7 +170,7 @@ int validate_svdq(const void* x, int64_t M, int64_t K, int64_t N, const void* pa
   if (precision == SVDQ_INT4 && wtscale != 1.0f) return fail(SVDQ_EINVAL, "wtscale must be 1.0 for int4");
   if (precision == SVDQ_NVFP4 && !(std::isfinite(wtscale) && wtscale > 0.f))
     return fail(SVDQ_EINVAL, "wtscale must be finite and positive");
-  const size_t need = workspace_bytes(M, K, precision, rank);
+  const size_t need = linear_workspace_bytes(M, K, N, precision, rank);
   const Range o{out, size_t(M) * size_t(N) * 2};
   const Range ins[] = {{x, size_t(M) * size_t(K) * 2},
                        {packed_w, size_t(N) * size_t(K / 2)},
@@ -218,13 +244,20 @@ int launch_quantize(const void* x, int64_t M, int64_t K, const void* smooth, con
   return launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
 }
 
+// Kernel 2 (plain store) from a linear workspace (linear_workspace_bytes).
 int launch_gemm(const void* workspace, int64_t M, int64_t K, int64_t N, const void* packed_w,
                 const void* wscales, float wtscale, const void* lora_up, const void* bias, int precision,
                 int rank, void* out, hipStream_t s) {
   const Carve c = carve(const_cast<void*>(workspace), M, K, precision);
   svdq::GemmArgs ga{c.act_f16, c.row_scale, c.lora_act, packed_w, wscales, lora_up, bias, out, nullptr,
                     wtscale, M, K, N, precision, rank};
-  return launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up launch");
+  ga.ksplit = choose_ksplit(M, N, K);
+  if (ga.ksplit > 1)
+    ga.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(workspace)) +
+                                          workspace_bytes(M, K, precision, rank));
+  int rc = launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up launch");
+  if (rc || ga.ksplit == 1) return rc;
+  return launch_status(svdq::launch_splitk_reduce(ga.partial, ga.ksplit, M, N, bias, out, s), "split-K sum launch");
 }
 
 // ---- fused GELU MLP ----------------------------------------------------------
@@ -253,7 +286,8 @@ int validate_layer(int64_t M, const svdq_w4a4_layer* L, const char* which) {
 }
 
 size_t mlp_workspace_bytes(int64_t M, const svdq_w4a4_layer* up, const svdq_w4a4_layer* down) {
-  return workspace_bytes(M, up->K, up->precision, up->rank) + workspace_bytes(M, down->K, SVDQ_NVFP4, down->rank);
+  return workspace_bytes(M, up->K, up->precision, up->rank) +
+         linear_workspace_bytes(M, down->K, down->N, SVDQ_NVFP4, down->rank);
 }
 
 int validate_mlp(const void* x, int64_t M, const svdq_w4a4_layer* up, const svdq_w4a4_layer* down,
@@ -347,7 +381,7 @@ size_t svdq_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision,
   const bool ok = check_svdq_kind(precision, group_size, rank) == SVDQ_OK && check_shape(M, K, N) == SVDQ_OK &&
                   check_gemm_tiles(M, N) == SVDQ_OK;
   g_last_error = saved;
-  return ok ? workspace_bytes(M, K, precision, rank) : 0;
+  return ok ? linear_workspace_bytes(M, K, N, precision, rank) : 0;
 }
 
 int svdq_w4a4_check(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
@@ -415,7 +449,7 @@ int svdq_w4a4_gemm(const void* workspace, size_t ws_bytes, int64_t M, int64_t K,
   if (precision == SVDQ_INT4 && wtscale != 1.0f) return fail(SVDQ_EINVAL, "wtscale must be 1.0 for int4");
   if (precision == SVDQ_NVFP4 && !(std::isfinite(wtscale) && wtscale > 0.f))
     return fail(SVDQ_EINVAL, "wtscale must be finite and positive");
-  const size_t need = workspace_bytes(M, K, precision, rank);
+  const size_t need = linear_workspace_bytes(M, K, N, precision, rank);
   const Range o{out, size_t(M) * size_t(N) * 2};
   const Range ins[] = {{workspace, need},
                        {packed_w, size_t(N) * size_t(K / 2)},

@@ -76,6 +76,7 @@ using IC = std::integral_constant<int, I>;
 constexpr int kEpiStore = 0;
 constexpr int kEpiGelu = 1;
 constexpr int kEpiQk = 2;
+constexpr int kEpiSplit = 3;  // split K: fp32 partials
 
 // QKV fusion column order.  The output is q | k | v with heads of 128
 // columns; a 192-column tile cannot hold whole heads of q or k in the natural
@@ -414,7 +415,15 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   int mt, nt;
   tile_of(blockIdx.x, nmt, nnt, mt, nt);
   const int m0 = mt * kBM, n0 = nt * kBN;
-  const int nstages = K / kBK;
+  // split K: this workgroup's stages [s0, s0 + nstages) (the loads below take
+  // their stage offsets from descriptor bases moved to stage s0)
+  constexpr bool kSplit = EPI == kEpiSplit;
+  int s0 = 0, nstages = K / kBK;
+  if constexpr (kSplit) {
+    const int per = (nstages + args.ksplit - 1) / args.ksplit;
+    s0 = blockIdx.y * per;
+    nstages = min(per, nstages - s0);
+  }
   // physical column of tile column c (the QKV fusion reorders columns)
   constexpr bool kQk = EPI == kEpiQk;
   const int qk_cols = kQk ? 2 * args.heads * kHeadDim : 0;
@@ -439,16 +448,17 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   const int lc = tid & 7;    // column chunk: columns 8 lc .. 8 lc + 7 of the stage
   const int lr = tid >> 3;   // tile row of piece 0 (piece i: lr + 64 i)
   const size_t a_row_bytes = PARTIALS ? (size_t)K2 : (size_t)K * 2;
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc((const uint8_t*)args.act + (size_t)m0 * a_row_bytes,
-                                                (size_t)(M - m0) * a_row_bytes);
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc((const uint8_t*)args.act + (size_t)m0 * a_row_bytes + s0 * 128,
+                                                (size_t)(M - m0) * a_row_bytes - s0 * 128);
   // (the QKV fusion addresses W rows from the matrix start: its tile rows
   // are not contiguous)
   const int w_base = kQk ? 0 : n0;
-  const __amdgpu_buffer_rsrc_t w_rs = make_rsrc((const uint8_t*)args.w_codes + (size_t)w_base * K2,
-                                                (size_t)(N - w_base) * K2);
+  const __amdgpu_buffer_rsrc_t w_rs = make_rsrc((const uint8_t*)args.w_codes + (size_t)w_base * K2 + s0 * 32,
+                                                (size_t)(N - w_base) * K2 - s0 * 32);
   const size_t ws_row_bytes = PREC == kInt4 ? (size_t)(K >> 6) * 2 : (size_t)(K >> 4);
-  const __amdgpu_buffer_rsrc_t ws_rs = make_rsrc((const uint8_t*)args.w_scales + (size_t)w_base * ws_row_bytes,
-                                                 PARTIALS ? 0 : (size_t)(N - w_base) * ws_row_bytes);
+  const int ws_s0 = s0 * (PREC == kInt4 ? 2 : 4);  // scale bytes per stage and row
+  const __amdgpu_buffer_rsrc_t ws_rs = make_rsrc((const uint8_t*)args.w_scales + (size_t)w_base * ws_row_bytes + ws_s0,
+                                                 PARTIALS ? 0 : (size_t)(N - w_base) * ws_row_bytes - ws_s0);
   // stages past the last read through an empty descriptor: all zeros
   const __amdgpu_buffer_rsrc_t zero_rs = make_rsrc(args.w_codes, 0);
   int w_off[kWP], ws_off[kWP], pa_off[kAP];
@@ -715,38 +725,41 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
           for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmul_rn(acc[i][j][e], t);
     }
     // ---- low-rank up: acc += (lora_act_hi + lora_act_lo) lora_up^T -----------
+    // (split K: in split 0 only)
     if constexpr (RB > 0) {
-      constexpr int rank = RB * 16;
-      const uint16_t* __restrict__ lu = (const uint16_t*)args.lora_up;
+      if (!kSplit || blockIdx.y == 0) {
+        constexpr int rank = RB * 16;
+        const uint16_t* __restrict__ lu = (const uint16_t*)args.lora_up;
 #pragma unroll
-      for (int rs16 = 0; rs16 < RB; ++rs16) {
-        bf16x8 ahi[kIB], alo[kIB], bo[kJB];
+        for (int rs16 = 0; rs16 < RB; ++rs16) {
+          bf16x8 ahi[kIB], alo[kIB], bo[kJB];
 #pragma unroll
-        for (int i = 0; i < kIB; ++i) {
-          const int row = min(m0 + wm * (kIB * 32) + i * 32 + l32, M - 1);
-          const float* la = args.lora_act + (size_t)row * rank + rs16 * 16 + h * 8;
-          const f32x4 v0 = *(const f32x4*)la, v1 = *(const f32x4*)(la + 4);
+          for (int i = 0; i < kIB; ++i) {
+            const int row = min(m0 + wm * (kIB * 32) + i * 32 + l32, M - 1);
+            const float* la = args.lora_act + (size_t)row * rank + rs16 * 16 + h * 8;
+            const f32x4 v0 = *(const f32x4*)la, v1 = *(const f32x4*)(la + 4);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = e < 4 ? v0[e] : v1[e - 4];
-            const __bf16 hb = (__bf16)v;
-            ahi[i][e] = hb;
-            alo[i][e] = (__bf16)(v - (float)hb);
+            for (int e = 0; e < 8; ++e) {
+              const float v = e < 4 ? v0[e] : v1[e - 4];
+              const __bf16 hb = (__bf16)v;
+              ahi[i][e] = hb;
+              alo[i][e] = (__bf16)(v - (float)hb);
+            }
           }
-        }
-#pragma unroll
-        for (int j = 0; j < kJB; ++j) {
-          const int tc = wn * (kJB * 32) + j * 32 + l32;
-          const int col = kQk ? pcol(tc) : min(n0 + tc, N - 1);
-          bo[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(lu + (size_t)col * rank + rs16 * 16 + h * 8));
-        }
-#pragma unroll
-        for (int i = 0; i < kIB; ++i)
 #pragma unroll
           for (int j = 0; j < kJB; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[i], bo[j], acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[i], bo[j], acc[i][j], 0, 0, 0);
+            const int tc = wn * (kJB * 32) + j * 32 + l32;
+            const int col = kQk ? pcol(tc) : min(n0 + tc, N - 1);
+            bo[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(lu + (size_t)col * rank + rs16 * 16 + h * 8));
           }
+#pragma unroll
+          for (int i = 0; i < kIB; ++i)
+#pragma unroll
+            for (int j = 0; j < kJB; ++j) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[i], bo[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[i], bo[j], acc[i][j], 0, 0, 0);
+            }
+        }
       }
     }
     if constexpr (EPI == kEpiGelu) {
@@ -755,6 +768,20 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     } else if constexpr (kQk) {
       qk_norm_rope_epilogue(args, acc, m0, nt, wave, wm, wn, lane, l32, h,
                             wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, (float*)lds_w1);
+    } else if constexpr (kSplit) {
+      // ---- fp32 partials of this split (no bias) ------------------------------
+      float* part = args.partial + (size_t)blockIdx.y * M * N;
+#pragma unroll
+      for (int j = 0; j < kJB; ++j) {
+        const int col = n0 + wn * (kJB * 32) + j * 32 + l32;
+#pragma unroll
+        for (int i = 0; i < kIB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = m0 + wm * (kIB * 32) + i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+            if (row < M && col < N) part[(size_t)row * N + col] = acc[i][j][e];
+          }
+      }
     } else {
       // ---- bias + bf16 store ------------------------------------------------
       const uint16_t* bias = (const uint16_t*)args.bias;
@@ -778,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
 template <int PREC, bool PARTIALS, int EPI>
 static hipError_t dispatch_rank(const GemmArgs& a, hipStream_t s) {
   const unsigned tiles = (unsigned)(((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN));
-  dim3 grid(tiles), block(kThreads);
+  dim3 grid(tiles, EPI == kEpiSplit ? (unsigned)a.ksplit : 1u), block(kThreads);
   if constexpr (PARTIALS) {
     hipLaunchKernelGGL((gemm_w4a4_lora_up_kernel<PREC, 0, true, kEpiStore>), grid, block, 0, s, a);
   } else {
@@ -814,18 +841,58 @@ hipError_t launch_gelu_table_copy(uint16_t* out, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Split K: out[m, n] = bf16(sum_j partial[j, m, n] + bias[n]), the splits
+// added in order (deterministic); 8 columns per thread (N % 64 == 0).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t M,
+                                                            int64_t N, const uint16_t* __restrict__ bias,
+                                                            uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;  // first element
+  if (i >= M * N) return;
+  const int64_t n = i % N;
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+  for (int j = 0; j < ksplit; ++j) {
+    const f32x4* p = (const f32x4*)(partial + (size_t)j * M * N + i);
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc[c] += a[c];
+      acc[4 + c] += b[c];
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float b0 = bias ? bf16_bits_to_f32(bias[n + 2 * c]) : 0.f;
+    const float b1 = bias ? bf16_bits_to_f32(bias[n + 2 * c + 1]) : 0.f;
+    o[c] = f32_to_bf16_bits(acc[2 * c] + b0) | (f32_to_bf16_bits(acc[2 * c + 1] + b1) << 16);
+  }
+  *(u32x4*)(out + i) = o;
+}
+
+hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N, const void* bias, void* out,
+                                hipStream_t stream) {
+  const int64_t threads = M * N / 8;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, partial,
+                     ksplit, M, N, (const uint16_t*)bias, (uint16_t*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream) {
   const bool partials = a.partials != nullptr;
-  const int epi = a.next_act != nullptr ? kEpiGelu : a.heads > 0 ? kEpiQk : kEpiStore;
+  const int epi = a.next_act != nullptr ? kEpiGelu : a.heads > 0 ? kEpiQk : a.ksplit > 1 ? kEpiSplit : kEpiStore;
   if (a.precision == kInt4) {
     if (partials) return dispatch_rank<kInt4, true, kEpiStore>(a, stream);
     if (epi == kEpiGelu) return dispatch_rank<kInt4, false, kEpiGelu>(a, stream);
     if (epi == kEpiQk) return dispatch_rank<kInt4, false, kEpiQk>(a, stream);
+    if (epi == kEpiSplit) return dispatch_rank<kInt4, false, kEpiSplit>(a, stream);
     return dispatch_rank<kInt4, false, kEpiStore>(a, stream);
   }
   if (partials) return dispatch_rank<kNvfp4, true, kEpiStore>(a, stream);
   if (epi == kEpiGelu) return dispatch_rank<kNvfp4, false, kEpiGelu>(a, stream);
   if (epi == kEpiQk) return dispatch_rank<kNvfp4, false, kEpiQk>(a, stream);
+  if (epi == kEpiSplit) return dispatch_rank<kNvfp4, false, kEpiSplit>(a, stream);
   return dispatch_rank<kNvfp4, false, kEpiStore>(a, stream);
 }
 

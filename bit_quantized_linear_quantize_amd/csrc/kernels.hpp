@@ -58,6 +58,11 @@ struct GemmArgs {
   const float* rope_sin = nullptr;  // f32 [M, 64]
   float eps = 0.f;
   int heads = 0;
+  // split K (ksplit > 1, plain linear only): workgroup (tile, j) covers stages
+  // [j per, (j + 1) per) and writes fp32 partials [ksplit, M, N] (the low-rank
+  // term in split 0, no bias); launch_splitk_reduce sums them into out
+  int ksplit = 1;
+  float* partial = nullptr;
 };
 
 struct AwqArgs {
@@ -93,6 +98,9 @@ hipError_t launch_smooth_factors(const SmoothArgs& a, hipStream_t stream);
 hipError_t launch_pack_weight(const PackArgs& a, hipStream_t stream);
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream);
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
+// out[m, n] = bf16(sum_j partial[j, m, n] + bias[n]), j in order
+hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N, const void* bias, void* out,
+                                hipStream_t stream);
 hipError_t launch_gelu_table_copy(uint16_t* out, hipStream_t stream);
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream);
 

@@ -55,7 +55,10 @@ enum svdq_status {
 /* Bytes of scratch svdq_w4a4_linear needs, each part 256-byte aligned: the
  * dequantized activations as fp16 [M, K] (the operand of the product kernel:
  * code times group scale is exact in fp16); for int4 also one fp32
- * power-of-two row factor [M]; and the low-rank activations fp32 [M, rank].
+ * power-of-two row factor [M]; the low-rank activations fp32 [M, rank]; and,
+ * when the 256 x 192 output tiles would fill less than half of the GPU, the
+ * fp32 partial sums [ksplit, M, N] of the product split along K (ksplit <= 8,
+ * a function of M, N and K; the splits are added in a fixed order).
  * Returns 0 for arguments svdq_w4a4_linear would reject. */
 size_t svdq_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision,
                                  int group_size, int rank);
@@ -141,10 +144,12 @@ typedef struct svdq_w4a4_layer {
   int precision, group_size, rank;
 } svdq_w4a4_layer;
 
-/* Bytes of scratch svdq_w4a4_mlp_gelu needs: the up layer's linear workspace
- * (svdq_w4a4_workspace_bytes(M, up->K, up->N, ...)) followed by the down
- * layer's (its fp16 product operand [M, H] and fp32 low-rank activations
- * [M, down->rank]).  Returns 0 for arguments svdq_w4a4_mlp_gelu would reject. */
+/* Bytes of scratch svdq_w4a4_mlp_gelu needs: the up layer's activations,
+ * row factors and low-rank activations (as in svdq_w4a4_workspace_bytes, no
+ * split partials) followed by the down layer's linear workspace (its fp16
+ * product operand [M, H], fp32 low-rank activations [M, down->rank] and, for
+ * small M x N, its split-K partials).  Returns 0 for arguments
+ * svdq_w4a4_mlp_gelu would reject. */
 size_t svdq_w4a4_mlp_workspace_bytes(int64_t M, const svdq_w4a4_layer* up,
                                      const svdq_w4a4_layer* down);
 

@@ -11,6 +11,7 @@ import re
 import pytest
 
 import bit_quantized_linear_quantize_amd as bq
+from split_rule import ksplit, split_bytes
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "svdq_w4a4.h")
@@ -146,13 +147,24 @@ def test_wtscale_rules(L):
     assert Args(precision=1, group=16).call(L, wt=float("inf")) == EINVAL
 
 
+def test_split_rule():
+    assert ksplit(4096, 3072, 3072) == 1          # 256 tiles
+    assert ksplit(512, 3072, 3072) == 8           # 32 tiles
+    assert ksplit(1024, 3072, 3072) == 4          # 64 tiles
+    assert ksplit(300, 320, 512) == 4             # 4 tiles, 8 stages
+    assert ksplit(64, 64, 128) == 1               # 2 stages
+    assert ksplit(64, 64, 576) == 3               # 9 stages: 4 splits of 3 would leave one empty
+
+
 def test_workspace_size(L):
     M, K, N = 300, 512, 320
     rnd = lambda v: (v + 255) // 256 * 256
     # fp16 activations [M, K]; int4 adds a row factor [M]; then lora_act
-    # fp32 [M, 32]
-    want = {0: rnd(2 * M * K) + rnd(4 * M) + rnd(M * 32 * 4),
-            1: rnd(2 * M * K) + rnd(M * 32 * 4)}
+    # fp32 [M, 32]; then the split-K partials fp32 [ksplit, M, N]
+    want = {0: rnd(2 * M * K) + rnd(4 * M) + rnd(M * 32 * 4) + split_bytes(M, N, K),
+            1: rnd(2 * M * K) + rnd(M * 32 * 4) + split_bytes(M, N, K)}
+    assert split_bytes(M, N, K) > 0
+    assert L.svdq_w4a4_workspace_bytes(4096, 3072, 3072, 1, 16, 32) == rnd(2 * 4096 * 3072) + rnd(4096 * 32 * 4)
     for prec, g in ((0, 64), (1, 16)):
         need = L.svdq_w4a4_workspace_bytes(M, K, N, prec, g, 32)
         assert need == want[prec]
@@ -215,8 +227,9 @@ def test_mlp_rules(L):
     B = ctypes.byref
     need = L.svdq_w4a4_mlp_workspace_bytes(M, B(up), B(down))
     rnd = lambda v: (v + 255) // 256 * 256
-    # the up layer's linear workspace (int4: operand, row factors, lora_act), then the down layer's
-    assert need == (rnd(2 * M * K) + rnd(4 * M) + rnd(4 * M * 32)) + (rnd(2 * M * H) + rnd(4 * M * 32))
+    # the up layer's operand, row factors and lora_act, then the down layer's linear workspace
+    assert need == (rnd(2 * M * K) + rnd(4 * M) + rnd(4 * M * 32)) + (rnd(2 * M * H) + rnd(4 * M * 32) +
+                                                                      split_bytes(M, N, H))
 
     def call(x=x, M=M, up=up, down=down, out=out, ws=ws, wsb=need, arch=GFX950):
         p = lambda v: None if v is None else _fake(v)
@@ -243,7 +256,8 @@ def test_qkv_rules(L):
     qn, kn, cs, sn = 0x6_0000_0000, 0x6_0001_0000, 0x7_0000_0000, 0x8_0000_0000
     qkv = _layer(0x1_0000_0000, K, N, precision=1)
     B = ctypes.byref
-    need = L.svdq_w4a4_workspace_bytes(M, K, N, 1, 16, 32)
+    # the linear's activations and lora_act (no split partials: the epilogue is not split)
+    need = (2 * M * K + 255) // 256 * 256 + (M * 32 * 4 + 255) // 256 * 256
 
     def call(x=x, M=M, qkv=qkv, heads=H, hd=128, qn=qn, kn=kn, eps=1e-6, cs=cs, sn=sn, out=out, ws=ws,
              wsb=need, arch=GFX950):
@@ -251,7 +265,7 @@ def test_qkv_rules(L):
         return L.svdq_w4a4_qkv_rmsnorm_rope_check(p(x), M, B(qkv) if qkv is not None else None, heads, hd, p(qn),
                                                   p(kn), eps, p(cs), p(sn), p(out), p(ws), wsb, arch)
     assert call() == OK
-    assert call(qkv=_layer(0x1_0000_0000, K, N, precision=0), wsb=L.svdq_w4a4_workspace_bytes(M, K, N, 0, 64, 32)) == OK
+    assert call(qkv=_layer(0x1_0000_0000, K, N, precision=0), wsb=need + (4 * M + 255) // 256 * 256) == OK
     assert call(hd=64) == EUNSUP                    # head_dim 128 only
     assert call(heads=3) == EINVAL                  # N != 3 heads head_dim
     assert call(heads=0) == EINVAL
