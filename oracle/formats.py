@@ -190,3 +190,29 @@ def bf16_bits_f64(x):
     r = np.where(sub, np.rint(x * 2.0 ** 133) * 2.0 ** -133, r)
     r = np.where(r == 0, np.copysign(0.0, x), r)
     return bf16_bits(r.astype(F32))
+
+
+# ----------------------------------------------------------------------------
+# IEEE binary16 (the matrix-instruction operand format of the GPU path)
+# ----------------------------------------------------------------------------
+F16_MAX = 65504.0
+
+
+def f16_round(x):
+    """float64 -> the nearest IEEE binary16 value (round half to even),
+    returned as float64.  Finite inputs with |x| below 65520 (the rounding
+    boundary of the largest finite value) only.
+
+    From the format definition: 11 significant bits for normal values
+    (|x| >= 2^-14), written as m * 2^e with 0.5 <= |m| < 1 and m scaled by
+    2^11 (exact) and rounded with ``np.rint``; below 2^-14 the fixed quantum
+    of the subnormals, 2^-24.  The sign of zero is kept.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) >= 65520.0):
+        raise ValueError("f16_round: input outside the finite binary16 range")
+    m, e = np.frexp(x)
+    r = np.ldexp(np.rint(m * 2048.0), e - 11)
+    sub = np.abs(x) < 2.0 ** -14
+    r = np.where(sub, np.rint(x * 2.0 ** 24) * 2.0 ** -24, r)
+    return np.where(r == 0, np.copysign(0.0, x), r)

@@ -38,7 +38,7 @@ W_deq = (q - z) * s, fp64 accumulation.
 import numpy as np
 
 from .formats import (F32, bf16_bits, bf16_bits_f64, bf16_to_f32, e4m3_decode,
-                      e2m1_decode, pack_nibbles, nibble_to_int4)
+                      e2m1_decode, f16_round, pack_nibbles, nibble_to_int4)
 from .quant import (quantize_int4, quantize_nvfp4_act, quantize_nvfp4_weight,
                     quantize_awq)
 
@@ -134,6 +134,43 @@ def svdq_quantize_act(x_bits, smooth_bits, lora_down_bits, precision):
     down = bf16_to_f32(lora_down_bits).astype(np.float64)
     lora_act = xhat.astype(np.float64) @ down.T if down.shape[0] else np.zeros((xhat.shape[0], 0))
     return dict(codes=nib, packed=pack_nibbles(nib), scales=scales, lora_act=lora_act, xhat=xhat)
+
+
+def product_operand_ref(codes, scales, precision):
+    """The dequantized activations as the product kernel receives them: each
+    value code * group scale held as an IEEE binary16, int4 rows rescaled by
+    one power of two 2^-E[m] so that they fit binary16.
+
+    Reading (the pages fix no operand format; this is the library's own
+    encoding of the activation codes and group scales, defined here value by
+    value):
+      nvfp4: value = e2m1 * dec(s8), always an exact binary16 (|v| <= 2688,
+             nonzero |v| >= 2^-10); no row factor (None is returned).
+      int4:  with s_max the row's largest group scale and s_min its smallest
+             nonzero one, E = 0 if s_max < 2^13 and s_min >= 2^-17 (then
+             every q * s is an exact binary16) or the row is all zero;
+             otherwise E = floor(log2 s_max) - 12.  value =
+             f16(q * f16(s * 2^-E)) -- exact for every group within 2^29 of
+             s_max, rounded (each step to nearest even) below that.  The row
+             factor 2^E is returned as float64 [R].
+
+    codes [R, K] nibbles; scales as returned by the quantizers ([R, K/G]).
+    Returns (values float64 [R, K], row factor float64 [R] or None).
+    """
+    G = GROUP[precision]
+    q = _code_values(codes, precision)
+    s = _scale_values(scales, precision)
+    R, K = q.shape
+    if precision == "nvfp4":
+        return (q.reshape(R, K // G, G) * s[..., None]).reshape(R, K), None
+    smax = s.max(axis=1)
+    smin = np.where(s > 0, s, np.inf).min(axis=1)
+    fits = (smax < 2.0 ** 13) & (smin >= 2.0 ** -17)
+    _, e = np.frexp(np.where(smax > 0, smax, 1.0))  # smax in [2^(e-1), 2^e)
+    E = np.where(fits | (smax == 0), 0, (e - 1) - 12).astype(np.int64)
+    s16 = f16_round(np.ldexp(s, -E[:, None]))
+    vals = f16_round(q.reshape(R, K // G, G) * s16[..., None]).reshape(R, K)
+    return vals, np.ldexp(1.0, E)
 
 
 def _code_values(codes, precision):
@@ -292,10 +329,14 @@ def awq_linear_ref(x_bits, layer):
 # error metrics used by the parity tests
 # ----------------------------------------------------------------------------
 def bf16_half_ulp(y):
-    """Half a bfloat16 ulp at |y| (float64), the size of the final rounding."""
+    """Half the bfloat16 spacing at |y| (float64): the largest error of
+    rounding y to bfloat16.  bfloat16 has 8 significant bits, so in the
+    binade [2^e, 2^(e+1)) its spacing is 2^(e-7); below 2^-126 the spacing of
+    its subnormals, 2^-133.  The binade comes from ``np.frexp`` (exact: a
+    value just below a power of two stays in the lower binade)."""
     a = np.abs(np.asarray(y, dtype=np.float64))
-    e = np.floor(np.log2(np.where(a > 0, a, 2.0 ** -126)))
-    e = np.maximum(e, -126)
+    _, e = np.frexp(a)  # a = m 2^e, 0.5 <= m < 1: a lies in [2^(e-1), 2^e)
+    e = np.maximum(np.where(a > 0, e - 1, -126), -126)
     return np.ldexp(1.0, (e - 8).astype(np.int64))
 
 
