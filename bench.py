@@ -31,9 +31,15 @@ Also measured in the same run (reported under "extra"):
     timed from a replayed graph), 8 passes (--no-stack skips it); also with
     the per-head RMSNorm and RoPE of q and k as torch ops, and with the QKV
     and MLP fusions.
-The weights of the timed legs are random but valid packed layers (prepared
-weight values do not change the work); parity with the oracle is the job of
-tests/.  The cpu_baseline leg times the CPU oracle on the same inputs.
+The headline int4 and nvfp4 legs run on the config-1 layer itself, prepared on
+the GPU by this library (smoothing calibrated on X, rank-32 split, residual
+packing) from the synthetic config-1 weight; the other legs use random but
+valid packed layers of their shapes (values do not change the work they do).
+Parity with the oracle is the job of tests/.  Before the counted warm-up steps
+every timed leg runs for a fixed wall time (--warm-seconds) so that the GPU
+clock has settled whatever --warmup is.  The cpu_baseline leg times the CPU
+oracle on bounded samples of configs 1-4 (config 4 extrapolated from one
+block's layers).
 """
 
 import argparse
@@ -331,6 +337,20 @@ def bench_mfma_peak(torch, stream, iters=20000):
             "published_dense_peak_TFLOPs": PEAK["f16"], "workgroups": blocks, "rounds_per_wave": iters}
 
 
+def warm_clock(fn, seconds, torch):
+    """Run fn back to back for at least `seconds` of wall time (the GPU clock
+    ramps up under sustained load); returns the calls made."""
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while True:
+        for _ in range(16):
+            fn()
+        n += 16
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
 def time_events(fn, steps, stream):
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
@@ -375,7 +395,7 @@ ONLY_LEGS = {"quant_int4", "quant_nvfp4", "gemm_int4", "gemm_nvfp4", "awq_m1", "
 
 def run_only(leg, steps):
     """Launch a single kernel of the headline workload `steps` times (after one
-    warm-up call), for per-kernel hardware-counter passes.  `mlp_fused` is the
+    warm-up call), for per-kernel hardware-counter passes and kernel traces.  `mlp_fused` is the
     fused GELU MLP pair (nvfp4, M=4096, 3072 -> 12288 -> 3072, rank 32);
     `qkv_fused` the QKV projection 3072 -> 9216 with RMSNorm + RoPE (nvfp4).
     `copy` is a plain device-to-device copy of 256 MiB, the reference for
@@ -426,10 +446,13 @@ def run_only(leg, steps):
         y = torch.empty((M, Nq), dtype=torch.bfloat16, device="cuda")
         fn = lambda: bq.svdq_w4a4_qkv_rmsnorm_rope(x, layer, heads, qn, kn, cos, sin, out=y, workspace=ws)
     else:
+        # the headline legs' layer: the synthetic config-1 weight prepared on the GPU
         precision = "int4" if leg.endswith("int4") else "nvfp4"
-        rx, rl = S.streams(0, 2)
-        x = torch.from_numpy(S.activations(M, K, round(0.01 * K), rx).view(np.int16).copy()).view(torch.bfloat16).cuda()
-        layer = bq.SVDQLinear.from_numpy(S.random_svdq_layer(N, K, precision, rank, rl))
+        c1 = S.config1()
+        x = torch.from_numpy(c1["x"].view(np.int16).copy()).view(torch.bfloat16).cuda()
+        w1 = torch.from_numpy(c1["w"].astype(np.float32)).cuda()
+        b1 = torch.from_numpy(c1["bias"].view(np.int16).copy()).view(torch.bfloat16).cuda()
+        layer = bq.prepare_layer(w1, x, rank, precision, bias=b1)
         ws = torch.empty(layer.workspace_bytes(M), dtype=torch.uint8, device="cuda")
         bq.svdq_w4a4_quantize(x, layer, ws)
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
@@ -445,13 +468,95 @@ def run_only(leg, steps):
     log(f"ran {leg} x{steps}")
 
 
+def layer_numpy(layer):
+    """The oracle's dict form of a device SVDQLinear (bf16 as uint16 bits)."""
+    import numpy as np
+    import torch
+    from oracle import formats as F
+
+    def bits(t):
+        return None if t is None else t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    p = layer.precision
+    ws = bits(layer.wscales) if p == "int4" else layer.wscales.cpu().numpy()
+    packed = layer.packed_w.cpu().numpy()
+    return dict(precision=p, rank=layer.rank, packed_w=packed, w_codes=F.unpack_nibbles(packed), wscales=ws,
+                wtscale=layer.wtscale, smooth=bits(layer.smooth),
+                lora_down=bits(layer.lora_down) if layer.rank else np.zeros((0, layer.K), np.uint16),
+                lora_up=bits(layer.lora_up) if layer.rank else np.zeros((layer.N, 0), np.uint16),
+                bias=bits(layer.bias))
+
+
+def cpu_baselines(S, np, x_bits, layers, budget):
+    """The CPU oracle (numpy / OpenBLAS fp64) timed on bounded samples of
+    configs 1-4: for each, calls repeat until about `budget` seconds (at least
+    one), and the rate is scaled to the config's full workload."""
+    from oracle import formats as F, layers as L
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+
+    def timed(fn, budget_s):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                return (time.perf_counter() - t0) / reps, reps
+    M, K = x_bits.shape
+    N = layers["int4"]["N"]
+    out = {}
+    for p in ("int4", "nvfp4"):
+        dt, reps = timed(lambda: L.svdq_linear_ref(x_bits, layers[p]), budget)
+        out[f"config_{1 if p == 'int4' else 2}_{p}"] = {
+            "value": round(2.0 * M * N * K / dt / 1e12, 6), "unit": "TOPS", "seconds_per_call": round(dt, 3),
+            "sample": f"the full workload ({M}x{K} activations, {N}x{K} {p} layer, rank 32), {reps} calls"}
+    # config 3: AWQ adaLN linear 3072 -> 18432 at M = 1, 2, 16
+    ra = S.streams(7, 2)
+    awq = S.random_awq_layer(18432, 3072, ra[0])
+    awq = dict(awq, q=F.unpack_nibbles(awq["packed_w"]), group_size=64)
+    for Ma in (1, 2, 16):
+        xa = S.activations(Ma, 3072, 0, ra[1])
+        dt, reps = timed(lambda: L.awq_linear_ref(xa, awq), budget / 4)
+        nbytes = 18432 * 3072 // 2 + 2 * 18432 * 48 * 2 + Ma * 3072 * 2 + Ma * 18432 * 2 + 18432 * 2
+        out[f"config_3_awq_M{Ma}"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s",
+                                      "seconds_per_call": round(dt, 4),
+                                      "sample": f"the full layer 18432x3072 at M={Ma}, {reps} calls"}
+    # config 4: one block's layers at full size, extrapolated to 24 blocks x 8 passes
+    # (identical work per block and pass)
+    rows = S.STACK["tokens"]
+    rs = S.streams(13, len(S.STACK_LAYERS) + 1)
+    blk, ops = 0.0, 0.0
+    for i, (name, Kl, Nl) in enumerate(S.STACK_LAYERS):
+        lay = S.random_svdq_layer(Nl, Kl, "nvfp4", 32, rs[i])
+        lay = dict(lay, w_codes=F.unpack_nibbles(lay["packed_w"]))
+        xl = S.activations(rows, Kl, round(0.01 * Kl), rs[-1])
+        dt, _ = timed(lambda: L.svdq_linear_ref(xl, lay), 0.0)
+        blk += dt
+        ops += 2.0 * rows * Nl * Kl
+    xa = S.activations(1, 3072, 0, ra[1])
+    dt, _ = timed(lambda: L.awq_linear_ref(xa, awq), 0.0)
+    blk += dt
+    passes, blocks = S.STACK["passes"], S.STACK["blocks"]
+    out["config_4_stack"] = {"value": round(ops / blk / 1e12, 6), "unit": "TOPS (svdq layers, block incl. adaLN)",
+                             "extrapolated": True, "block_s": round(blk, 2), "pass_s": round(blk * blocks, 1),
+                             "eight_passes_s": round(blk * blocks * passes, 1),
+                             "sample": f"one block: its QKV, out, up and down linears (nvfp4, rank 32, {rows} "
+                                       f"tokens) and its adaLN AWQ linear at M=1, one call each; the pass is "
+                                       f"{blocks} such blocks and the config {passes} passes"}
+    return out, threads
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=1000,
-                    help="untimed steps first; about 0.1 s, enough for the GPU clock to settle")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps after the wall-time warm-up")
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="wall time each timed leg runs untimed first, for the GPU clock to settle")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-budget", type=float, default=4.0, help="seconds of CPU oracle work per config sample")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the nvfp4, AWQ, MLP-pair and DiT-stack legs")
     ap.add_argument("--no-stack", action="store_true", help="skip the DiT-stack leg")
@@ -480,20 +585,27 @@ def main():
     log(f"device {props.name} {getattr(props, 'gcnArchName', '')}")
 
     M, K, N, rank = 4096, 3072, 3072, 32
-    rx, rl4, rl8 = S.streams(0, 3)
-    x_bits = S.activations(M, K, round(0.01 * K), rx)
+    c1 = S.config1()
+    x_bits = c1["x"]
     x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    w1 = torch.from_numpy(c1["w"].astype(np.float32)).cuda()
+    b1 = torch.from_numpy(c1["bias"].view(np.int16).copy()).view(torch.bfloat16).cuda()
     ops = 2.0 * M * N * K
+    log("preparing the config-1 layer on the GPU (int4 and nvfp4) ...")
+    t0 = time.perf_counter()
+    layers = {p: bq.prepare_layer(w1, x, rank, p, bias=b1) for p in ("int4", "nvfp4")}
+    torch.cuda.synchronize()
+    prep_s = (time.perf_counter() - t0) / 2
 
-    def bench_svdq(precision, rng, steps, warmup):
-        lay_np = S.random_svdq_layer(N, K, precision, rank, rng)
-        layer = bq.SVDQLinear.from_numpy(lay_np)
+    def bench_svdq(precision, steps, warmup):
+        layer = layers[precision]
         ws = torch.empty(layer.workspace_bytes(M), dtype=torch.uint8, device="cuda")
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         G = bq.GROUP_SIZE[precision]
         step = lambda: layer(x, out=out, workspace=ws)
         k1 = lambda: bq.svdq_w4a4_quantize(x, layer, ws)
         k2 = lambda: bq.svdq_w4a4_gemm(ws, M, layer, out=out)
+        warm_clock(step, args.warm_seconds, torch)
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
@@ -509,10 +621,10 @@ def main():
         # algorithmic bytes of kernel 1: read x, smooth, lora_down; write 4-bit codes
         # (counted at 4 bits although the workspace keeps fp16 operands), scales, lora_act
         k1_bytes = M * K * 2 + K * 2 + rank * K * 2 + M * K // 2 + M * (K // G) * sb + M * rank * 4
-        return dict(ms=ms, k1_ms=t1, k2_ms=t2, k1_bytes=k1_bytes, lay=lay_np)
+        return dict(ms=ms, k1_ms=t1, k2_ms=t2, k1_bytes=k1_bytes)
 
     log("timing svdq_w4a4 int4 ...")
-    r4 = bench_svdq("int4", rl4, args.steps, args.warmup)
+    r4 = bench_svdq("int4", args.steps, args.warmup)
     value = ops / (r4["ms"] * 1e-3) / 1e12
     k2_tops = ops / (r4["k2_ms"] * 1e-3) / 1e12
     # the product runs on fp16 matrix instructions (int4 code x group scale is an
@@ -528,11 +640,12 @@ def main():
                       "quantize_act_lora_down_us": round(r4["k1_ms"] * 1e3, 2),
                       "quantize_act_lora_down_GBps": round(r4["k1_bytes"] / (r4["k1_ms"] * 1e-3) / 1e9, 1),
                       "gemm_w4a4_lora_up_us": round(r4["k2_ms"] * 1e3, 2),
-                      "gemm_w4a4_lora_up_TOPS": round(k2_tops, 1)}}
+                      "gemm_w4a4_lora_up_TOPS": round(k2_tops, 1)},
+             "config1_layer_prepared_on_gpu_s": round(prep_s, 3)}
 
     if not args.no_extra:
         log("timing svdq_w4a4 nvfp4 ...")
-        r8 = bench_svdq("nvfp4", rl8, args.steps, args.warmup)
+        r8 = bench_svdq("nvfp4", args.steps, args.warmup)
         k2n = ops / (r8["k2_ms"] * 1e-3) / 1e12
         extra["nvfp4"] = {"value_TOPS": round(ops / (r8["ms"] * 1e-3) / 1e12, 1),
                           "step_us": round(r8["ms"] * 1e3, 2),
@@ -546,12 +659,11 @@ def main():
         # 32 of the 256 x 192 tiles, so 1/8 of the CUs get work
         log("timing the M=512 token shard ...")
         xs = x[:512].contiguous()
-        lay_s = bq.SVDQLinear.from_numpy(r4["lay"])
+        lay_s = layers["int4"]
         ws_s = torch.empty(lay_s.workspace_bytes(512), dtype=torch.uint8, device="cuda")
         out_s = torch.empty((512, N), dtype=torch.bfloat16, device="cuda")
         f_s = lambda: lay_s(xs, out=out_s, workspace=ws_s)
-        for _ in range(50):
-            f_s()
+        warm_clock(f_s, args.warm_seconds / 4, torch)
         t_s = time_graph(f_s, 200, stream)
         if t_s is None:
             t_s = time_events(f_s, 200, stream)
@@ -561,7 +673,7 @@ def main():
         log("timing awq_w4a16 ...")
         Na, Ka, copies = 18432, 3072, 12
         ra = S.streams(7, copies + 1)
-        layers = [bq.AWQLinear.from_numpy(S.random_awq_layer(Na, Ka, ra[i])) for i in range(copies)]
+        awq_layers = [bq.AWQLinear.from_numpy(S.random_awq_layer(Na, Ka, ra[i])) for i in range(copies)]
         awq = {}
         for Ma in (1, 2, 16):
             xa = torch.from_numpy(S.activations(Ma, Ka, 0, ra[-1]).view(np.int16).copy()).view(torch.bfloat16).cuda()
@@ -569,10 +681,9 @@ def main():
             it = [0]
 
             def call():
-                layers[it[0] % copies](xa, out=oa)
+                awq_layers[it[0] % copies](xa, out=oa)
                 it[0] += 1
-            for _ in range(2 * copies):
-                call()
+            warm_clock(call, args.warm_seconds / 4, torch)
 
             def seq():  # 4 rounds over the rotating copies
                 for _ in range(4 * copies):
@@ -587,7 +698,7 @@ def main():
             awq[f"M={Ma}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
                               "frac_of_hbm": round(gbps / PEAK["hbm"], 4), "bytes": nbytes}
         extra["awq_w4a16_N18432_K3072"] = awq
-        del layers
+        del awq_layers
         torch.cuda.empty_cache()
 
         peak = bench_mfma_peak(torch, stream)
@@ -606,36 +717,27 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle ...")
-        from oracle import formats as F, layers as L
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-        except Exception:
-            threads = os.cpu_count()
-        lay = dict(r4["lay"])
-        lay["w_codes"] = F.unpack_nibbles(lay["packed_w"])
-        rows = M
-        reps, t0 = 0, time.perf_counter()
-        while True:  # the full workload, repeated for ~10 s of CPU work
-            L.svdq_linear_ref(x_bits[:rows], lay)
-            reps += 1
-            if time.perf_counter() - t0 >= 10.0 or reps >= 50:
-                break
-        dt = (time.perf_counter() - t0) / reps
-        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TOPS", "cores": threads,
-               "kind": "oracle", "seconds_per_call": round(dt, 3), "calls": reps,
-               "sample": f"the full workload ({rows}x{K} activations, {N}x{K} int4 layer, rank {rank}), "
-                         f"{reps} calls: activation quantizer + fp64 dequantized GEMM + low-rank + bias "
-                         "(numpy/OpenBLAS)"}
+        lays = {p: layer_numpy(layers[p]) for p in ("int4", "nvfp4")}
+        for p in lays:
+            lays[p]["N"] = N
+        per, threads = cpu_baselines(S, np, x_bits, lays, args.cpu_budget)
+        head = per["config_1_int4"]
+        cpu = {"value": head["value"], "unit": "TOPS", "cores": threads, "kind": "oracle",
+               "seconds_per_call": head["seconds_per_call"],
+               "sample": head["sample"] + ": activation quantizer + fp64 dequantized GEMM + low-rank + bias "
+                                          "(numpy/OpenBLAS); other configs under per_config",
+               "per_config": per}
 
     rec = {"metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r4["ms"], 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
            "data": "synthetic",
            "config": {"workload": "svdq_w4a4 int4 linear, M=4096 K=N=3072, rank 32, group 64 "
-                                  "(DiT attention projection, 1% outlier channels)",
+                                  "(DiT attention projection, 1% outlier channels; the synthetic config-1 "
+                                  "weight prepared on the GPU)",
                       "M": M, "K": K, "N": N, "rank": rank, "group_size": 64, "precision": "int4",
                       "parallelism": "none (1 GPU)"},
+           "warmup_wall_s_per_leg": args.warm_seconds,
            "roofline": roofline, "cpu_baseline": cpu, "extra": extra}
     print(json.dumps(rec), flush=True)
 

@@ -18,7 +18,7 @@ LIB = os.path.join(LIBDIR, "libsvdq_w4a4.so")
 PEAK_LIB = os.path.join(LIBDIR, "libsvdq_peak.so")
 PEAK_SOURCES = ["mfma_peak.hip"]
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["api.cpp", "quantize_act.hip", "gemm_w4a4.hip", "awq_gemv.hip", "weight_prep.hip"]
+SOURCES = ["api.cpp", "quantize_act.hip", "gemm_w4a4.hip", "awq_gemv.hip", "weight_prep.hip", "prep_svd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -21,11 +21,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -369,6 +371,251 @@ int validate_qkv(const void* x, int64_t M, const svdq_w4a4_layer* qkv, int heads
   return SVDQ_OK;
 }
 
+
+// ---- offline preparation: the rank-r split -------------------------------------
+// A randomized range finder with subspace iteration (Halko, Martinsson and
+// Tropp, "Finding structure with randomness", 2011, Algorithms 4.3 / 4.4):
+// the products with the weight run on the GPU (prep_svd.hip); the l x l
+// factorizations (l = rank + oversampling) run here in fp64, after a copy of
+// the l x l Gram matrix to the host.
+
+constexpr int64_t kMaxPrepN = int64_t(1) << 20;
+constexpr int kMaxOversample = 32;
+constexpr int kMaxPowerIters = 16;
+
+// row slices of an A^T B product with C columns (about 512 workgroups)
+int prep_slices(int64_t R, int64_t C) {
+  const int64_t chunks = (C + 63) / 64;
+  int64_t s = std::max<int64_t>(1, 512 / chunks);
+  s = std::min<int64_t>(s, 32);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, R / 32));
+  return int(s);
+}
+
+// Workspace of svdq_w4a4_prepare_weight, each part 256-byte aligned.
+struct PrepCarve {
+  uint32_t* amax;   // u32 [2K]  column / tensor maxima
+  double* omega;    // [K, l]    Gaussian test matrix
+  double* y;        // [N, l]
+  double* q;        // [N, l]
+  double* tmp;      // [max(N, K), l]
+  double* z;        // [K, l]
+  double* zq;       // [K, l]
+  double* part;     // [slices, C, l] partial sums of A^T B
+  double* g;        // [l, l]
+  double* small;    // [l, l]      small right factors uploaded from the host
+  double* up64;     // [N, rank]
+  double* dt64;     // [K, rank]
+  float* resid;     // [N, K]
+};
+
+size_t prep_part_elems(int64_t N, int64_t K, int l) {
+  const int64_t R = std::max(N, K);
+  const int64_t a = int64_t(prep_slices(N, K)) * K, b = int64_t(prep_slices(K, N)) * N;
+  const int64_t c = int64_t(prep_slices(R, l)) * l;
+  return size_t(std::max(std::max(a, b), c)) * size_t(l);
+}
+
+size_t prep_carve(void* base, int64_t N, int64_t K, int rank, int l, PrepCarve* c) {
+  uint8_t* p = static_cast<uint8_t*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + off : nullptr;
+    off += round_up(bytes);
+    return r;
+  };
+  const size_t d = sizeof(double);
+  PrepCarve t{};
+  t.amax = static_cast<uint32_t*>(take(size_t(K) * 8));
+  if (rank > 0) {
+    t.omega = static_cast<double*>(take(size_t(K) * l * d));
+    t.y = static_cast<double*>(take(size_t(N) * l * d));
+    t.q = static_cast<double*>(take(size_t(N) * l * d));
+    t.tmp = static_cast<double*>(take(size_t(std::max(N, K)) * l * d));
+    t.z = static_cast<double*>(take(size_t(K) * l * d));
+    t.zq = static_cast<double*>(take(size_t(K) * l * d));
+    t.part = static_cast<double*>(take(prep_part_elems(N, K, l) * d));
+    t.g = static_cast<double*>(take(size_t(l) * l * d));
+    t.small = static_cast<double*>(take(size_t(l) * l * d));
+    t.up64 = static_cast<double*>(take(size_t(N) * rank * d));
+    t.dt64 = static_cast<double*>(take(size_t(K) * rank * d));
+  }
+  t.resid = static_cast<float*>(take(size_t(N) * size_t(K) * 4));
+  if (c) *c = t;
+  return off;
+}
+
+// Upper Cholesky factor Rm (l x l, row-major) of G + shift I.  A pivot not
+// above 1e-13 of its diagonal entry marks a column that depends on the
+// earlier ones: it is dropped (keep = 0, its row of Rm zero).
+void chol_upper(const std::vector<double>& G, int l, double shift, std::vector<double>& Rm,
+                std::vector<char>& keep) {
+  Rm.assign(size_t(l) * l, 0.0);
+  keep.assign(l, 0);
+  for (int i = 0; i < l; ++i) {
+    const double gii = G[size_t(i) * l + i] + shift;
+    double d = gii;
+    for (int m = 0; m < i; ++m)
+      if (keep[m]) d -= Rm[size_t(m) * l + i] * Rm[size_t(m) * l + i];
+    if (!(gii > 0.0) || !(d > 1e-13 * gii)) continue;
+    keep[i] = 1;
+    const double rii = std::sqrt(d);
+    Rm[size_t(i) * l + i] = rii;
+    for (int j = i + 1; j < l; ++j) {
+      double v = G[size_t(i) * l + j];
+      for (int m = 0; m < i; ++m)
+        if (keep[m]) v -= Rm[size_t(m) * l + i] * Rm[size_t(m) * l + j];
+      Rm[size_t(i) * l + j] = v / rii;
+    }
+  }
+}
+
+// T = Rm^-1 on the kept rows and columns (upper triangular), zero elsewhere
+void inv_upper(const std::vector<double>& Rm, const std::vector<char>& keep, int l, std::vector<double>& T) {
+  T.assign(size_t(l) * l, 0.0);
+  for (int j = 0; j < l; ++j) {
+    if (!keep[j]) continue;
+    T[size_t(j) * l + j] = 1.0 / Rm[size_t(j) * l + j];
+    for (int i = j - 1; i >= 0; --i) {
+      if (!keep[i]) continue;
+      double v = 0.0;
+      for (int m = i + 1; m <= j; ++m)
+        if (keep[m]) v += Rm[size_t(i) * l + m] * T[size_t(m) * l + j];
+      T[size_t(i) * l + j] = -v / Rm[size_t(i) * l + i];
+    }
+  }
+}
+
+struct PrepCtx {
+  hipStream_t s;
+  int l;
+  PrepCarve c;
+};
+
+int prep_status(hipError_t e, const char* what) {
+  return e == hipSuccess ? SVDQ_OK : fail(SVDQ_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Device X [R, l] -> Qo [R, l] with orthonormal columns (dependent columns
+// zero) and, if Rf is given, the upper triangular Rf [l, l] with X = Qo Rf:
+// shifted CholeskyQR followed by two CholeskyQR passes (Fukaya, Kannan,
+// Nakatsukasa, Yamamoto and Yanagisawa, "Shifted Cholesky QR for computing
+// the QR factorization of ill-conditioned matrices", 2020).  X may not be Qo
+// or the context's tmp buffer.
+int prep_orth(PrepCtx& x, const double* X, int64_t R, double* Qo, std::vector<double>* Rf) {
+  const int l = x.l;
+  std::vector<double> G(size_t(l) * l), Rm, T, acc;
+  std::vector<char> keep;
+  if (Rf) {
+    acc.assign(size_t(l) * l, 0.0);
+    for (int i = 0; i < l; ++i) acc[size_t(i) * l + i] = 1.0;
+  }
+  const double* cur = X;
+  double* const dst[3] = {Qo, x.c.tmp, Qo};
+  svdq::PrepSrc src;
+  for (int pass = 0; pass < 3; ++pass) {
+    src.dense = cur;
+    int rc = prep_status(svdq::launch_prep_atb(src, R, l, cur, l, prep_slices(R, l), x.c.part, x.c.g, x.s),
+                         "Gram matrix launch");
+    if (rc) return rc;
+    rc = prep_status(hipMemcpyAsync(G.data(), x.c.g, G.size() * sizeof(double), hipMemcpyDeviceToHost, x.s),
+                     "Gram matrix copy");
+    if (rc) return rc;
+    rc = prep_status(hipStreamSynchronize(x.s), "stream synchronize");
+    if (rc) return rc;
+    double shift = 0.0;
+    if (pass == 0) {
+      double tr = 0.0;
+      for (int i = 0; i < l; ++i) tr += G[size_t(i) * l + i];
+      shift = 11.0 * (double(R) * l + double(l) * (l + 1)) * 0x1p-53 * tr;
+    }
+    chol_upper(G, l, shift, Rm, keep);
+    inv_upper(Rm, keep, l, T);
+    rc = prep_status(hipMemcpyAsync(x.c.small, T.data(), T.size() * sizeof(double), hipMemcpyHostToDevice, x.s),
+                     "factor copy");
+    if (rc) return rc;
+    rc = prep_status(svdq::launch_prep_ab(src, R, l, x.c.small, l, dst[pass], x.s), "CholeskyQR product launch");
+    if (rc) return rc;
+    // the host T must outlive its copy
+    rc = prep_status(hipStreamSynchronize(x.s), "stream synchronize");
+    if (rc) return rc;
+    if (Rf) {  // acc = Rm acc
+      std::vector<double> nxt(size_t(l) * l, 0.0);
+      for (int i = 0; i < l; ++i)
+        for (int m = i; m < l; ++m) {
+          const double r = Rm[size_t(i) * l + m];
+          if (r == 0.0) continue;
+          for (int j = 0; j < l; ++j) nxt[size_t(i) * l + j] += r * acc[size_t(m) * l + j];
+        }
+      acc.swap(nxt);
+    }
+    cur = dst[pass];
+  }
+  if (Rf) Rf->swap(acc);
+  return SVDQ_OK;
+}
+
+// One-sided Jacobi SVD (Hestenes) of the l x l row-major A: A = U diag(sig)
+// V^T, singular values in descending order.  Columns of A are rotated in
+// pairs until every pair is orthogonal to 1e-15 of the product of their norms.
+void jacobi_svd(std::vector<double> A, int l, std::vector<double>& U, std::vector<double>& sig,
+                std::vector<double>& V) {
+  V.assign(size_t(l) * l, 0.0);
+  for (int i = 0; i < l; ++i) V[size_t(i) * l + i] = 1.0;
+  for (int sweep = 0; sweep < 60; ++sweep) {
+    bool rotated = false;
+    for (int p = 0; p < l - 1; ++p)
+      for (int q = p + 1; q < l; ++q) {
+        double a = 0.0, b = 0.0, g = 0.0;
+        for (int i = 0; i < l; ++i) {
+          const double xp = A[size_t(i) * l + p], xq = A[size_t(i) * l + q];
+          a += xp * xp;
+          b += xq * xq;
+          g += xp * xq;
+        }
+        if (g == 0.0 || std::fabs(g) <= 1e-15 * std::sqrt(a * b)) continue;
+        rotated = true;
+        const double zeta = (b - a) / (2.0 * g);
+        const double t = std::copysign(1.0, zeta) / (std::fabs(zeta) + std::sqrt(1.0 + zeta * zeta));
+        const double cs = 1.0 / std::sqrt(1.0 + t * t), sn = cs * t;
+        for (int i = 0; i < l; ++i) {
+          double& xp = A[size_t(i) * l + p];
+          double& xq = A[size_t(i) * l + q];
+          const double np = cs * xp - sn * xq, nq = sn * xp + cs * xq;
+          xp = np;
+          xq = nq;
+          double& vp = V[size_t(i) * l + p];
+          double& vq = V[size_t(i) * l + q];
+          const double mp = cs * vp - sn * vq, mq = sn * vp + cs * vq;
+          vp = mp;
+          vq = mq;
+        }
+      }
+    if (!rotated) break;
+  }
+  std::vector<double> s(l);
+  for (int j = 0; j < l; ++j) {
+    double n2 = 0.0;
+    for (int i = 0; i < l; ++i) n2 += A[size_t(i) * l + j] * A[size_t(i) * l + j];
+    s[j] = std::sqrt(n2);
+  }
+  std::vector<int> order(l);
+  for (int j = 0; j < l; ++j) order[j] = j;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return s[a] > s[b]; });
+  U.assign(size_t(l) * l, 0.0);
+  sig.assign(l, 0.0);
+  std::vector<double> Vs(size_t(l) * l);
+  for (int jj = 0; jj < l; ++jj) {
+    const int j = order[jj];
+    sig[jj] = s[j];
+    for (int i = 0; i < l; ++i) {
+      U[size_t(i) * l + jj] = s[j] > 0.0 ? A[size_t(i) * l + j] / s[j] : 0.0;
+      Vs[size_t(i) * l + jj] = V[size_t(i) * l + j];
+    }
+  }
+  V.swap(Vs);
+}
+
 }  // namespace
 
 extern "C" {
@@ -510,6 +757,40 @@ int svdq_w4a4_quantize_act(const void* x, int64_t M, int64_t K, const void* smoo
   rc = check_device_arch();
   if (rc) return rc;
   svdq::QuantActArgs qa{x, smooth, lora_down, codes_out, scales_out, lora_act_out, nullptr, nullptr, M, K,
+                        precision, rank};
+  return launch_status(svdq::launch_quantize_act(qa, static_cast<hipStream_t>(stream)),
+                       "quantize_act_lora_down launch");
+}
+
+int svdq_w4a4_quantize_operand(const void* x, int64_t M, int64_t K, const void* smooth,
+                               const void* lora_down, int precision, int group_size, int rank,
+                               void* operand_out, float* row_scale_out, float* lora_act_out,
+                               void* stream) {
+  g_last_error.clear();
+  int rc = check_svdq_kind(precision, group_size, rank);
+  if (rc) return rc;
+  rc = check_shape(M, K, 64);
+  if (rc) return rc;
+  if (!x || !smooth || !operand_out) return fail(SVDQ_EINVAL, "null pointer argument");
+  if ((precision == SVDQ_INT4) != (row_scale_out != nullptr))
+    return fail(SVDQ_EINVAL, "row_scale_out must be non-null exactly for int4");
+  if ((rank > 0) != (lora_down != nullptr) || (rank > 0) != (lora_act_out != nullptr))
+    return fail(SVDQ_EINVAL, "lora_down / lora_act_out must be non-null exactly when rank > 0");
+  const void* ptrs[] = {x, smooth, lora_down, operand_out, row_scale_out, lora_act_out};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  const Range outs[] = {{operand_out, size_t(M) * size_t(K) * 2},
+                        {row_scale_out, size_t(M) * 4},
+                        {lora_act_out, size_t(M) * size_t(rank) * 4}};
+  const Range xr{x, size_t(M) * size_t(K) * 2};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], xr)) return fail(SVDQ_EINVAL, "an output overlaps x");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(SVDQ_EINVAL, "outputs overlap");
+  }
+  rc = check_device_arch();
+  if (rc) return rc;
+  svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, lora_act_out, operand_out, row_scale_out, M, K,
                         precision, rank};
   return launch_status(svdq::launch_quantize_act(qa, static_cast<hipStream_t>(stream)),
                        "quantize_act_lora_down launch");
@@ -678,6 +959,134 @@ int svdq_w4a4_pack_weight(const float* resid, int64_t N, int64_t K, int precisio
   svdq::PackArgs a{resid, packed_w_out, wscales_out, wtscale_out, static_cast<uint32_t*>(workspace), N, K,
                    precision};
   return launch_status(svdq::launch_pack_weight(a, static_cast<hipStream_t>(stream)), "pack weight launch");
+}
+
+size_t svdq_w4a4_prepare_workspace_bytes(int64_t N, int64_t K, int rank, int oversample) {
+  if (N < 1 || N > kMaxPrepN || K < 128 || K > kMaxK || K % 128) return 0;
+  if (rank < 0 || rank > 128 || rank % 16 || rank > std::min(N, K)) return 0;
+  if (oversample < 0 || oversample > kMaxOversample) return 0;
+  return prep_carve(nullptr, N, K, rank, rank + oversample, nullptr);
+}
+
+int svdq_w4a4_prepare_weight(const float* w, const void* x_calib, int64_t Mc, int64_t N, int64_t K,
+                             int precision, int group_size, int rank, int oversample, int power_iters,
+                             uint64_t seed, void* smooth_out, void* lora_down_out, void* lora_up_out,
+                             void* packed_w_out, void* wscales_out, float* wtscale_out, double* sigma_out,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_svdq_kind(precision, group_size, rank);
+  if (rc) return rc;
+  if (N < 1 || N > kMaxPrepN) return fail(SVDQ_EINVAL, "N must be in [1, 2^20]");
+  if (Mc < 1 || Mc > kMaxPrepRows) return fail(SVDQ_EINVAL, "the calibration rows must be in [1, 2^22]");
+  if (K < 128 || K > kMaxK || K % 128) return fail(SVDQ_EINVAL, "K must be a multiple of 128 in [128, 16384]");
+  if (rank > std::min(N, K)) return fail(SVDQ_EINVAL, "rank exceeds min(N, K)");
+  if (oversample < 0 || oversample > kMaxOversample) return fail(SVDQ_EINVAL, "oversample must be in [0, 32]");
+  if (power_iters < 0 || power_iters > kMaxPowerIters) return fail(SVDQ_EINVAL, "power_iters must be in [0, 16]");
+  if (!w || !x_calib || !smooth_out || !packed_w_out || !wscales_out || !wtscale_out || !workspace)
+    return fail(SVDQ_EINVAL, "null pointer argument");
+  if ((rank > 0) != (lora_down_out != nullptr) || (rank > 0) != (lora_up_out != nullptr))
+    return fail(SVDQ_EINVAL, "lora_down_out / lora_up_out must be non-null exactly when rank > 0");
+  const void* ptrs[] = {w, x_calib, smooth_out, lora_down_out, lora_up_out, packed_w_out, wscales_out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(wtscale_out) % 4) return fail(SVDQ_EINVAL, "wtscale_out must be 4-byte aligned");
+  const int l = rank + oversample;
+  const size_t need = prep_carve(nullptr, N, K, rank, l, nullptr);
+  const Range outs[] = {{smooth_out, size_t(K) * 2},
+                        {lora_down_out, size_t(rank) * size_t(K) * 2},
+                        {lora_up_out, size_t(N) * size_t(rank) * 2},
+                        {packed_w_out, size_t(N) * size_t(K / 2)},
+                        {wscales_out, w_scale_bytes(N, K, precision)},
+                        {wtscale_out, 4}};
+  const Range ins[] = {{w, size_t(N) * size_t(K) * 4}, {x_calib, size_t(Mc) * size_t(K) * 2}, {workspace, need}};
+  for (size_t i = 0; i < 6; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return fail(SVDQ_EINVAL, "an output overlaps an input or the workspace");
+    for (size_t j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(SVDQ_EINVAL, "outputs overlap");
+  }
+  if (ws_bytes < need) return fail(SVDQ_EWORKSPACE, "workspace too small");
+  rc = check_device_arch();
+  if (rc) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PrepCtx x{s, l, {}};
+  prep_carve(workspace, N, K, rank, l, &x.c);
+  // 1. smoothing factors from the calibration activations
+  svdq::SmoothArgs sa{x_calib, w, smooth_out, x.c.amax, Mc, N, K};
+  rc = launch_status(svdq::launch_smooth_factors(sa, s), "smooth factors launch");
+  if (rc) return rc;
+  if (rank > 0) {
+    svdq::PrepSrc W;
+    W.w = w;
+    W.smooth = smooth_out;
+    // 2. range finder: Y = W_hat Omega, Q = orth(Y); subspace iteration
+    rc = launch_status(svdq::launch_prep_gauss(x.c.omega, K * l, seed, s), "test matrix launch");
+    if (rc) return rc;
+    rc = launch_status(svdq::launch_prep_ab(W, N, K, x.c.omega, l, x.c.y, s), "range product launch");
+    if (rc) return rc;
+    rc = prep_orth(x, x.c.y, N, x.c.q, nullptr);
+    if (rc) return rc;
+    for (int it = 0; it < power_iters; ++it) {
+      rc = launch_status(svdq::launch_prep_atb(W, N, K, x.c.q, l, prep_slices(N, K), x.c.part, x.c.z, s),
+                         "transposed product launch");
+      if (rc) return rc;
+      rc = prep_orth(x, x.c.z, K, x.c.zq, nullptr);
+      if (rc) return rc;
+      rc = launch_status(svdq::launch_prep_ab(W, N, K, x.c.zq, l, x.c.y, s), "range product launch");
+      if (rc) return rc;
+      rc = prep_orth(x, x.c.y, N, x.c.q, nullptr);
+      if (rc) return rc;
+    }
+    // 3. Z = W_hat^T Q = Zq Rz, so W_hat ~ Q Rz^T Zq^T; SVD of the l x l Rz^T
+    rc = launch_status(svdq::launch_prep_atb(W, N, K, x.c.q, l, prep_slices(N, K), x.c.part, x.c.z, s),
+                       "transposed product launch");
+    if (rc) return rc;
+    std::vector<double> Rz;
+    rc = prep_orth(x, x.c.z, K, x.c.zq, &Rz);
+    if (rc) return rc;
+    std::vector<double> At(size_t(l) * l), U, sig, V;
+    for (int i = 0; i < l; ++i)
+      for (int j = 0; j < l; ++j) At[size_t(i) * l + j] = Rz[size_t(j) * l + i];
+    jacobi_svd(At, l, U, sig, V);
+    if (sigma_out)
+      for (int i = 0; i < rank; ++i) sigma_out[i] = sig[i];
+    // 4. lora_up = (Q U)[:, :rank]; lora_down = ((Zq V)[:, :rank] diag(sig))^T, both rounded to bf16
+    std::vector<double> B(size_t(l) * rank);
+    for (int i = 0; i < l; ++i)
+      for (int j = 0; j < rank; ++j) B[size_t(i) * rank + j] = U[size_t(i) * l + j];
+    svdq::PrepSrc D;
+    D.dense = x.c.q;
+    rc = prep_status(hipMemcpyAsync(x.c.small, B.data(), B.size() * sizeof(double), hipMemcpyHostToDevice, s),
+                     "factor copy");
+    if (rc) return rc;
+    rc = launch_status(svdq::launch_prep_ab(D, N, l, x.c.small, rank, x.c.up64, s), "factor product launch");
+    if (rc) return rc;
+    rc = prep_status(hipStreamSynchronize(s), "stream synchronize");
+    if (rc) return rc;
+    for (int i = 0; i < l; ++i)
+      for (int j = 0; j < rank; ++j) B[size_t(i) * rank + j] = V[size_t(i) * l + j] * sig[j];
+    D.dense = x.c.zq;
+    rc = prep_status(hipMemcpyAsync(x.c.small, B.data(), B.size() * sizeof(double), hipMemcpyHostToDevice, s),
+                     "factor copy");
+    if (rc) return rc;
+    rc = launch_status(svdq::launch_prep_ab(D, K, l, x.c.small, rank, x.c.dt64, s), "factor product launch");
+    if (rc) return rc;
+    rc = launch_status(svdq::launch_prep_to_bf16(x.c.up64, N, rank, rank, false, static_cast<uint16_t*>(lora_up_out),
+                                                 s), "factor rounding launch");
+    if (rc) return rc;
+    rc = launch_status(svdq::launch_prep_to_bf16(x.c.dt64, K, rank, rank, true,
+                                                 static_cast<uint16_t*>(lora_down_out), s), "factor rounding launch");
+    if (rc) return rc;
+  }
+  // 5. residual from the bf16 factors, then quantization and packing
+  rc = launch_status(svdq::launch_prep_residual(w, smooth_out, lora_up_out, lora_down_out, N, K, rank, x.c.resid, s),
+                     "residual launch");
+  if (rc) return rc;
+  svdq::PackArgs pa{x.c.resid, packed_w_out, wscales_out, wtscale_out, x.c.amax, N, K, precision};
+  rc = launch_status(svdq::launch_pack_weight(pa, s), "pack weight launch");
+  if (rc) return rc;
+  return prep_status(hipStreamSynchronize(s), "stream synchronize");
 }
 
 int svdq_w4a4_gelu_table(void* out, void* stream) {

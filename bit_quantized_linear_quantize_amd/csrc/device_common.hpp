@@ -39,6 +39,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// float64 -> bf16 bits, one round-to-nearest-even step (bf16 subnormals have
+// the quantum 2^-133; overflow gives infinity)
+__device__ __forceinline__ uint16_t bf16_from_f64(double v) {
+  const double a = fabs(v);
+  double r;
+  if (a < 0x1p-126) {
+    r = rint(v * 0x1p133) * 0x1p-133;
+  } else {
+    // keep 7 of the 52 fraction bits: add half an ulp minus one plus the
+    // kept lowest bit (ties to even), then clear the 45 dropped bits
+    uint64_t u = (uint64_t)__double_as_longlong(v);
+    u += 0xFFFFFFFFFFFull + ((u >> 45) & 1ull);
+    u &= ~0x1FFFFFFFFFFFull;
+    r = __longlong_as_double((long long)u);
+  }
+  return (uint16_t)(__float_as_uint((float)r) >> 16);
+}
+
 // Two floats -> packed bf16 pair (RNE), low half = a, with the hardware
 // pair conversion (finite inputs).
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {

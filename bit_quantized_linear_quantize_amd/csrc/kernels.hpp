@@ -94,6 +94,27 @@ struct PackArgs {
   int precision;
 };
 
+// Low-rank split of the weight preparation (prep_svd.hip).  A matrix operand
+// of the products: the smoothed weight w[n, k] * smooth[k] (w non-null) or a
+// dense row-major fp64 matrix.
+struct PrepSrc {
+  const float* w = nullptr;       // fp32 [R, C]
+  const void* smooth = nullptr;   // bf16 [C]
+  const double* dense = nullptr;  // fp64 [R, C] when w is null
+};
+constexpr int kPrepMaxL = 160;  // widest product (rank + oversampling)
+hipError_t launch_prep_gauss(double* omega, int64_t n, uint64_t seed, hipStream_t s);
+// out [R, l] = A [R, C] B [C, l]
+hipError_t launch_prep_ab(const PrepSrc& a, int64_t R, int64_t C, const double* B, int l, double* out,
+                          hipStream_t s);
+// out [C, l] = A^T B, A [R, C], B [R, l]; part: fp64 [slices, C, l] scratch
+hipError_t launch_prep_atb(const PrepSrc& a, int64_t R, int64_t C, const double* B, int l, int slices, double* part,
+                           double* out, hipStream_t s);
+hipError_t launch_prep_to_bf16(const double* src, int64_t rows, int64_t cols, int64_t ld, bool transpose,
+                               uint16_t* dst, hipStream_t s);
+hipError_t launch_prep_residual(const float* w, const void* smooth, const void* up, const void* down, int64_t N,
+                                int64_t K, int rank, float* resid, hipStream_t s);
+
 hipError_t launch_smooth_factors(const SmoothArgs& a, hipStream_t stream);
 hipError_t launch_pack_weight(const PackArgs& a, hipStream_t stream);
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream);

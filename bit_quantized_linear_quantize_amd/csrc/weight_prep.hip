@@ -12,8 +12,8 @@
 //   nvfp4: t = fl32(amax_tensor / 2688), s8 = E4M3(fl32(amax / fl32(6 t))),
 //          S = fl32(dec(s8) t), code = E2M1(fl32(r * fl32(1 / S)));
 //   groups with amax < 2^-100 (or a zero scale): scale 0, codes 0.
-// The low-rank split (an SVD) is not here: it is not bit-reproducible across
-// libraries, and runs once per layer.
+// The low-rank split between the two (an SVD of the smoothed weight) is in
+// prep_svd.hip.
 //
 // Column maxima and the tensor maximum are reduced with atomicMax on the bit
 // patterns of non-negative floats, whose order is that of the values.
@@ -46,24 +46,6 @@ __global__ __launch_bounds__(256) void prep_colmax_kernel(const uint16_t* __rest
   }
   if (r0 < M) atomicMax(amax + k, mx);
   if (r0 < N) atomicMax(amax + K + k, mw);
-}
-
-// float64 -> bf16 bits, one round-to-nearest-even step (bf16 subnormals have
-// the quantum 2^-133; overflow gives infinity)
-__device__ __forceinline__ uint16_t bf16_from_f64(double v) {
-  const double a = fabs(v);
-  double r;
-  if (a < 0x1p-126) {
-    r = rint(v * 0x1p133) * 0x1p-133;
-  } else {
-    // keep 7 of the 52 fraction bits: add half an ulp minus one plus the
-    // kept lowest bit (ties to even), then clear the 45 dropped bits
-    uint64_t u = (uint64_t)__double_as_longlong(v);
-    u += 0xFFFFFFFFFFFull + ((u >> 45) & 1ull);
-    u &= ~0x1FFFFFFFFFFFull;
-    r = __longlong_as_double((long long)u);
-  }
-  return (uint16_t)(__float_as_uint((float)r) >> 16);
 }
 
 __global__ __launch_bounds__(256) void prep_smooth_kernel(const uint32_t* amax, int64_t K, uint16_t* smooth) {

@@ -211,11 +211,11 @@ int svdq_w4a4_qkv_rmsnorm_rope(const void* x, int64_t M, const svdq_w4a4_layer* 
                                const float* rope_cos, const float* rope_sin, void* out,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Offline weight preparation on the GPU (what the diffuse-compressor tool the
- * Nunchaku Lite pages name under "Resources" does before a checkpoint is
- * saved), bit-identical to the CPU reference packer.  The low-rank split (an
- * SVD of smooth-scaled W) is not part of it: the caller computes the
- * residual R = W * smooth - lora_up lora_down between the two calls.
+/* Offline weight preparation on the GPU, step by step (what the
+ * diffuse-compressor tool the Nunchaku Lite pages name under "Resources" does
+ * before a checkpoint is saved), bit-identical to the CPU reference packer.
+ * svdq_w4a4_prepare_weight below runs the whole preparation, the low-rank
+ * split included; these two calls are its first and last steps on their own.
  *
  * Scratch for both calls: svdq_w4a4_prep_workspace_bytes(K) bytes (0 for an
  * invalid K). */
@@ -248,14 +248,64 @@ int svdq_w4a4_pack_weight(const float* resid, int64_t N, int64_t K, int precisio
                           void* packed_w_out, void* wscales_out, float* wtscale_out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of scratch svdq_w4a4_prepare_weight needs for an [N, K] weight with
+ * the given rank and oversampling (0 for arguments it would reject): the
+ * fp64 matrices of the range finder ([max(N, K), rank + oversample] each,
+ * and row-slice partial sums) and the fp32 residual [N, K]. */
+size_t svdq_w4a4_prepare_workspace_bytes(int64_t N, int64_t K, int rank, int oversample);
+
+/* Offline preparation of one svdq_w4a4 layer on the GPU, from a weight and
+ * calibration activations to every weight-side input of svdq_w4a4_linear --
+ * what the diffuse-compressor tool named under "Resources" on the Nunchaku
+ * Lite pages does before a checkpoint is saved:
+ *   1. smooth = the factors of svdq_w4a4_smooth_factors(x_calib, w);
+ *   2. the rank-r split of W_hat = W * smooth (per input channel) by a
+ *      randomized range finder with subspace iteration (Halko, Martinsson and
+ *      Tropp, "Finding structure with randomness", 2011, Algorithms 4.3 and
+ *      4.4): l = rank + oversample Gaussian test vectors drawn from `seed`,
+ *      power_iters iterations, each product re-orthonormalized (shifted
+ *      CholeskyQR, then two CholeskyQR passes); the SVD of the final l x l
+ *      factor runs on the host in fp64 (one-sided Jacobi).  lora_up =
+ *      bf16(U_r) [N, rank], lora_down = bf16(Sigma_r V_r^T) [rank, K];
+ *   3. the residual R = fl32(W_hat - lora_up lora_down), in fp64 from the bf16
+ *      factors with the rank terms added in order, quantized and packed as
+ *      svdq_w4a4_pack_weight does.
+ * The products run as this library's kernels; the call synchronizes `stream`
+ * (small matrices go to and from the host), so it is for offline use.  The
+ * same arguments and seed give the same bits.
+ *
+ * w             fp32 [N, K] weight (device); 1 <= N <= 2^20, K as for the linear
+ * x_calib       bf16 [Mc, K] calibration activations (device), 1 <= Mc <= 2^22
+ * precision, group_size, rank  as for svdq_w4a4_linear; rank <= min(N, K)
+ * oversample    0..32 extra test vectors; power_iters 0..16; seed any value
+ * outputs (device): smooth_out bf16 [K]; lora_down_out bf16 [rank, K] and
+ *   lora_up_out bf16 [N, rank] (NULL iff rank == 0); packed_w_out uint8
+ *   [N, K/2]; wscales_out as for svdq_w4a4_pack_weight; wtscale_out fp32 [1]
+ * sigma_out     host double [rank], the estimated leading singular values of
+ *               W_hat, or NULL
+ * workspace     at least svdq_w4a4_prepare_workspace_bytes(N, K, rank,
+ *               oversample) bytes of device memory
+ * Outputs may not overlap each other, the inputs or the workspace; errors as
+ * for svdq_w4a4_linear (validation before any launch). */
+int svdq_w4a4_prepare_weight(const float* w, const void* x_calib, int64_t Mc, int64_t N, int64_t K,
+                             int precision, int group_size, int rank, int oversample, int power_iters,
+                             uint64_t seed, void* smooth_out, void* lora_down_out, void* lora_up_out,
+                             void* packed_w_out, void* wscales_out, float* wtscale_out, double* sigma_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Parity export of the fused MLP's GELU: out (bf16 [65536]) receives, for
  * every bf16 bit pattern b, the bits of GELU(h) = h/2 (1 + erf(h / sqrt 2))
  * of the value h with bits b, rounded once to bf16 -- the table the epilogue
  * of svdq_w4a4_mlp_gelu looks its GELU up in. */
 int svdq_w4a4_gelu_table(void* out, void* stream);
 
-/* Parity export of the first svdq_w4a4 kernel (same kernel as the linear):
- * smoothing, activation quantization and the low-rank down projection.
+/* Parity export of the first svdq_w4a4 kernel in its packed-code form:
+ * smoothing, activation quantization and the low-rank down projection
+ * ("Supported quantization types": the svdq_w4a4 activation formats).  This
+ * is the export instantiation of the kernel template the linear runs: the
+ * same smoothing, scale and low-rank code, but it writes packed nibbles and
+ * scales (its int4 codes are rounded by the fp32 1.5 * 2^23 addition) where
+ * the linear writes the product operand (see svdq_w4a4_quantize_operand).
  * codes_out  uint8 [M, K/2]; scales_out bf16 [M, K/64] (int4) or uint8 E4M3
  * [M, K/16] (nvfp4); lora_act_out fp32 [M, rank] (may be NULL iff rank == 0).
  * Arguments as for svdq_w4a4_linear. */
@@ -263,6 +313,26 @@ int svdq_w4a4_quantize_act(const void* x, int64_t M, int64_t K, const void* smoo
                            const void* lora_down, int precision, int group_size, int rank,
                            void* codes_out, void* scales_out, float* lora_act_out,
                            void* stream);
+
+/* Parity export of the first svdq_w4a4 kernel exactly as svdq_w4a4_linear
+ * launches it: the product operand the second kernel multiplies, written to
+ * caller buffers instead of the workspace ("Supported quantization types":
+ * the svdq_w4a4 activation formats, held dequantized).
+ *   operand_out    IEEE binary16 [M, K]: nvfp4 e2m1 * dec(s8) (always exact);
+ *                  int4 q * s * 2^-E[m], where E[m] = 0 when every group scale
+ *                  s of row m lies in [2^-17, 2^13) (then each value is the
+ *                  exact product), else E[m] = floor(log2 max_g s) - 12 and
+ *                  each value is f16(q * f16(s * 2^-E[m])) (exact for groups
+ *                  within 2^29 of the row's largest scale, rounded to nearest
+ *                  even below that)
+ *   row_scale_out  int4: fp32 [M], 2^E[m]; must be NULL for nvfp4
+ *   lora_act_out   fp32 [M, rank] (NULL iff rank == 0)
+ * Other arguments and rules as for svdq_w4a4_quantize_act; no output may
+ * overlap x or another output. */
+int svdq_w4a4_quantize_operand(const void* x, int64_t M, int64_t K, const void* smooth,
+                               const void* lora_down, int precision, int group_size, int rank,
+                               void* operand_out, float* row_scale_out, float* lora_act_out,
+                               void* stream);
 
 /* Parity export of the 4-bit product of the second svdq_w4a4 kernel (same
  * operand unpacking and matrix instructions): exact per-group integer dot

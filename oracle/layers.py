@@ -23,9 +23,9 @@ outliers move into a 16-bit low-rank branch) -- readings, in order:
    W_hat[n, k] = W[n, k] * smooth_k, so X_hat W_hat^T = X W^T;
 3. W_hat = U Sigma V^T (fp64 SVD); lora_down = Sigma_r V_r^T, lora_up = U_r,
    both rounded to bf16;
-4. residual R = W_hat - lora_up lora_down (fp64, from the bf16 factors), cast to
-   fp32 and quantized per row with the activation quantizer of the precision
-   (nvfp4 adds one fp32 tensor scale);
+4. residual R = W_hat - lora_up lora_down (fp64, from the bf16 factors, the
+   rank terms added in order), cast to fp32 and quantized per row with the
+   activation quantizer of the precision (nvfp4 adds one fp32 tensor scale);
 5. forward: X_hat = fl32(x * fl32(1/smooth)); quantize X_hat per token;
    Y = sum_g P_g * s_a * s_w * c + (X_hat lora_down^T) lora_up^T + bias,
    accumulated in fp64, with P_g the integer dot product of the codes in group
@@ -70,7 +70,6 @@ def prepare_svdq_layer(w, smooth_bits, rank, precision, bias_bits=None):
     """
     if precision not in GROUP:
         raise ValueError(precision)
-    G = GROUP[precision]
     w = np.asarray(w, dtype=np.float64)
     N, K = w.shape
     smooth = bf16_to_f32(smooth_bits).astype(np.float64)
@@ -80,12 +79,47 @@ def prepare_svdq_layer(w, smooth_bits, rank, precision, bias_bits=None):
     up = u[:, :rank]                                # [N, r]
     down_bits = bf16_bits_f64(down).reshape(rank, K)
     up_bits = bf16_bits_f64(up).reshape(N, rank)
-    low = bf16_to_f32(up_bits).astype(np.float64) @ bf16_to_f32(down_bits).astype(np.float64)
-    resid = w_hat - low
+    out = prepare_svdq_layer_from_factors(w, smooth_bits, down_bits, up_bits, precision, bias_bits)
+    out["sigma"] = sig
+    return out
+
+
+def low_rank_residual(w, smooth_bits, down_bits, up_bits):
+    """R = W_hat - lora_up lora_down in fp64 from the bf16 factors, with
+    W_hat[n, k] = w[n, k] * smooth[k].  The r terms of each entry are added in
+    order j = 0 .. r-1, each product rounded to fp64 on its own (reading: the
+    pages give no arithmetic; a fixed order makes the residual reproducible
+    bit for bit by any implementation, whatever its matrix-product library).
+    Returns (W_hat, R) as float64 [N, K]."""
+    w = np.asarray(w, dtype=np.float64)
+    smooth = bf16_to_f32(smooth_bits).astype(np.float64)
+    w_hat = w * smooth[None, :]
+    up = bf16_to_f32(up_bits).astype(np.float64)
+    down = bf16_to_f32(down_bits).astype(np.float64)
+    low = np.zeros_like(w_hat)
+    for j in range(up.shape[1]):
+        low = low + up[:, j:j + 1] * down[j:j + 1, :]
+    return w_hat, w_hat - low
+
+
+def prepare_svdq_layer_from_factors(w, smooth_bits, down_bits, up_bits, precision, bias_bits=None):
+    """The rest of the preparation given the bf16 low-rank factors
+    (lora_down [r, K], lora_up [N, r]): the residual (low_rank_residual), cast
+    to fp32, quantized per row and packed.  Same dict as prepare_svdq_layer,
+    without the singular values."""
+    if precision not in GROUP:
+        raise ValueError(precision)
+    G = GROUP[precision]
+    w = np.asarray(w, dtype=np.float64)
+    N, K = w.shape
+    down_bits = np.asarray(down_bits, np.uint16).reshape(-1, K)
+    up_bits = np.asarray(up_bits, np.uint16).reshape(N, -1)
+    rank = down_bits.shape[0]
+    w_hat, resid = low_rank_residual(w, smooth_bits, down_bits, up_bits)
     r32 = resid.astype(F32)
     out = dict(precision=precision, group_size=G, rank=rank, N=N, K=K,
                smooth=np.asarray(smooth_bits, np.uint16), lora_down=down_bits,
-               lora_up=up_bits, sigma=sig, w_hat=w_hat, resid=resid,
+               lora_up=up_bits, w_hat=w_hat, resid=resid,
                bias=None if bias_bits is None else np.asarray(bias_bits, np.uint16))
     if precision == "int4":
         nib, s, q = quantize_int4(r32, G)

@@ -211,6 +211,27 @@ def test_linear_rejects_before_touching_the_device(L):
     assert rc == EUNSUP
 
 
+def test_operand_export_rejects_before_touching_the_device(L):
+    # svdq_w4a4_quantize_operand validates everything before its device check
+    def call(prec=0, group=64, rank=16, rs=0x3000_0000, la=0x4000_0000, op=0x2000_0000, ld=0x5000_0000,
+             M=64, K=512):
+        return L.svdq_w4a4_quantize_operand(_fake(0x1000_0000), M, K, _fake(0x6000_0000),
+                                            None if ld is None else _fake(ld), prec, group, rank,
+                                            None if op is None else _fake(op), None if rs is None else _fake(rs),
+                                            None if la is None else _fake(la), None)
+    assert call(group=16) == EUNSUP
+    assert call(rank=24) == EUNSUP
+    assert call(K=100) == EINVAL
+    assert call(rs=None) == EINVAL              # int4 needs the row factors
+    assert call(prec=1, group=16) == EINVAL     # nvfp4 has none
+    assert call(la=None) == EINVAL
+    assert call(ld=None) == EINVAL
+    assert call(op=None) == EINVAL
+    assert call(op=0x1000_0000 + 64) == EINVAL  # overlaps x
+    assert call(rs=0x2000_0000 + 256) == EINVAL  # overlaps the operand
+    assert call(op=0x2000_0008) == EINVAL       # misaligned
+
+
 # ------------------------------------------------------------------ fused GELU MLP
 def _layer(base, K, N, precision=1, rank=32, wt=None):
     group = 16 if precision == 1 else 64

@@ -347,3 +347,50 @@ def test_qkv_norm_rope_brute_force():
                     assert math.isclose(got[m, c0 + 2 * i], a * cs - b * sn, rel_tol=0, abs_tol=1e-12)
                     assert math.isclose(got[m, c0 + 2 * i + 1], a * sn + b * cs, rel_tol=0, abs_tol=1e-12)
         assert np.array_equal(got[m, 2 * H * D:], h64[m, 2 * H * D:])
+
+
+def test_low_rank_residual_against_exact_arithmetic():
+    # R = W_hat - up down with the rank terms added in order: against
+    # Fraction arithmetic, the error is at most r + 1 roundings of the
+    # largest partial sum; with factors on a common power-of-two grid every
+    # partial sum is exact and so is R
+    from fractions import Fraction
+    rng = np.random.default_rng(12)
+    N, K, r = 6, 8, 5
+    w = F.bf16_round(rng.standard_normal((N, K)).astype(np.float32)).astype(np.float64)
+    sm = F.bf16_bits(rng.uniform(0.5, 2, K).astype(np.float32))
+    up = F.bf16_bits(rng.standard_normal((N, r)).astype(np.float32))
+    dn = F.bf16_bits(rng.standard_normal((r, K)).astype(np.float32))
+    w_hat, R = L.low_rank_residual(w, sm, dn, up)
+    upf, dnf, smf = (F.bf16_to_f32(a).astype(np.float64) for a in (up, dn, sm))
+    for n in range(N):
+        for k in range(K):
+            wh = Fraction(w[n, k]) * Fraction(smf[k])
+            assert Fraction(w_hat[n, k]) == wh            # the product is exact
+            exact = wh - sum(Fraction(upf[n, j]) * Fraction(dnf[j, k]) for j in range(r))
+            big = max([abs(wh)] + [abs(Fraction(upf[n, j]) * Fraction(dnf[j, k])) for j in range(r)])
+            assert abs(Fraction(R[n, k]) - exact) <= (r + 1) * r * big * Fraction(2) ** -53
+    # small-integer factors times 2^-4: every partial sum is exact
+    up2 = F.bf16_bits((rng.integers(-8, 8, (N, r)) / 16).astype(np.float32))
+    dn2 = F.bf16_bits((rng.integers(-8, 8, (r, K)) / 16).astype(np.float32))
+    ones = F.bf16_bits(np.ones(K, np.float32))
+    _, R2 = L.low_rank_residual(w, ones, dn2, up2)
+    u2, d2 = F.bf16_to_f32(up2).astype(np.float64), F.bf16_to_f32(dn2).astype(np.float64)
+    for n in range(N):
+        for k in range(K):
+            exact = Fraction(w[n, k]) - sum(Fraction(u2[n, j]) * Fraction(d2[j, k]) for j in range(r))
+            assert Fraction(R2[n, k]) == exact
+
+
+def test_prepare_from_factors_reproduces_prepare():
+    # the split of prepare_svdq_layer is the composition of the SVD and
+    # prepare_svdq_layer_from_factors
+    rng = np.random.default_rng(13)
+    w = S.weight(96, 256, 0.02, rng, spike_rank=2)
+    sm = F.bf16_bits(rng.uniform(0.5, 2, 256).astype(np.float32))
+    for p in ("int4", "nvfp4"):
+        a = L.prepare_svdq_layer(w, sm, 16, p)
+        b = L.prepare_svdq_layer_from_factors(w, sm, a["lora_down"], a["lora_up"], p)
+        for key in ("packed_w", "wscales", "resid"):
+            assert np.array_equal(a[key], b[key]), key
+        assert a["wtscale"] == b["wtscale"]
