@@ -23,7 +23,8 @@ STATUS = {0: "SVDQ_OK", -1: "SVDQ_EINVAL", -2: "SVDQ_EUNSUPPORTED", -3: "SVDQ_EA
           -4: "SVDQ_EWORKSPACE", -5: "SVDQ_EDEVICE"}
 
 # entry points declared in include/svdq_w4a4.h
-EXPORTS = ("svdq_w4a4_workspace_bytes", "svdq_w4a4_linear", "svdq_w4a4_quantize", "svdq_w4a4_gemm",
+EXPORTS = ("svdq_w4a4_workspace_bytes", "svdq_w4a4_linear", "svdq_w4a4_linear_noalloc", "svdq_w4a4_quantize",
+           "svdq_w4a4_gemm",
            "awq_w4a16_linear", "svdq_w4a4_mlp_workspace_bytes", "svdq_w4a4_mlp_gelu",
            "svdq_w4a4_quantize_act", "svdq_w4a4_quantize_operand", "svdq_w4a4_gemm_partials",
            "svdq_w4a4_check",
@@ -65,6 +66,8 @@ def lib():
         L.svdq_w4a4_linear.argtypes = [P, I64, I64, I64, P, P, ctypes.c_float, P, P, P, P, I, I, I,
                                        P, P, ctypes.c_size_t, P]
         L.svdq_w4a4_linear.restype = I
+        L.svdq_w4a4_linear_noalloc.argtypes = [P, I64, I64, I64, P, P, ctypes.c_float, P, P, P, P, I, I, I, P, P]
+        L.svdq_w4a4_linear_noalloc.restype = I
         L.svdq_w4a4_quantize.argtypes = [P, I64, I64, P, P, I, I, I, P, ctypes.c_size_t, P]
         L.svdq_w4a4_quantize.restype = I
         L.svdq_w4a4_gemm.argtypes = [P, ctypes.c_size_t, I64, I64, I64, P, P, ctypes.c_float, P, P, I, I, I,
@@ -248,6 +251,24 @@ def svdq_w4a4_linear(x, layer, out=None, workspace=None, stream=None):
         _ptr(layer.smooth), _ptr(layer.lora_down), _ptr(layer.lora_up), _ptr(layer.bias),
         PRECISIONS[layer.precision], GROUP_SIZE[layer.precision], layer.rank, _ptr(out),
         _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SVDQ_NOALLOC_SCRATCH_BYTES of include/svdq_w4a4.h
+
+
+def svdq_w4a4_linear_noalloc(x, layer, out, stream=None):
+    """svdq_w4a4_linear with the library's static device scratch instead of a
+    workspace (for callers that cannot allocate: graph capture, serving loops);
+    out is required (bf16 [M, N]).  Calls that overlap in time on one GPU race."""
+    x = _x(x, layer.K)
+    M, K = x.shape
+    out = _contig(out, torch.bfloat16, "out", (M, layer.N))
+    _on_gpu(x=x, out=out)
+    _check(lib().svdq_w4a4_linear_noalloc(
+        _ptr(x), M, K, layer.N, _ptr(layer.packed_w), _ptr(layer.wscales), layer.wtscale,
+        _ptr(layer.smooth), _ptr(layer.lora_down), _ptr(layer.lora_up), _ptr(layer.bias),
+        PRECISIONS[layer.precision], GROUP_SIZE[layer.precision], layer.rank, _ptr(out), _stream(stream)))
     return out
 
 

@@ -44,7 +44,9 @@ def build(verbose=False):
 
     def compile_one(src):
         obj = os.path.join(BUILD, src + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        # api.cpp is host code that also defines the static device scratch
+        # of the allocation-free entry point, so it is compiled as HIP too
+        lang = ["-x", "hip"] if src.endswith(".hip") or src == "api.cpp" else []
         _run([HIPCC] + FLAGS + ["-I", BUILD] + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 

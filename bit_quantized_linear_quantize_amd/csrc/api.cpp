@@ -26,10 +26,19 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "kernels.hpp"
+
+// Scratch of svdq_w4a4_linear_noalloc: a static array in device memory, one
+// copy on every GPU the library runs on, held until the process ends.  Host
+// code never takes the array's name as an address (on the host it is only a
+// stand-in): the per-device address comes from hipGetSymbolAddress, taken
+// once per device with that device current (noalloc_scratch below).
+constexpr size_t kNoallocScratchBytes = SVDQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -152,17 +161,20 @@ size_t linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision, in
   return workspace_bytes(M, K, precision, rank) + split_bytes(M, K, N);
 }
 
+// with_workspace false: the caller's workspace is not checked (the
+// allocation-free entry brings its own)
 int validate_svdq(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
                   const void* wscales, float wtscale, const void* smooth, const void* lora_down,
                   const void* lora_up, const void* bias, int precision, int group_size, int rank,
-                  const void* out, const void* workspace, size_t workspace_bytes_given) {
+                  const void* out, const void* workspace, size_t workspace_bytes_given,
+                  bool with_workspace = true) {
   int rc = check_svdq_kind(precision, group_size, rank);
   if (rc) return rc;
   rc = check_shape(M, K, N);
   if (rc) return rc;
   rc = check_gemm_tiles(M, N);
   if (rc) return rc;
-  if (!x || !packed_w || !wscales || !smooth || !out || !workspace)
+  if (!x || !packed_w || !wscales || !smooth || !out || (with_workspace && !workspace))
     return fail(SVDQ_EINVAL, "null pointer argument");
   if ((rank > 0) != (lora_down != nullptr) || (rank > 0) != (lora_up != nullptr))
     return fail(SVDQ_EINVAL, "lora_down / lora_up must be non-null exactly when rank > 0");
@@ -184,6 +196,7 @@ int validate_svdq(const void* x, int64_t M, int64_t K, int64_t N, const void* pa
                        {workspace, need}};
   for (const Range& r : ins)
     if (overlaps(o, r)) return fail(SVDQ_EINVAL, "out overlaps an input or the workspace");
+  if (!with_workspace) return SVDQ_OK;
   if (overlaps(Range{x, size_t(M) * size_t(K) * 2}, Range{workspace, need}))
     return fail(SVDQ_EINVAL, "workspace overlaps x");
   if (workspace_bytes_given < need) return fail(SVDQ_EWORKSPACE, "workspace too small");
@@ -371,6 +384,29 @@ int validate_qkv(const void* x, int64_t M, const svdq_w4a4_layer* qkv, int heads
   return SVDQ_OK;
 }
 
+
+// ---- allocation-free linear ----------------------------------------------------
+std::mutex g_scratch_mu;
+void* g_scratch[64];
+
+// This device's address of `scratch`, looked up on the first call on the
+// device (with it current) and kept.
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SVDQ_EDEVICE, std::string("hipGetDevice failed: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(SVDQ_EDEVICE, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SVDQ_EDEVICE, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SVDQ_OK;
+}
 
 // ---- offline preparation: the rank-r split -------------------------------------
 // A randomized range finder with subspace iteration (Halko, Martinsson and
@@ -726,6 +762,30 @@ int svdq_w4a4_linear(const void* x, int64_t M, int64_t K, int64_t N, const void*
   rc = launch_quantize(x, M, K, smooth, lora_down, precision, rank, workspace, s);
   if (rc) return rc;
   return launch_gemm(workspace, M, K, N, packed_w, wscales, wtscale, lora_up, bias, precision, rank, out, s);
+}
+
+int svdq_w4a4_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,
+                             const void* wscales, float wtscale, const void* smooth, const void* lora_down,
+                             const void* lora_up, const void* bias, int precision, int group_size, int rank,
+                             void* out, void* stream) {
+  g_last_error.clear();
+  int rc = validate_svdq(x, M, K, N, packed_w, wscales, wtscale, smooth, lora_down, lora_up, bias, precision,
+                         group_size, rank, out, nullptr, 0, false);
+  if (rc) return rc;
+  const size_t need = linear_workspace_bytes(M, K, N, precision, rank);
+  if (need > kNoallocScratchBytes)
+    return fail(SVDQ_EWORKSPACE, "svdq_w4a4_linear_noalloc: this call needs " + std::to_string(need) +
+                                     " bytes of scratch, more than the " + std::to_string(kNoallocScratchBytes) +
+                                     " of the static scratch (use svdq_w4a4_linear with a workspace)");
+  rc = check_device_arch();
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = noalloc_scratch(&ws);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = launch_quantize(x, M, K, smooth, lora_down, precision, rank, ws, s);
+  if (rc) return rc;
+  return launch_gemm(ws, M, K, N, packed_w, wscales, wtscale, lora_up, bias, precision, rank, out, s);
 }
 
 int awq_w4a16_linear(const void* x, int64_t M, int64_t K, int64_t N, const void* packed_w,

@@ -111,6 +111,32 @@ int svdq_w4a4_gemm(const void* workspace, size_t workspace_bytes, int64_t M, int
                    const void* lora_up, const void* bias, int precision, int group_size,
                    int rank, void* out, void* stream);
 
+/* svdq_w4a4_linear for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: the scratch (the same parts, in the same layout, as
+ * svdq_w4a4_linear's workspace) is a static device array of
+ * SVDQ_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy per GPU,
+ * held until the process ends.  The call allocates and frees nothing.
+ *   - A call whose scratch need (svdq_w4a4_workspace_bytes of its arguments)
+ *     exceeds SVDQ_NOALLOC_SCRATCH_BYTES returns SVDQ_EWORKSPACE and writes
+ *     nothing; with K = 3072 that is M up to about 10400 tokens for int4
+ *     rank 32 (M = 4096 needs 25.7 MB; M = 512, whose product is split along
+ *     K, 53.5 MB).
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *     time on one GPU (different streams, or host threads) race and give
+ *     undefined results; calls on one stream are ordered and safe.  No part
+ *     of the scratch needs to start at zero.
+ *   - The first call on a device looks up that device's copy of the array
+ *     (hipGetSymbolAddress); later calls only launch.
+ * Arguments, results and other rules as for svdq_w4a4_linear, whose output
+ * this reproduces bit for bit. */
+#define SVDQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int svdq_w4a4_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t N,
+                             const void* packed_w, const void* wscales, float wtscale,
+                             const void* smooth, const void* lora_down, const void* lora_up,
+                             const void* bias, int precision, int group_size, int rank,
+                             void* out, void* stream);
+
 /* AWQ W4A16 linear ("Supported quantization types": awq_w4a16, int4, group 64).
  *
  *   Y = X ((q - z) * s)^T + bias, fp32 accumulation, bf16 output.
