@@ -248,14 +248,12 @@ Carve carve(void* workspace, int64_t M, int64_t K, int precision) {
   return c;
 }
 
-// Kernel 1 into the workspace; `clear` (clear_n floats, optional) is set to
-// zero by the same launch.
+// Kernel 1 into the workspace.
 int launch_quantize(const void* x, int64_t M, int64_t K, const void* smooth, const void* lora_down,
-                    int precision, int rank, void* workspace, hipStream_t s, float* clear = nullptr,
-                    int64_t clear_n = 0) {
+                    int precision, int rank, void* workspace, hipStream_t s) {
   const Carve c = carve(workspace, M, K, precision);
   svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, c.lora_act, c.act_f16, c.row_scale,
-                        M, K, precision, rank, clear, clear_n};
+                        M, K, precision, rank};
   return launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
 }
 
@@ -300,9 +298,15 @@ int validate_layer(int64_t M, const svdq_w4a4_layer* L, const char* which) {
   return SVDQ_OK;
 }
 
+// The fused MLP's workspace: the up layer's (no split partials), the down
+// layer's linear workspace, then the down layer's low-rank partials of the up
+// projection's column tiles, fp32 [ceil(H / 192), M, down rank].
+size_t mlp_tiles(const svdq_w4a4_layer* up) { return size_t((up->N + 191) / 192); }
+
 size_t mlp_workspace_bytes(int64_t M, const svdq_w4a4_layer* up, const svdq_w4a4_layer* down) {
   return workspace_bytes(M, up->K, up->precision, up->rank) +
-         linear_workspace_bytes(M, down->K, down->N, SVDQ_NVFP4, down->rank);
+         linear_workspace_bytes(M, down->K, down->N, SVDQ_NVFP4, down->rank) +
+         round_up(mlp_tiles(up) * size_t(M) * size_t(down->rank) * 4);
 }
 
 int validate_mlp(const void* x, int64_t M, const svdq_w4a4_layer* up, const svdq_w4a4_layer* down,
@@ -907,18 +911,25 @@ int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up, cons
   const Carve cu = carve(workspace, M, up->K, up->precision);
   void* ws_down = static_cast<uint8_t*>(workspace) + workspace_bytes(M, up->K, up->precision, up->rank);
   const Carve cd = carve(ws_down, M, H, SVDQ_NVFP4);
-  // up layer: kernel 1 into the first part of the workspace; the same launch
-  // clears the down layer's low-rank accumulator
-  rc = launch_quantize(x, M, up->K, up->smooth, up->lora_down, up->precision, up->rank, workspace, s,
-                       cd.lora_act, M * down->rank);
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws_down) +
+                                        linear_workspace_bytes(M, H, down->N, SVDQ_NVFP4, down->rank));
+  // up layer: kernel 1 into the first part of the workspace
+  rc = launch_quantize(x, M, up->K, up->smooth, up->lora_down, up->precision, up->rank, workspace, s);
   if (rc) return rc;
   // up layer: kernel 2 with the GELU + nvfp4 epilogue writing the down
-  // layer's workspace (its bf16 output is not stored)
+  // layer's operand and its column tiles' low-rank partials (the up layer's
+  // bf16 output is not stored)
   svdq::GemmArgs ga{cu.act_f16, cu.row_scale, cu.lora_act, up->packed_w, up->wscales, up->lora_up, up->bias,
                     nullptr, nullptr, up->wtscale, M, up->K, H, up->precision, up->rank,
-                    down->smooth, down->lora_down, cd.act_f16, cd.lora_act, down->rank};
+                    down->smooth, down->lora_down, cd.act_f16, part, down->rank};
   rc = launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up (GELU epilogue) launch");
   if (rc) return rc;
+  // the down layer's low-rank activations: the tiles' partials added in order
+  if (down->rank > 0) {
+    rc = launch_status(svdq::launch_tile_partial_sum(part, int(mlp_tiles(up)), M * down->rank, cd.lora_act, s),
+                       "low-rank partial sum launch");
+    if (rc) return rc;
+  }
   // down layer: kernel 2 from its workspace
   return launch_gemm(ws_down, M, H, down->N, down->packed_w, down->wscales, down->wtscale, down->lora_up,
                      down->bias, SVDQ_NVFP4, down->rank, out, s);

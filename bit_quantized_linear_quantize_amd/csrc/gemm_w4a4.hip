@@ -151,10 +151,13 @@ constexpr int kGeluRow = 208;
 //  1. g = bf16(GELU(bf16(acc + bias))) -- the values a bf16 up output followed
 //     by a bf16 GELU would give; GELU by the table kGeluBf16 -- into the
 //     wave's LDS tile `tile_base` (+ 64 kGeluRow for odd waves);
-//  2. the next layer's low-rank activations: x = fl32(g * (1 / smooth_next))
-//     in the 16x16x32 bf16 operand layout, split hi + lo, times
-//     next_lora_down, added into next_lora_act with fp32 atomics (one
-//     partial per wave and tile);
+//  2. the next layer's low-rank activations of this tile's 192 columns: x =
+//     fl32(g * (1 / smooth_next)) in the 16x16x32 bf16 operand layout, split
+//     hi + lo, times next_lora_down.  After a workgroup barrier the two waves
+//     of a row group read both of their tiles, and each takes every other
+//     16-rank block over all 192 columns, so the tile's sum is formed in one
+//     place and stored (no atomics) as this column tile's partial,
+//     next_lora_part[tile, m, r]; a second kernel adds the tiles in order;
 //  3. lane l takes tile row l: the same x, nvfp4 per 16 columns
 //     (nvfp4_quant16, the quantize kernel's reading); the next layer's
 //     product operand e2m1 * dec(s8) as fp16 overwrites the lane's own tile
@@ -162,9 +165,12 @@ constexpr int kGeluRow = 208;
 //     consecutive 16-byte pieces of a row.
 // Columns past N have 1/smooth 0 (x = 0) and are not stored; rows past M are
 // not stored.
+// `pair` holds the tile bases of the waves (wm, 0) and (wm, 1) of this
+// wave's row group (their 64 x 96 blocks are tile columns 0..95 and 96..191).
 __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16 (&acc)[kIB][kJB], int m0, int n0,
                                                     int wave, int wm, int wn, int lane, int l32, int h,
-                                                    const float* nmu, uint8_t* tile_base) {
+                                                    const float* nmu, uint8_t* tile_base,
+                                                    const uint8_t* const (&pair)[2]) {
   const int M = (int)args.M, N = (int)args.N;
   uint8_t* gt = tile_base + (wave & 1) * (64 * kGeluRow);
   // every wave has left the main loop (its LDS reads are done) and every
@@ -190,21 +196,27 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
   }
   // (the wave's own LDS writes and reads execute in order)
 
-  // 2 and 3 both read the next layer's 1 / smooth of this wave's columns
+  // 3 reads the next layer's 1 / smooth of this wave's columns
   const float* mu = nmu + wn * (kJB * 32);
-  // 2. the next layer's low-rank down projection of this tile's columns (it
-  // reads the GELU values before step 3 replaces them)
+  // 2. the next layer's low-rank down projection of this tile's 192 columns
+  // (it reads the GELU values of both waves of the row group, before step 3
+  // replaces them)
+  lds_barrier();  // every wave's GELU tile is complete
   const int nrank = args.next_rank;
   if (nrank > 0) {
     const int r16 = lane & 15, q = lane >> 4;
-    bf16x8 ahi[4][3], alo[4][3];
+    const int nt = n0 / kBN;
+    // next_lora_down [nrank, N]: reads past the end of the array return zero
+    const __amdgpu_buffer_rsrc_t ld_rs = make_rsrc(args.next_lora_down, (size_t)nrank * N * 2);
+#pragma unroll 1
+    for (int rb = 0; rb < 4; ++rb) {
+      bf16x8 ahi[6], alo[6];
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
-      const f32x4 mu0 = *(const f32x4*)(mu + ks * 32 + 8 * q);
-      const f32x4 mu1 = *(const f32x4*)(mu + ks * 32 + 8 * q + 4);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const u32x4 g = *(const u32x4*)(gt + (rb * 16 + r16) * kGeluRow + (ks * 32 + 8 * q) * 2);
+      for (int ks = 0; ks < 6; ++ks) {
+        const uint8_t* t = pair[ks / 3] + (rb * 16 + r16) * kGeluRow + ((ks % 3) * 32 + 8 * q) * 2;
+        const u32x4 g = *(const u32x4*)t;
+        const f32x4 mu0 = *(const f32x4*)(nmu + ks * 32 + 8 * q);
+        const f32x4 mu1 = *(const f32x4*)(nmu + ks * 32 + 8 * q + 4);
         u32x4 hi4, lo4;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -214,36 +226,28 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
           hi4[p] = hh;
           lo4[p] = bf16x2_rne(__fsub_rn(a, bf16_lo(hh)), __fsub_rn(b, bf16_hi(hh)));
         }
-        ahi[rb][ks] = __builtin_bit_cast(bf16x8, hi4);
-        alo[rb][ks] = __builtin_bit_cast(bf16x8, lo4);
+        ahi[ks] = __builtin_bit_cast(bf16x8, hi4);
+        alo[ks] = __builtin_bit_cast(bf16x8, lo4);
       }
-    }
-    // next_lora_down [nrank, N]: reads past the end of the array return zero
-    const __amdgpu_buffer_rsrc_t ld_rs = make_rsrc(args.next_lora_down, (size_t)nrank * N * 2);
-    for (int rk = 0; rk < nrank; rk += 16) {
-      bf16x8 b[3];
-#pragma unroll
-      for (int ks = 0; ks < 3; ++ks)
-        b[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                               ld_rs, ((rk + r16) * N + n0 + wn * (kJB * 32) + ks * 32 + 8 * q) * 2,
-                                               0, 0));
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
+      for (int rk = 16 * wn; rk < nrank; rk += 32) {
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 3; ++ks) {
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[rb][ks], b[ks], d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[rb][ks], b[ks], d, 0, 0, 0);
+        for (int ks = 0; ks < 6; ++ks) {
+          const bf16x8 b = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ld_rs, ((rk + r16) * N + n0 + ks * 32 + 8 * q) * 2, 0, 0));
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], b, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], b, d, 0, 0, 0);
         }
         // D: lane (c, q) holds rows 4q + j of the row block, rank column c
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int m = m0 + wm * 64 + rb * 16 + 4 * q + j;
-          if (m < M) unsafeAtomicAdd(args.next_lora_act + (size_t)m * nrank + rk + r16, d[j]);
+          if (m < M) args.next_lora_part[((size_t)nt * M + m) * nrank + rk + r16] = d[j];
         }
       }
     }
   }
+  lds_barrier();  // the partner wave has read this wave's tile
 
   // 3. quantization for the next layer, one tile row per lane; each group's
   // fp16 operand replaces its GELU values in the lane's own tile row, then
@@ -763,8 +767,11 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       }
     }
     if constexpr (EPI == kEpiGelu) {
+      // tile of wave w: base (w < 2: a0, < 4: a1, < 6: a2, else w0) + (w & 1) 64 rows
+      const uint8_t* const pair[2] = {(wm < 2 ? lds_a0 : lds_a1) + (wm & 1) * (64 * kGeluRow),
+                                      (wm < 2 ? lds_a2 : lds_w0) + (wm & 1) * (64 * kGeluRow)};
       gelu_quant_epilogue(args, acc, m0, n0, wave, wm, wn, lane, l32, h, nmu,
-                          wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0);
+                          wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, pair);
     } else if constexpr (kQk) {
       qk_norm_rope_epilogue(args, acc, m0, nt, wave, wm, wn, lane, l32, h,
                             wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, (float*)lds_w1);
@@ -869,6 +876,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     o[c] = f32_to_bf16_bits(acc[2 * c] + b0) | (f32_to_bf16_bits(acc[2 * c + 1] + b1) << 16);
   }
   *(u32x4*)(out + i) = o;
+}
+
+// out[i] = sum_t part[t, i], t = 0 .. tiles-1 in order (the fused MLP's
+// low-rank activations of the down layer from the up projection's column tiles)
+__global__ __launch_bounds__(256) void tile_partial_sum_kernel(const float* __restrict__ part, int tiles, int64_t n,
+                                                               float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float a = 0.f;
+  for (int t = 0; t < tiles; ++t) a += part[(size_t)t * n + i];
+  out[i] = a;
+}
+
+hipError_t launch_tile_partial_sum(const float* part, int tiles, int64_t n, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(tile_partial_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, part, tiles, n,
+                     out);
+  return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N, const void* bias, void* out,

@@ -20,8 +20,6 @@ struct QuantActArgs {
   float* row_scale;       // linear int4 only: f32 [M] power-of-two factor of each row of act_f16
   int64_t M, K;
   int precision, rank;
-  float* clear = nullptr;  // optional: f32 [clear_n] set to zero by the same launch (the fused
-  int64_t clear_n = 0;     // MLP's accumulator for the next layer's low-rank activations)
 };
 
 // act_f16 holds the dequantized activations exactly: int4 q * s * 2^-E[m]
@@ -47,7 +45,7 @@ struct GemmArgs {
   const void* next_smooth = nullptr;     // bf16 [N]
   const void* next_lora_down = nullptr;  // bf16 [next_rank, N] or null
   void* next_act = nullptr;              // f16 [M, N]: the next layer's product operand e2m1 * dec(s8)
-  float* next_lora_act = nullptr;        // f32 [M, next_rank], zero on entry, accumulated with atomics
+  float* next_lora_part = nullptr;       // f32 [column tiles, M, next_rank]: each tile's partial sum
   int next_rank = 0;
   // QKV fusion (heads > 0): N = 3 heads 128 columns q | k | v.  Column tile t
   // of the 2 heads tiles computes head t of q | k and v columns 64 t ..
@@ -123,6 +121,8 @@ hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N, const void* bias, void* out,
                                 hipStream_t stream);
 hipError_t launch_gelu_table_copy(uint16_t* out, hipStream_t stream);
+// out[i] = sum_t part[t, i] over t = 0 .. tiles-1 in order, i < n
+hipError_t launch_tile_partial_sum(const float* part, int tiles, int64_t n, float* out, hipStream_t stream);
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream);
 
 }  // namespace svdq

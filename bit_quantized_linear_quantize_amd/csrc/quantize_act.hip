@@ -22,7 +22,9 @@
 // of the 16x16x32 bf16 matrix instruction used for the low-rank product.  X_hat
 // is split into bf16 hi + lo parts so the low-rank product keeps ~16 bits.
 // The per-wave low-rank partials are summed in LDS in a fixed order
-// (deterministic).  Loads of X are 16 bytes per lane, several chunks in flight.
+// (deterministic).  Loads of X are 16 bytes per lane, several chunks in
+// flight; the first ones are issued before the workgroup computes its table
+// of 1 / smooth.
 //
 // Outputs.  The parity export writes packed nibbles (low nibble = even
 // column), the group scales and lora_act.  Inside svdq_w4a4_linear the kernel
@@ -73,16 +75,6 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-
-  // optional side job: clear args.clear (grid-stride over all workgroups)
-  if constexpr (LINEAR) {
-    for (int64_t i = (int64_t)blockIdx.x * kK1Threads + tid; i < args.clear_n; i += (int64_t)gridDim.x * kK1Threads)
-      args.clear[i] = 0.f;
-  }
-
-  // 1 / smooth for every input channel (IEEE division, one per channel).
-  for (int k = tid; k < K; k += kK1Threads) lds[k] = __fdiv_rn(1.0f, bf16_bits_to_f32(smooth[k]));
-  __syncthreads();
 
   const int r = lane & 15;
   const int q = lane >> 4;
@@ -176,6 +168,11 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
 
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, wave + p * kK1Waves);
+
+  // 1 / smooth for every input channel (IEEE division, one per channel),
+  // computed while the first chunks are in flight
+  for (int k = tid; k < K; k += kK1Threads) lds[k] = __fdiv_rn(1.0f, bf16_bits_to_f32(smooth[k]));
+  __syncthreads();
 
   for (int base = wave; base < nchunks; base += PF * kK1Waves) {
 #pragma unroll

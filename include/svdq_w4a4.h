@@ -174,7 +174,9 @@ typedef struct svdq_w4a4_layer {
  * row factors and low-rank activations (as in svdq_w4a4_workspace_bytes, no
  * split partials) followed by the down layer's linear workspace (its fp16
  * product operand [M, H], fp32 low-rank activations [M, down->rank] and, for
- * small M x N, its split-K partials).  Returns 0 for arguments
+ * small M x N, its split-K partials), then fp32 partial sums of the down
+ * layer's low-rank activations per 192-column tile of the up projection
+ * [ceil(H / 192), M, down->rank].  Returns 0 for arguments
  * svdq_w4a4_mlp_gelu would reject. */
 size_t svdq_w4a4_mlp_workspace_bytes(int64_t M, const svdq_w4a4_layer* up,
                                      const svdq_w4a4_layer* down);
@@ -188,9 +190,10 @@ size_t svdq_w4a4_mlp_workspace_bytes(int64_t M, const svdq_w4a4_layer* up,
  *
  * The values are those of svdq_w4a4_linear(up), a bf16 GELU of its output and
  * svdq_w4a4_linear(down) on that, except that the down layer's low-rank
- * activations are summed over the up projection's column tiles with fp32
- * atomics: their rounding (and so the last bit of some outputs) may differ
- * from run to run.
+ * activations are summed per 192-column tile of the up projection and the
+ * tiles' sums then added in order (not in the quantize kernel's order), so
+ * their last bits may differ from the unfused chain's.  The result is
+ * deterministic: the same inputs give the same bits on every call.
  *
  * x      bf16 [M, up->K]; H = up->N must equal down->K
  * up     any svdq_w4a4 layer (int4 or nvfp4)

@@ -248,9 +248,12 @@ def test_mlp_rules(L):
     B = ctypes.byref
     need = L.svdq_w4a4_mlp_workspace_bytes(M, B(up), B(down))
     rnd = lambda v: (v + 255) // 256 * 256
-    # the up layer's operand, row factors and lora_act, then the down layer's linear workspace
+    # the up layer's operand, row factors and lora_act, the down layer's linear
+    # workspace, then the down layer's low-rank partials per 192-column tile
+    # of the up projection
     assert need == (rnd(2 * M * K) + rnd(4 * M) + rnd(4 * M * 32)) + (rnd(2 * M * H) + rnd(4 * M * 32) +
-                                                                      split_bytes(M, N, H))
+                                                                      split_bytes(M, N, H)) + \
+        rnd(4 * ((H + 191) // 192) * M * 32)
 
     def call(x=x, M=M, up=up, down=down, out=out, ws=ws, wsb=need, arch=GFX950):
         p = lambda v: None if v is None else _fake(v)

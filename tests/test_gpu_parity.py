@@ -611,6 +611,23 @@ def test_mlp_gelu_fused_ragged(M, up_prec, ranks):
     assert_output(y, y_ref, f"fused mlp M={M} {up_prec} r{ranks}")
 
 
+def test_mlp_gelu_deterministic():
+    # the down layer's low-rank activations are summed per column tile and
+    # the tiles added in order: the same inputs give the same bits, whatever
+    # the workspace held before
+    rng = np.random.default_rng(2)
+    x, lay_up = exact_up_problem(300, 256, 640, "nvfp4", 32, rng)
+    lay_down, _ = fused_mlp_ref(x[:4], lay_up, S.weight(320, 640, 0.02, rng), S.bias(320, rng), 32)
+    up, down = bq.SVDQLinear.from_numpy(lay_up), bq.SVDQLinear.from_numpy(lay_down)
+    xd = dev_bf16(x)
+    need = bq.mlp_workspace_bytes(300, up, down)
+    outs = []
+    for poison in (0x00, 0xFF, 0x7F):
+        ws = torch.full((need,), poison, dtype=torch.uint8, device="cuda")
+        outs.append(host_bits(bq.svdq_w4a4_mlp_gelu(xd, up, down, workspace=ws)))
+    assert all(np.array_equal(o, outs[0]) for o in outs[1:])
+
+
 def test_mlp_gelu_rejects_int4_down():
     rng = np.random.default_rng(5)
     x = S.activations(64, 256, 0, rng)

@@ -218,6 +218,5 @@ def test_fused_compile_fullgraph(fused_layers, backend):
     got_q, got_y = torch.compile(f, fullgraph=True, backend=backend)(xd)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(got_q), host_bits(ref_q))
-    _, excess, mre = L.output_errors(F.bf16_to_f32(host_bits(got_y)).astype(np.float64),
-                                     F.bf16_to_f32(host_bits(ref_y)).astype(np.float64))
-    assert excess <= 1e-3 and mre <= 1e-3
+    # the fused MLP is deterministic: the compiled call gives the eager bits
+    assert np.array_equal(host_bits(got_y), host_bits(ref_y))
