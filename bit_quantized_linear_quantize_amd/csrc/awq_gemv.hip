@@ -439,21 +439,18 @@ static hipError_t launch_awq_gemv1(const AwqArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#ifndef AWQ_V1_ROWS
-#define AWQ_V1_ROWS 4
-#endif
+// weight rows per wave of the one-token kernel (4 measured fastest of 2..16)
+constexpr int kAwqGemvRows = 4;
 
 hipError_t launch_awq_gemv(const AwqArgs& a, hipStream_t stream) {
-#ifndef AWQ_NO_VALU
   if (a.M == 1 && a.K % 1024 == 0 && a.K <= 4096) {
     switch (a.K / 1024) {
-      case 1: return launch_awq_gemv1<AWQ_V1_ROWS, 1>(a, stream);
-      case 2: return launch_awq_gemv1<AWQ_V1_ROWS, 2>(a, stream);
-      case 3: return launch_awq_gemv1<AWQ_V1_ROWS, 3>(a, stream);
-      default: return launch_awq_gemv1<AWQ_V1_ROWS, 4>(a, stream);
+      case 1: return launch_awq_gemv1<kAwqGemvRows, 1>(a, stream);
+      case 2: return launch_awq_gemv1<kAwqGemvRows, 2>(a, stream);
+      case 3: return launch_awq_gemv1<kAwqGemvRows, 3>(a, stream);
+      default: return launch_awq_gemv1<kAwqGemvRows, 4>(a, stream);
     }
   }
-#endif
   if (a.M <= 2) return launch_awq_mt<2, 1>(a, stream);
   if (a.M <= 4) return launch_awq_mt<4, 1>(a, stream);
   return launch_awq_mt<16, 1>(a, stream);
