@@ -352,10 +352,14 @@ def warm_clock(fn, seconds, torch):
 
 
 def time_events(fn, steps, stream):
+    """Per-call time of `steps` eager calls of fn, bracketed by events on
+    `stream`.  One untimed call is queued before the start event, so the GPU
+    is already busy while the host issues the first timed call."""
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    fn()
     e0.record(stream)
     for _ in range(steps):
         fn()
@@ -387,6 +391,27 @@ def time_graph(calls, reps, stream):
     e1.record()
     e1.synchronize()
     return e0.elapsed_time(e1) / reps  # ms per replay
+
+
+def time_split(fns, steps, stream):
+    """Run the calls fns in order, `steps` times, with an event on `stream`
+    before and after each call; return each call's average duration in ms.
+    The durations are those the kernels have inside the step, between their
+    neighbours, rather than back to back with themselves (the product kernel
+    alone, launched back to back, runs several percent slower: the chip's
+    clock drops under sustained matrix load)."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for f in fns:
+        f()
+    for row in ev:
+        row[0].record(stream)
+        for f, e in zip(fns, row[1:]):
+            f()
+            e.record(stream)
+    torch.cuda.synchronize()
+    return [sum(row[i].elapsed_time(row[i + 1]) for row in ev) / steps for i in range(len(fns))]
 
 
 ONLY_LEGS = {"quant_int4", "quant_nvfp4", "gemm_int4", "gemm_nvfp4", "awq_m1", "awq_m16", "mlp_fused", "qkv_fused",
@@ -615,8 +640,10 @@ def main():
         for _ in range(warmup):
             k1()
             k2()
-        t1 = time_events(k1, steps, stream)
-        t2 = time_events(k2, steps, stream)
+        # each kernel's own duration inside the step: events around kernel 1
+        # and kernel 2 of every timed step (a separate pass, so that the extra
+        # event packets stay out of the step figure above)
+        t1, t2 = time_split((k1, k2), steps, stream)
         sb = 2 if precision == "int4" else 1
         # algorithmic bytes of kernel 1: read x, smooth, lora_down; write 4-bit codes
         # (counted at 4 bits although the workspace keeps fp16 operands), scales, lora_act

@@ -138,6 +138,10 @@ __device__ __forceinline__ void tile_of(int bid, int nmt, int nnt, int& mt, int&
 // bf16 columns, rows padded to 208 bytes (conflict-free row-wise and
 // operand-layout reads).
 constexpr int kGeluRow = 208;
+// the fused MLP's low-rank exchange: rows of 32 sums + 4 pad floats, so that
+// the four 16-lane quarters of a wave write distinct banks
+constexpr int kXchRow = 36;
+static_assert(2 * kWM * 16 * kXchRow * 4 <= kBN * kWRow, "the exchange fits the second W buffer");
 
 // GELU with the exact erf of every bf16 value, rounded to bf16 (the table is
 // generated at build time in double precision: gelu_bf16_gen.py).  The epilogue's
@@ -153,11 +157,11 @@ constexpr int kGeluRow = 208;
 //     wave's LDS tile `tile_base` (+ 64 kGeluRow for odd waves);
 //  2. the next layer's low-rank activations of this tile's 192 columns: x =
 //     fl32(g * (1 / smooth_next)) in the 16x16x32 bf16 operand layout, split
-//     hi + lo, times next_lora_down.  After a workgroup barrier the two waves
-//     of a row group read both of their tiles, and each takes every other
-//     16-rank block over all 192 columns, so the tile's sum is formed in one
-//     place and stored (no atomics) as this column tile's partial,
-//     next_lora_part[tile, m, r]; a second kernel adds the tiles in order;
+//     hi + lo, times next_lora_down.  Each wave takes its own 96 columns; the
+//     two waves of a row group add their sums through LDS in a fixed order,
+//     and the tile's sum is stored (no atomics) as this column tile's
+//     partial, next_lora_part[tile, m, r]; a second kernel adds the tiles in
+//     order;
 //  3. lane l takes tile row l: the same x, nvfp4 per 16 columns
 //     (nvfp4_quant16, the quantize kernel's reading); the next layer's
 //     product operand e2m1 * dec(s8) as fp16 overwrites the lane's own tile
@@ -165,12 +169,10 @@ constexpr int kGeluRow = 208;
 //     consecutive 16-byte pieces of a row.
 // Columns past N have 1/smooth 0 (x = 0) and are not stored; rows past M are
 // not stored.
-// `pair` holds the tile bases of the waves (wm, 0) and (wm, 1) of this
-// wave's row group (their 64 x 96 blocks are tile columns 0..95 and 96..191).
+// `xch` is LDS of 2 kWM 16 kXchRow floats, free during this epilogue.
 __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16 (&acc)[kIB][kJB], int m0, int n0,
                                                     int wave, int wm, int wn, int lane, int l32, int h,
-                                                    const float* nmu, uint8_t* tile_base,
-                                                    const uint8_t* const (&pair)[2]) {
+                                                    const float* nmu, uint8_t* tile_base, float* xch) {
   const int M = (int)args.M, N = (int)args.N;
   uint8_t* gt = tile_base + (wave & 1) * (64 * kGeluRow);
   // every wave has left the main loop (its LDS reads are done) and every
@@ -196,58 +198,84 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
   }
   // (the wave's own LDS writes and reads execute in order)
 
-  // 3 reads the next layer's 1 / smooth of this wave's columns
+  // 2 and 3 read the next layer's 1 / smooth of this wave's columns
   const float* mu = nmu + wn * (kJB * 32);
-  // 2. the next layer's low-rank down projection of this tile's 192 columns
-  // (it reads the GELU values of both waves of the row group, before step 3
-  // replaces them)
-  lds_barrier();  // every wave's GELU tile is complete
+  // 2. the next layer's low-rank down projection of this wave's 96 columns
+  // (its own GELU tile, in program order after step 1), 16 tile rows and 32
+  // ranks at a time; the wave wn = 1 hands its sums to the wave wn = 0 of
+  // its row group through `xch`, which adds them to its own (in that order)
+  // and stores the column tile's partial.  xch alternates between two halves,
+  // so one workgroup barrier per exchange suffices.
   const int nrank = args.next_rank;
   if (nrank > 0) {
     const int r16 = lane & 15, q = lane >> 4;
     const int nt = n0 / kBN;
     // next_lora_down [nrank, N]: reads past the end of the array return zero
     const __amdgpu_buffer_rsrc_t ld_rs = make_rsrc(args.next_lora_down, (size_t)nrank * N * 2);
+    int parity = 0;
 #pragma unroll 1
-    for (int rb = 0; rb < 4; ++rb) {
-      bf16x8 ahi[6], alo[6];
+    for (int rc = 0; rc < nrank; rc += 32) {
+#pragma unroll 1
+      for (int rb = 0; rb < 4; ++rb, parity ^= 1) {
+        bf16x8 ahi[kJB], alo[kJB];
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) {
-        const uint8_t* t = pair[ks / 3] + (rb * 16 + r16) * kGeluRow + ((ks % 3) * 32 + 8 * q) * 2;
-        const u32x4 g = *(const u32x4*)t;
-        const f32x4 mu0 = *(const f32x4*)(nmu + ks * 32 + 8 * q);
-        const f32x4 mu1 = *(const f32x4*)(nmu + ks * 32 + 8 * q + 4);
-        u32x4 hi4, lo4;
+        for (int ks = 0; ks < kJB; ++ks) {
+          const u32x4 g = *(const u32x4*)(gt + (rb * 16 + r16) * kGeluRow + (ks * 32 + 8 * q) * 2);
+          const f32x4 mu0 = *(const f32x4*)(mu + ks * 32 + 8 * q);
+          const f32x4 mu1 = *(const f32x4*)(mu + ks * 32 + 8 * q + 4);
+          u32x4 hi4, lo4;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float a = __fmul_rn(bf16_lo(g[p]), p < 2 ? mu0[2 * p] : mu1[2 * p - 4]);
-          const float b = __fmul_rn(bf16_hi(g[p]), p < 2 ? mu0[2 * p + 1] : mu1[2 * p - 3]);
-          const uint32_t hh = bf16x2_rne(a, b);
-          hi4[p] = hh;
-          lo4[p] = bf16x2_rne(__fsub_rn(a, bf16_lo(hh)), __fsub_rn(b, bf16_hi(hh)));
+          for (int p = 0; p < 4; ++p) {
+            const float a = __fmul_rn(bf16_lo(g[p]), p < 2 ? mu0[2 * p] : mu1[2 * p - 4]);
+            const float b = __fmul_rn(bf16_hi(g[p]), p < 2 ? mu0[2 * p + 1] : mu1[2 * p - 3]);
+            const uint32_t hh = bf16x2_rne(a, b);
+            hi4[p] = hh;
+            lo4[p] = bf16x2_rne(__fsub_rn(a, bf16_lo(hh)), __fsub_rn(b, bf16_hi(hh)));
+          }
+          ahi[ks] = __builtin_bit_cast(bf16x8, hi4);
+          alo[ks] = __builtin_bit_cast(bf16x8, lo4);
         }
-        ahi[ks] = __builtin_bit_cast(bf16x8, hi4);
-        alo[ks] = __builtin_bit_cast(bf16x8, lo4);
-      }
-      for (int rk = 16 * wn; rk < nrank; rk += 32) {
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        f32x4 d[2];
 #pragma unroll
-        for (int ks = 0; ks < 6; ++ks) {
-          const bf16x8 b = __builtin_bit_cast(
-              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ld_rs, ((rk + r16) * N + n0 + ks * 32 + 8 * q) * 2, 0, 0));
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], b, d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], b, d, 0, 0, 0);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int rk = rc + 16 * h2;
+          d[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (rk < nrank) {
+#pragma unroll
+            for (int ks = 0; ks < kJB; ++ks) {
+              const bf16x8 b = __builtin_bit_cast(
+                  bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                              ld_rs, ((rk + r16) * N + n0 + wn * (kJB * 32) + ks * 32 + 8 * q) * 2, 0, 0));
+              d[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], b, d[h2], 0, 0, 0);
+              d[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], b, d[h2], 0, 0, 0);
+            }
+          }
         }
         // D: lane (c, q) holds rows 4q + j of the row block, rank column c
+        float* xb = xch + (parity * kWM + wm) * (16 * kXchRow);
+        if (wn == 1) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = m0 + wm * 64 + rb * 16 + 4 * q + j;
-          if (m < M) args.next_lora_part[((size_t)nt * M + m) * nrank + rk + r16] = d[j];
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xb[(4 * q + j) * kXchRow + 16 * h2 + r16] = d[h2][j];
+        }
+        lds_barrier();
+        if (wn == 0) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int rk = rc + 16 * h2;
+            if (rk >= nrank) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int m = m0 + wm * 64 + rb * 16 + 4 * q + j;
+              const float v = __fadd_rn(d[h2][j], xb[(4 * q + j) * kXchRow + 16 * h2 + r16]);
+              if (m < M) args.next_lora_part[((size_t)nt * M + m) * nrank + rk + r16] = v;
+            }
+          }
         }
       }
     }
   }
-  lds_barrier();  // the partner wave has read this wave's tile
 
   // 3. quantization for the next layer, one tile row per lane; each group's
   // fp16 operand replaces its GELU values in the lane's own tile row, then
@@ -768,10 +796,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     }
     if constexpr (EPI == kEpiGelu) {
       // tile of wave w: base (w < 2: a0, < 4: a1, < 6: a2, else w0) + (w & 1) 64 rows
-      const uint8_t* const pair[2] = {(wm < 2 ? lds_a0 : lds_a1) + (wm & 1) * (64 * kGeluRow),
-                                      (wm < 2 ? lds_a2 : lds_w0) + (wm & 1) * (64 * kGeluRow)};
       gelu_quant_epilogue(args, acc, m0, n0, wave, wm, wn, lane, l32, h, nmu,
-                          wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, pair);
+                          wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, (float*)lds_w1);
     } else if constexpr (kQk) {
       qk_norm_rope_epilogue(args, acc, m0, nt, wave, wm, wn, lane, l32, h,
                             wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, (float*)lds_w1);
@@ -879,18 +905,37 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // out[i] = sum_t part[t, i], t = 0 .. tiles-1 in order (the fused MLP's
-// low-rank activations of the down layer from the up projection's column tiles)
-__global__ __launch_bounds__(256) void tile_partial_sum_kernel(const float* __restrict__ part, int tiles, int64_t n,
-                                                               float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float a = 0.f;
-  for (int t = 0; t < tiles; ++t) a += part[(size_t)t * n + i];
-  out[i] = a;
+// low-rank activations of the down layer from the up projection's column
+// tiles).  A thread sums four consecutive floats; the loads of eight tiles
+// are issued before their additions, which stay in tile order.
+__global__ __launch_bounds__(64) void tile_partial_sum_kernel(const float* __restrict__ part, int tiles, int64_t n4,
+                                                              float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* p = (const f32x4*)part + i;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  int t = 0;
+  for (; t + 8 <= tiles; t += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + (size_t)(t + u) * n4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] = __fadd_rn(a[c], v[u][c]);
+  }
+  for (; t < tiles; ++t) {
+    const f32x4 v = __builtin_nontemporal_load(p + (size_t)t * n4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[c] = __fadd_rn(a[c], v[c]);
+  }
+  ((f32x4*)out)[i] = a;
 }
 
+// n must be a multiple of 4 (M * rank, rank a multiple of 16)
 hipError_t launch_tile_partial_sum(const float* part, int tiles, int64_t n, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(tile_partial_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, part, tiles, n,
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(tile_partial_sum_kernel, dim3((unsigned)((n4 + 63) / 64)), dim3(64), 0, stream, part, tiles, n4,
                      out);
   return hipGetLastError();
 }
