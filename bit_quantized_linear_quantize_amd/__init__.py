@@ -334,9 +334,10 @@ def svdq_w4a4_mlp_gelu(x, up, down, out=None, workspace=None, stream=None):
 def svdq_w4a4_qkv_rmsnorm_rope(x, qkv, heads, q_norm, k_norm, rope_cos, rope_sin, eps=1e-6, out=None,
                                workspace=None, stream=None):
     """Fused QKV projection: q | k | v = qkv(x) with per-head RMSNorm (weights
-    q_norm / k_norm, bf16 [128]) and RoPE (rope_cos / rope_sin, fp32 [M, 64],
-    interleaved pairs) applied to the q and k heads in the projection's
-    epilogue; returns bf16 [M, 3 heads 128]."""
+    q_norm / k_norm, bf16 [D]; the head dim D = 32, 64 or 128 is their
+    length) and RoPE (rope_cos / rope_sin, fp32 [M, D/2], interleaved pairs)
+    applied to the q and k heads in the projection's epilogue; returns bf16
+    [M, 3 heads D]."""
     x = _x(x, qkv.K)
     M = x.shape[0]
     q = layer_struct(qkv)

@@ -345,9 +345,9 @@ int validate_mlp(const void* x, int64_t M, const svdq_w4a4_layer* up, const svdq
   return SVDQ_OK;
 }
 
-// QKV fusion: heads of 128 columns (the epilogue's column order needs two
-// heads' v columns per head: 2 * (192 - 128) == 128)
-constexpr int kQkvHeadDim = 128;
+// QKV fusion: heads of 32, 64 or 128 columns (a column tile holds 128 q | k
+// columns, whole heads, and 64 v columns, so heads * head_dim must be a
+// multiple of 64)
 constexpr int kQkvMaxHeads = 256;
 
 int validate_qkv(const void* x, int64_t M, const svdq_w4a4_layer* qkv, int heads, int head_dim,
@@ -355,8 +355,11 @@ int validate_qkv(const void* x, int64_t M, const svdq_w4a4_layer* qkv, int heads
                  const float* rope_sin, const void* out, const void* workspace, size_t ws_bytes) {
   int rc = validate_layer(M, qkv, "qkv");
   if (rc) return rc;
-  if (head_dim != kQkvHeadDim) return fail(SVDQ_EUNSUPPORTED, "head_dim must be 128");
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(SVDQ_EUNSUPPORTED, "head_dim must be 32, 64 or 128");
   if (heads < 1 || heads > kQkvMaxHeads) return fail(SVDQ_EINVAL, "heads must be in [1, 256]");
+  if ((heads * head_dim) % 64 != 0)
+    return fail(SVDQ_EUNSUPPORTED, "heads * head_dim must be a multiple of 64 (head_dim 32: an even head count)");
   if (qkv->N != int64_t(3) * heads * head_dim) return fail(SVDQ_EINVAL, "qkv->N must equal 3 * heads * head_dim");
   if (!(std::isfinite(eps) && eps > 0.f)) return fail(SVDQ_EINVAL, "eps must be finite and positive");
   if (!x || !out || !workspace || !q_norm || !k_norm || !rope_cos || !rope_sin)
@@ -969,6 +972,7 @@ int svdq_w4a4_qkv_rmsnorm_rope(const void* x, int64_t M, const svdq_w4a4_layer* 
   ga.rope_sin = rope_sin;
   ga.eps = eps;
   ga.heads = heads;
+  ga.head_dim = head_dim;
   return launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up (RMSNorm + RoPE epilogue) launch");
 }
 

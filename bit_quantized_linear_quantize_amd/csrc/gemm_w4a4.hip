@@ -78,15 +78,15 @@ constexpr int kEpiGelu = 1;
 constexpr int kEpiQk = 2;
 constexpr int kEpiSplit = 3;  // split K: fp32 partials
 
-// QKV fusion column order.  The output is q | k | v with heads of 128
-// columns; a 192-column tile cannot hold whole heads of q or k in the natural
-// order, so column tile t of the 2 H tiles takes the 128 columns of head t
-// of q | k and 64 columns of v (two tiles' v columns make one head), and
-// RMSNorm needs no data from another workgroup.
-constexpr int kHeadDim = 128;
-static_assert(2 * (kBN - kHeadDim) == kHeadDim, "the v columns of two tiles make one head");
+// QKV fusion column order.  The output is q | k | v with heads of D = 32, 64
+// or 128 consecutive columns; a 192-column tile cannot hold whole heads of q
+// or k in the natural order, so column tile t takes the 128 q | k columns
+// 128 t .. 128 t + 127 (whole heads: 128 / D of them) and the 64 v columns
+// 64 t .. 64 t + 63, and RMSNorm needs no data from another workgroup.
+constexpr int kQkCols = 128;  // q | k columns per tile
+static_assert(kBN - kQkCols == 64, "64 v columns per tile");
 __device__ __forceinline__ int qk_col(int nt, int c, int qk_cols) {
-  return c < kHeadDim ? nt * kHeadDim + c : qk_cols + nt * (kBN - kHeadDim) + (c - kHeadDim);
+  return c < kQkCols ? nt * kQkCols + c : qk_cols + nt * (kBN - kQkCols) + (c - kQkCols);
 }
 
 // Workgroup barrier for the main loop: this wave's LDS reads and writes are
@@ -319,24 +319,27 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
 // The QKV fusion epilogue of one wave ("Fused kernels" of the Nunchaku Lite
 // docs page: the Q, K and V projections merged with RMSNorm and RoPE).  acc
 // holds this wave's 64 x 96 block before the bias; tile columns 0..127 are
-// head nt of q | k (q for nt < heads), 128..191 v columns (qk_col).  Wave
-// column group wn = 0 holds head dims 0..95, wn = 1 head dims 96..127 and
-// the 64 v columns.  Steps:
+// the q | k heads 128 nt / D .. of this tile (head index below `heads`: q,
+// else k), 128..191 v columns (qk_col).  Wave column group wn = 0 holds tile
+// columns 0..95, wn = 1 columns 96..127 and the 64 v columns; a head may
+// span both (D = 64: head 1 of the tile; D = 128: the only one).  Steps:
 //  1. h = bf16(acc + bias) into the wave's LDS tile (rows of kGeluRow bytes);
-//  2. lane l takes tile row l: the sum of squares of its head columns; the
-//     two waves of a row block add theirs through LDS (`ssq`, in a fixed
-//     order) and r = 1 / sqrt(sum / 128 + eps);
+//  2. lane l takes tile row l: the sums of squares of its columns of each
+//     head; the two waves of a row block add theirs through LDS (`ssq`, in a
+//     fixed order: wn = 0 first) and r = 1 / sqrt(sum / D + eps) per head;
 //  3. each head pair (2i, 2i+1): n = bf16(fl32(fl32(h r) w_d)), then
 //     (n_a cos - n_b sin, n_a sin + n_b cos) in fp32, rounded to bf16 in
 //     place; v columns keep h;
 //  4. the wave stores the tile with consecutive lanes on consecutive 16-byte
 //     pieces of a row.
+// Pieces of 8 columns never cross a head edge (D is a multiple of 8).
 __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmArgs& args, f32x16 (&acc)[kIB][kJB], int m0, int nt,
                                                       int wave, int wm, int wn, int lane, int l32, int h,
                                                       uint8_t* tile_base, float* ssq) {
   const int M = (int)args.M, N = (int)args.N;
   const int heads = args.heads;
-  const int qk_cols = 2 * heads * kHeadDim;
+  const int D = args.head_dim;
+  const int qk_cols = 2 * heads * D;
   uint8_t* gt = tile_base + (wave & 1) * (64 * kGeluRow);
   // every wave has left the main loop and every direct-to-LDS load has landed
   // before the stage buffers are reused
@@ -361,48 +364,75 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmArgs& args, f32x
   }
   // (the wave's own LDS writes and reads execute in order)
 
-  // 2. RMSNorm factor of the lane's row
+  // 2. RMSNorm factors of the lane's row, one per head of the tile
+  constexpr int kMaxHeads = kQkCols / 32;
   uint8_t* rowp = gt + lane * kGeluRow;
-  const int nhead = wn == 0 ? kJB * 32 : kHeadDim - kJB * 32;  // head columns of this wave (96 | 32)
-  float ss = 0.f;
+  const int c0 = wn * (kJB * 32);                            // tile column of the wave's first column
+  const int nqk = wn == 0 ? kJB * 32 : kQkCols - kJB * 32;  // q | k columns of this wave (96 | 32)
+  float ss[kMaxHeads];
+#pragma unroll
+  for (int hh = 0; hh < kMaxHeads; ++hh) ss[hh] = 0.f;
 #pragma unroll
   for (int t = 0; t < 12; ++t) {
-    if (8 * t < nhead) {
+    if (8 * t < nqk) {
       const u32x4 v = *(const u32x4*)(rowp + 16 * t);
+      const int hl = (c0 + 8 * t) / D;  // head of the tile
+      float acc2 = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < kMaxHeads; ++hh) acc2 = hh == hl ? ss[hh] : acc2;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const float a = bf16_lo(v[p]), b = bf16_hi(v[p]);
-        ss = __fmaf_rn(a, a, ss);
-        ss = __fmaf_rn(b, b, ss);
+        acc2 = __fmaf_rn(a, a, acc2);
+        acc2 = __fmaf_rn(b, b, acc2);
       }
+#pragma unroll
+      for (int hh = 0; hh < kMaxHeads; ++hh) ss[hh] = hh == hl ? acc2 : ss[hh];
     }
   }
   const int trow = wm * 64 + lane;  // row of the workgroup tile
-  ssq[wn * kBM + trow] = ss;
+  const int nh = kQkCols / D;       // heads per tile
+#pragma unroll
+  for (int hh = 0; hh < kMaxHeads; ++hh)
+    if (hh < nh) ssq[(wn * kMaxHeads + hh) * kBM + trow] = ss[hh];
   lds_barrier();
-  const float tot = __fadd_rn(ssq[trow], ssq[kBM + trow]);
-  const float rr = __fdiv_rn(1.0f, __fsqrt_rn(__fmaf_rn(tot, 1.0f / kHeadDim, args.eps)));
+  float rr[kMaxHeads];
+  const float invd = 1.0f / (float)D;  // exact: D is a power of two
+#pragma unroll
+  for (int hh = 0; hh < kMaxHeads; ++hh) {
+    rr[hh] = 0.f;
+    if (hh < nh) {
+      const float tot = __fadd_rn(ssq[hh * kBM + trow], ssq[(kMaxHeads + hh) * kBM + trow]);
+      rr[hh] = __fdiv_rn(1.0f, __fsqrt_rn(__fmaf_rn(tot, invd, args.eps)));
+    }
+  }
 
   // 3. normalize and rotate the head columns in place
-  const uint32_t* nw = (const uint32_t*)(nt < heads ? args.q_norm : args.k_norm);  // bf16 pairs
   const int m = m0 + trow;
-  const size_t trow_off = (size_t)min(m, M - 1) * (kHeadDim / 2);
+  const size_t trow_off = (size_t)min(m, M - 1) * (D / 2);
   const float* cs = args.rope_cos + trow_off;
   const float* sn = args.rope_sin + trow_off;
-  const int d0 = wn * (kJB * 32);  // head dim of the wave's first column
 #pragma unroll
   for (int t = 0; t < 12; ++t) {
-    if (8 * t < nhead) {
+    if (8 * t < nqk) {
       const u32x4 v = *(const u32x4*)(rowp + 16 * t);
-      const int pr = (d0 + 8 * t) >> 1;  // first pair of the piece
+      const int tc = c0 + 8 * t;
+      const int hl = tc / D;
+      const int d = tc - hl * D;  // head dim of the piece's first column
+      float r = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < kMaxHeads; ++hh) r = hh == hl ? rr[hh] : r;
+      // q heads come first in q | k
+      const uint32_t* nw = (const uint32_t*)(nt * nh + hl < heads ? args.q_norm : args.k_norm);  // bf16 pairs
+      const int pr = d >> 1;  // first pair of the piece
       const f32x4 c4 = *(const f32x4*)(cs + pr);
       const f32x4 s4 = *(const f32x4*)(sn + pr);
       u32x4 o;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const uint32_t wp = nw[pr + p];
-        const float na = __uint_as_float(f32_to_bf16_bits(__fmul_rn(__fmul_rn(bf16_lo(v[p]), rr), bf16_lo(wp))) << 16);
-        const float nb = __uint_as_float(f32_to_bf16_bits(__fmul_rn(__fmul_rn(bf16_hi(v[p]), rr), bf16_hi(wp))) << 16);
+        const float na = __uint_as_float(f32_to_bf16_bits(__fmul_rn(__fmul_rn(bf16_lo(v[p]), r), bf16_lo(wp))) << 16);
+        const float nb = __uint_as_float(f32_to_bf16_bits(__fmul_rn(__fmul_rn(bf16_hi(v[p]), r), bf16_hi(wp))) << 16);
         const float oa = __fsub_rn(__fmul_rn(na, c4[p]), __fmul_rn(nb, s4[p]));
         const float ob = __fadd_rn(__fmul_rn(na, s4[p]), __fmul_rn(nb, c4[p]));
         o[p] = bf16x2_rne(oa, ob);
@@ -458,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   }
   // physical column of tile column c (the QKV fusion reorders columns)
   constexpr bool kQk = EPI == kEpiQk;
-  const int qk_cols = kQk ? 2 * args.heads * kHeadDim : 0;
+  const int qk_cols = kQk ? 2 * args.heads * args.head_dim : 0;
   auto pcol = [&](int c) -> int {
     if constexpr (kQk) return qk_col(nt, c, qk_cols);
     else return n0 + c;

@@ -47,15 +47,17 @@ struct GemmArgs {
   void* next_act = nullptr;              // f16 [M, N]: the next layer's product operand e2m1 * dec(s8)
   float* next_lora_part = nullptr;       // f32 [column tiles, M, next_rank]: each tile's partial sum
   int next_rank = 0;
-  // QKV fusion (heads > 0): N = 3 heads 128 columns q | k | v.  Column tile t
-  // of the 2 heads tiles computes head t of q | k and v columns 64 t ..
-  // 64 t + 63; the epilogue applies RMSNorm and RoPE to the head's columns.
-  const void* q_norm = nullptr;     // bf16 [128]
-  const void* k_norm = nullptr;     // bf16 [128]
-  const float* rope_cos = nullptr;  // f32 [M, 64]
-  const float* rope_sin = nullptr;  // f32 [M, 64]
+  // QKV fusion (heads > 0): N = 3 heads head_dim columns q | k | v, head_dim
+  // 32, 64 or 128.  Column tile t of the heads head_dim / 64 tiles computes
+  // the q | k columns 128 t .. 128 t + 127 (whole heads) and the v columns
+  // 64 t .. 64 t + 63; the epilogue applies RMSNorm and RoPE to the heads.
+  const void* q_norm = nullptr;     // bf16 [head_dim]
+  const void* k_norm = nullptr;     // bf16 [head_dim]
+  const float* rope_cos = nullptr;  // f32 [M, head_dim / 2]
+  const float* rope_sin = nullptr;  // f32 [M, head_dim / 2]
   float eps = 0.f;
   int heads = 0;
+  int head_dim = 0;
   // split K (ksplit > 1, plain linear only): workgroup (tile, j) covers stages
   // [j per, (j + 1) per) and writes fp32 partials [ksplit, M, N] (the low-rank
   // term in split 0, no bias); launch_splitk_reduce sums them into out

@@ -214,8 +214,8 @@ int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up,
  * projections merged with RMSNorm and RoPE): one svdq_w4a4 linear whose
  * epilogue normalizes and rotates the q and k heads before they are stored.
  *
- *   h = svdq_w4a4_linear(qkv, x)  (bf16 [M, 3 heads 128]: q | k | v, heads of
- *                                  128 consecutive columns)
+ *   h = svdq_w4a4_linear(qkv, x)  (bf16 [M, 3 heads head_dim]: q | k | v,
+ *                                  heads of head_dim consecutive columns)
  *   for each token m and q or k head: n = bf16(h / sqrt(mean(h^2) + eps) * w)
  *     with w = q_norm or k_norm; out pair (2i, 2i+1) =
  *     bf16(n_2i cos[m,i] - n_2i+1 sin[m,i], n_2i sin[m,i] + n_2i+1 cos[m,i])
@@ -225,7 +225,9 @@ int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up,
  *
  * x       bf16 [M, qkv->K]
  * qkv     an svdq_w4a4 layer with N = 3 * heads * head_dim
- * heads   1..256; head_dim must be 128 (else SVDQ_EUNSUPPORTED)
+ * heads   1..256; head_dim 32, 64 or 128, with heads * head_dim a multiple
+ *         of 64 (else SVDQ_EUNSUPPORTED): a tile of the product holds 128
+ *         q | k columns, whole heads, so that RMSNorm stays in one workgroup
  * q_norm, k_norm  bf16 [head_dim] RMSNorm weights
  * eps     finite, > 0
  * rope_cos, rope_sin  fp32 [M, head_dim / 2]: the rotation of pair i at token m

@@ -290,7 +290,12 @@ def test_qkv_rules(L):
                                                   p(kn), eps, p(cs), p(sn), p(out), p(ws), wsb, arch)
     assert call() == OK
     assert call(qkv=_layer(0x1_0000_0000, K, N, precision=0), wsb=need + (4 * M + 255) // 256 * 256) == OK
-    assert call(hd=64) == EUNSUP                    # head_dim 128 only
+    assert call(hd=64) == EINVAL                    # N != 3 heads head_dim
+    assert call(hd=64, heads=8) == OK               # head dims 32, 64 and 128
+    assert call(hd=32, heads=16) == OK
+    for hd in (16, 48, 96, 256):                    # other head dims
+        assert call(hd=hd, heads=N // (3 * hd)) == EUNSUP
+    assert call(hd=256, heads=2) == EUNSUP
     assert call(heads=3) == EINVAL                  # N != 3 heads head_dim
     assert call(heads=0) == EINVAL
     big = 257

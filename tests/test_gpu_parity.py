@@ -678,6 +678,7 @@ def check_qkv(x, lay, heads, qn, kn, cos, sin, eps, label, rows=None):
     last place, so each output may also differ by two ulps of each n it
     combines: |err| <= half-ulp(out) + 2 (ulp(n_a) |c| + ulp(n_b) |s|) +
     1e-2 RMS, with MRE <= 2e-3."""
+    D = len(qn)
     layer = bq.SVDQLinear.from_numpy(lay)
     xd = dev_bf16(x)
     y = bq.svdq_w4a4_qkv_rmsnorm_rope(xd, layer, heads, dev_bf16(qn), dev_bf16(kn),
@@ -686,15 +687,15 @@ def check_qkv(x, lay, heads, qn, kn, cos, sin, eps, label, rows=None):
     torch.cuda.synchronize()
     rows = np.arange(x.shape[0]) if rows is None else rows
     ref = L.qkv_norm_rope_ref(x[rows], lay, heads, qn, kn, eps, cos[rows], sin[rows])
-    qk = 2 * heads * 128
+    qk = 2 * heads * D
     yb = host_bits(y)[rows]
-    if ksplit(x.shape[0], 3 * heads * 128, x.shape[1]) == 1:
+    if ksplit(x.shape[0], 3 * heads * D, x.shape[1]) == 1:
         # the plain linear sums in the same order
         assert np.array_equal(yb[:, qk:], host_bits(plain)[rows][:, qk:]), label
     assert_output(torch.from_numpy(yb[:, qk:].view(np.int16).copy()).view(torch.bfloat16), ref[:, qk:], label + " v")
     # q | k with the allowance for the intermediate rounding
     R = len(rows)
-    h = F.bf16_bits_f64(L.svdq_linear_ref(x[rows], lay))[:, :qk].reshape(R, 2, heads, 128)
+    h = F.bf16_bits_f64(L.svdq_linear_ref(x[rows], lay))[:, :qk].reshape(R, 2, heads, D)
     n = np.stack([F.bf16_to_f32(L.rmsnorm_bf16(h[:, p], w, eps)).astype(np.float64) for p, w in ((0, qn), (1, kn))],
                  axis=1)
     c, s_ = np.abs(cos[rows])[:, None, None, :], np.abs(sin[rows])[:, None, None, :]
@@ -715,17 +716,22 @@ def check_qkv(x, lay, heads, qn, kn, cos, sin, eps, label, rows=None):
     assert excess <= 1e-2 and mre <= 2e-3, label
 
 
-@pytest.mark.parametrize("M,heads,precision,rank", [(1, 1, "nvfp4", 32), (37, 2, "int4", 16), (300, 3, "nvfp4", 0),
-                                                    (257, 2, "int4", 32), (300, 1, "nvfp4", 128)])
-def test_qkv_rmsnorm_rope_ragged(M, heads, precision, rank):
-    # M ragged against the 256-row tiles; 2 heads column tiles per call
-    rng = np.random.default_rng(M * 7 + heads)
-    K, N = 256, 3 * heads * 128
+@pytest.mark.parametrize("M,heads,D,precision,rank", [
+    (1, 1, 128, "nvfp4", 32), (37, 2, 128, "int4", 16), (300, 3, 128, "nvfp4", 0), (257, 2, 128, "int4", 32),
+    (300, 1, 128, "nvfp4", 128),
+    # head dims 64 (two heads per column tile, one of them split between the
+    # tile's two waves) and 32 (four per tile), heads of q and k in one tile
+    (1, 1, 64, "int4", 32), (37, 3, 64, "nvfp4", 16), (300, 5, 64, "int4", 0), (257, 2, 32, "nvfp4", 32),
+    (300, 6, 32, "int4", 128), (64, 10, 32, "nvfp4", 16)])
+def test_qkv_rmsnorm_rope_ragged(M, heads, D, precision, rank):
+    # M ragged against the 256-row tiles; heads D / 64 column tiles per call
+    rng = np.random.default_rng(M * 7 + heads + D)
+    K, N = 256, 3 * heads * D
     x = S.activations(M, K, 3, rng)
     lay = prepared(x, S.weight(N, K, 0.05, rng, spike_rank=2), S.bias(N, rng), precision, rank, smooth="calibrated")
-    qn, kn = S.norm_weight(128, rng), S.norm_weight(128, rng)
-    cos, sin = S.rope_tables(M, 128, offset=M)
-    check_qkv(x, lay, heads, qn, kn, cos, sin, 1e-6, f"qkv M={M} H={heads} {precision} r{rank}")
+    qn, kn = S.norm_weight(D, rng), S.norm_weight(D, rng)
+    cos, sin = S.rope_tables(M, D, offset=M)
+    check_qkv(x, lay, heads, qn, kn, cos, sin, 1e-6, f"qkv M={M} H={heads} D={D} {precision} r{rank}")
 
 
 def test_qkv_rmsnorm_rope_dit_sampled():
@@ -739,11 +745,12 @@ def test_qkv_rmsnorm_rope_dit_sampled():
 
 
 def test_qkv_rejects_head_dim():
+    # head dim 256: a q or k head would span two column tiles
     rng = np.random.default_rng(1)
     x = S.activations(8, 256, 0, rng)
-    lay = bq.SVDQLinear.from_numpy(prepared(x, S.weight(384, 256, 0.05, rng), None, "nvfp4", 16))
-    cos, sin = (torch.from_numpy(t).cuda() for t in S.rope_tables(8, 64))
-    q = dev_bf16(S.norm_weight(64, rng))
+    lay = bq.SVDQLinear.from_numpy(prepared(x, S.weight(768, 256, 0.05, rng), None, "nvfp4", 16))
+    cos, sin = (torch.from_numpy(t).cuda() for t in S.rope_tables(8, 256))
+    q = dev_bf16(S.norm_weight(256, rng))
     with pytest.raises(bq.SvdqError) as e:
-        bq.svdq_w4a4_qkv_rmsnorm_rope(dev_bf16(x), lay, 2, q, q, cos, sin)
+        bq.svdq_w4a4_qkv_rmsnorm_rope(dev_bf16(x), lay, 1, q, q, cos, sin)
     assert e.value.status == -2
