@@ -340,6 +340,22 @@ def bench_mfma_peak(torch, stream, iters=20000):
             run()
         tflops = flops / (time_events(run, 5, stream) * 1e-3) / 1e12
         out[key] = {"measured_TFLOPs": round(tflops, 1), "implied_clock_GHz": round(2.4 * tflops / PEAK["f16"], 3)}
+    # the other int4 datapath's inner loop: codes as fp8 / fp6 operands of the
+    # 32x32x64 f8f6f4 instruction (one group per product) with the bf16 group
+    # scales applied on the vector ALU
+    fn = lib.svdq_peak_group_scaled
+    fn.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    giters = iters // 4
+    gflops = blocks * 8 * giters * 8 * 2.0 * 32 * 32 * 64
+    for key, fmt in (("int4_as_fp8_group_scaled", 0), ("int4_as_fp6_group_scaled", 2)):
+        def run():
+            if fn(fmt, giters, blocks, sink.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("group-scaled probe launch failed")
+        for _ in range(3):
+            run()
+        out[key] = {"measured_TFLOPs": round(gflops / (time_events(run, 5, stream) * 1e-3) / 1e12, 1),
+                    "instruction": "v_mfma_scale_f32_32x32x64_f8f6f4 + 2 VALU per output and group"}
     return out
 
 

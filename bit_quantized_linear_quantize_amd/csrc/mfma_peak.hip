@@ -79,7 +79,86 @@ __global__ __launch_bounds__(512) void mfma_f16_peak_switching_kernel(int64_t it
   sink[t] = s;
 }
 
+// The inner loop of the other datapath for int4 x int4 group products: the
+// codes (|q| <= 7) are exact fp8 E4M3 or fp6 E2M3 operands, one
+// 32x32x64 f8f6f4 product gives a group's integer sum P (64 = the group
+// size), and the bf16 group scales, which these instructions cannot take
+// (their block scales are powers of two per 32 values), are applied on the
+// vector ALU: acc += P * (s_x[row] * s_w[col]), 16 multiplies and 16 FMAs
+// per 32x32 tile and group (the same per tile for any wave tile).  A wave
+// computes a 64 x 64 block (2 x 2 tiles); its operand pairs rotate and the
+// scales change every group.  FMT: 0 = fp8 E4M3, 2 = fp6 E2M3.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int FMT>
+__global__ __launch_bounds__(512) void group_scaled_probe_kernel(int64_t iters, float* sink) {
+  const uint32_t t = blockIdx.x * 512u + threadIdx.x;
+  i32x8 a[2], b[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // bytes of small-magnitude codes (E4M3 / E2M3 patterns of values <= 7)
+    const uint32_t h0 = peak_hash(t * 97u + i), h1 = peak_hash(~(t * 89u + i));
+    a[0][i] = (int)(h0 & 0x2d3d2d3du);
+    a[1][i] = (int)(h1 & 0x3d2d3d2du);
+    b[0][i] = (int)((h0 >> 3) & 0x2d3d2d3du);
+    b[1][i] = (int)((h1 >> 3) & 0x3d2d3d2du);
+  }
+  f32x16 sx[2];
+  float sw[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    sx[0][e] = 0.01f + 1e-4f * (float)((t + e) & 63);
+    sx[1][e] = 0.02f + 1e-4f * (float)((t + 3 * e) & 63);
+  }
+  for (int j = 0; j < 2; ++j) sw[j] = 0.03f + 1e-4f * (float)((t >> j) & 31);
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const f32x16 zero = {};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {  // two groups per iteration with the operand pairs rotated
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(i + v) & 1], b[(j + v) & 1], zero, FMT,
+                                                                           FMT, 0, 0x7f, 0, 0x7f);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(p[e], sx[i][e] * sw[j], acc[i][j][e]);
+        }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sw[j] = sw[j] * 1.0000001f;
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) s += acc[i][j][0] + acc[i][j][15];
+  sink[t] = s;
+}
+
 extern "C" {
+
+// The group-scaled int4 product loop above: `iters` rounds of two groups per
+// wave (8 products of 32 x 32 x 64, 131072 flops each).  fmt 0: fp8
+// operands, 2: fp6.  Returns 0, -5 on a launch error, -1 on another fmt.
+int svdq_peak_group_scaled(int fmt, int64_t iters, int blocks, void* sink, void* stream) {
+  if (fmt == 0)
+    hipLaunchKernelGGL(group_scaled_probe_kernel<0>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters,
+                       (float*)sink);
+  else if (fmt == 2)
+    hipLaunchKernelGGL(group_scaled_probe_kernel<2>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters,
+                       (float*)sink);
+  else
+    return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // As svdq_peak_mfma_f16, with operands that switch on every product.
 int svdq_peak_mfma_f16_switching(int64_t iters, int blocks, void* sink, void* stream) {
