@@ -512,10 +512,10 @@ def svdq_w4a4_quantize_act(x, smooth, lora_down, precision, stream=None, out=Non
 
 
 def svdq_w4a4_quantize_operand(x, smooth, lora_down, precision, stream=None):
-    """Kernel 1 exactly as the linear launches it: returns (operand float16
-    [M, K], row_scale fp32 [M] (int4) or None, lora_act fp32 [M, rank] or
-    None) -- the product operand code * scale (int4: times 2^-E[m],
-    row_scale = 2^E[m])."""
+    """Kernel 1 exactly as the linear launches it: returns (operand, scale,
+    lora_act fp32 [M, rank] or None) -- int4: operand uint8 [M, K], the codes
+    as fp8 E4M3 bytes, and scale fp32 [M, K/64], the group scales; nvfp4:
+    operand float16 [M, K], e2m1 * dec(s8), and scale None."""
     if precision not in PRECISIONS:
         raise ValueError(f"precision must be one of {sorted(PRECISIONS)}")
     x = _x(x, None)
@@ -523,14 +523,15 @@ def svdq_w4a4_quantize_operand(x, smooth, lora_down, precision, stream=None):
     smooth = _contig(smooth, torch.bfloat16, "smooth", (K,))
     lora_down = _contig(lora_down, torch.bfloat16, "lora_down", (None, K))
     rank = 0 if lora_down is None else lora_down.shape[0]
-    operand = torch.empty((M, K), dtype=torch.float16, device=x.device)
-    row_scale = torch.empty(M, dtype=torch.float32, device=x.device) if precision == "int4" else None
+    int4 = precision == "int4"
+    operand = torch.empty((M, K), dtype=torch.uint8 if int4 else torch.float16, device=x.device)
+    scale = torch.empty((M, K // 64), dtype=torch.float32, device=x.device) if int4 else None
     lora_act = torch.empty((M, rank), dtype=torch.float32, device=x.device) if rank else None
     _on_gpu(x=x, smooth=smooth, lora_down=lora_down)
     _check(lib().svdq_w4a4_quantize_operand(
         _ptr(x), M, K, _ptr(smooth), _ptr(lora_down), PRECISIONS[precision], GROUP_SIZE[precision], rank,
-        _ptr(operand), _ptr(row_scale), _ptr(lora_act), _stream(stream)))
-    return operand, row_scale, lora_act
+        _ptr(operand), _ptr(scale), _ptr(lora_act), _stream(stream)))
+    return operand, scale, lora_act
 
 
 def svdq_w4a4_gemm_partials(act_codes, w_codes, precision, stream=None):

@@ -126,22 +126,24 @@ size_t w_scale_bytes(int64_t N, int64_t K, int precision) {
 }
 
 // Base workspace of one layer (each part 256-byte aligned):
-//   act_f16    f16 [M, K]   dequantized activations, the product operand
-//   row_scale  int4 only: f32 [M], the power of two factored out of each row
+//   act_op     the product operand [M, K]: int4 codes as fp8 E4M3 bytes,
+//              nvfp4 the dequantized values as fp16
+//   act_scale  int4 only: f32 [M, K/64], the group scales
 //   lora_act   f32 [M, rank]
 size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
-  size_t b = round_up(size_t(M) * size_t(K) * 2);
-  if (precision == SVDQ_INT4) b += round_up(size_t(M) * 4);
+  size_t b = round_up(size_t(M) * size_t(K) * (precision == SVDQ_INT4 ? 1 : 2));
+  if (precision == SVDQ_INT4) b += round_up(size_t(M) * size_t(K / 64) * 4);
   return b + round_up(size_t(M) * size_t(rank) * 4);
 }
 
 // Split K for the plain linear: when the 256 x 192 tiles would occupy less
-// than half of the 256 compute units, each tile's stages are shared by up to
-// 8 workgroups (at least 2 stages each) that write fp32 partials, summed in a
-// fixed order by a second kernel.
-int choose_ksplit(int64_t M, int64_t N, int64_t K) {
+// than half of the 256 compute units, each tile's stages (128 values of K for
+// int4, 64 for nvfp4) are shared by up to 8 workgroups (at least 2 stages
+// each where there are enough) that write fp32 partials, summed in a fixed
+// order by a second kernel.
+int choose_ksplit(int64_t M, int64_t N, int64_t K, int precision) {
   const int64_t tiles = ((M + 255) / 256) * ((N + 191) / 192);
-  const int nst = int(K / 64);
+  const int nst = int(K / (precision == SVDQ_INT4 ? 128 : 64));
   if (tiles >= 128) return 1;
   int s = int(std::min<int64_t>(8, 256 / tiles));
   s = std::min(s, nst / 2);
@@ -150,15 +152,15 @@ int choose_ksplit(int64_t M, int64_t N, int64_t K) {
   return s;
 }
 
-size_t split_bytes(int64_t M, int64_t K, int64_t N) {
-  const int s = choose_ksplit(M, N, K);
+size_t split_bytes(int64_t M, int64_t K, int64_t N, int precision) {
+  const int s = choose_ksplit(M, N, K, precision);
   return s > 1 ? round_up(size_t(s) * size_t(M) * size_t(N) * 4) : 0;
 }
 
 // Workspace of svdq_w4a4_linear / svdq_w4a4_gemm: workspace_bytes, then the
 // split-K partials fp32 [ksplit, M, N] when K is split.
 size_t linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision, int rank) {
-  return workspace_bytes(M, K, precision, rank) + split_bytes(M, K, N);
+  return workspace_bytes(M, K, precision, rank) + split_bytes(M, K, N, precision);
 }
 
 // with_workspace false: the caller's workspace is not checked (the
@@ -230,19 +232,19 @@ int launch_status(hipError_t e, const char* what) {
 }
 
 struct Carve {
-  uint8_t* act_f16;   // f16 [M, K]
-  float* row_scale;   // int4: f32 [M]; else null
+  uint8_t* act_op;    // int4: E4M3 bytes [M, K]; nvfp4: f16 [M, K]
+  float* act_scale;   // int4: f32 [M, K/64]; else null
   float* lora_act;    // f32 [M, rank]
 };
 
 Carve carve(void* workspace, int64_t M, int64_t K, int precision) {
   uint8_t* p = static_cast<uint8_t*>(workspace);
   Carve c{};
-  c.act_f16 = p;
-  p += round_up(size_t(M) * size_t(K) * 2);
+  c.act_op = p;
+  p += round_up(size_t(M) * size_t(K) * (precision == SVDQ_INT4 ? 1 : 2));
   if (precision == SVDQ_INT4) {
-    c.row_scale = reinterpret_cast<float*>(p);
-    p += round_up(size_t(M) * 4);
+    c.act_scale = reinterpret_cast<float*>(p);
+    p += round_up(size_t(M) * size_t(K / 64) * 4);
   }
   c.lora_act = reinterpret_cast<float*>(p);
   return c;
@@ -252,7 +254,7 @@ Carve carve(void* workspace, int64_t M, int64_t K, int precision) {
 int launch_quantize(const void* x, int64_t M, int64_t K, const void* smooth, const void* lora_down,
                     int precision, int rank, void* workspace, hipStream_t s) {
   const Carve c = carve(workspace, M, K, precision);
-  svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, c.lora_act, c.act_f16, c.row_scale,
+  svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, c.lora_act, c.act_op, c.act_scale,
                         M, K, precision, rank};
   return launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
 }
@@ -262,9 +264,9 @@ int launch_gemm(const void* workspace, int64_t M, int64_t K, int64_t N, const vo
                 const void* wscales, float wtscale, const void* lora_up, const void* bias, int precision,
                 int rank, void* out, hipStream_t s) {
   const Carve c = carve(const_cast<void*>(workspace), M, K, precision);
-  svdq::GemmArgs ga{c.act_f16, c.row_scale, c.lora_act, packed_w, wscales, lora_up, bias, out, nullptr,
+  svdq::GemmArgs ga{c.act_op, c.act_scale, c.lora_act, packed_w, wscales, lora_up, bias, out, nullptr,
                     wtscale, M, K, N, precision, rank};
-  ga.ksplit = choose_ksplit(M, N, K);
+  ga.ksplit = choose_ksplit(M, N, K, precision);
   if (ga.ksplit > 1)
     ga.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(workspace)) +
                                           workspace_bytes(M, K, precision, rank));
@@ -831,7 +833,7 @@ int svdq_w4a4_quantize_act(const void* x, int64_t M, int64_t K, const void* smoo
 
 int svdq_w4a4_quantize_operand(const void* x, int64_t M, int64_t K, const void* smooth,
                                const void* lora_down, int precision, int group_size, int rank,
-                               void* operand_out, float* row_scale_out, float* lora_act_out,
+                               void* operand_out, float* scale_out, float* lora_act_out,
                                void* stream) {
   g_last_error.clear();
   int rc = check_svdq_kind(precision, group_size, rank);
@@ -839,15 +841,15 @@ int svdq_w4a4_quantize_operand(const void* x, int64_t M, int64_t K, const void* 
   rc = check_shape(M, K, 64);
   if (rc) return rc;
   if (!x || !smooth || !operand_out) return fail(SVDQ_EINVAL, "null pointer argument");
-  if ((precision == SVDQ_INT4) != (row_scale_out != nullptr))
-    return fail(SVDQ_EINVAL, "row_scale_out must be non-null exactly for int4");
+  if ((precision == SVDQ_INT4) != (scale_out != nullptr))
+    return fail(SVDQ_EINVAL, "scale_out must be non-null exactly for int4");
   if ((rank > 0) != (lora_down != nullptr) || (rank > 0) != (lora_act_out != nullptr))
     return fail(SVDQ_EINVAL, "lora_down / lora_act_out must be non-null exactly when rank > 0");
-  const void* ptrs[] = {x, smooth, lora_down, operand_out, row_scale_out, lora_act_out};
+  const void* ptrs[] = {x, smooth, lora_down, operand_out, scale_out, lora_act_out};
   for (const void* p : ptrs)
     if (p && !aligned(p)) return fail(SVDQ_EINVAL, "pointer arguments must be 16-byte aligned");
-  const Range outs[] = {{operand_out, size_t(M) * size_t(K) * 2},
-                        {row_scale_out, size_t(M) * 4},
+  const Range outs[] = {{operand_out, size_t(M) * size_t(K) * (precision == SVDQ_INT4 ? 1 : 2)},
+                        {scale_out, size_t(M) * size_t(K / 64) * 4},
                         {lora_act_out, size_t(M) * size_t(rank) * 4}};
   const Range xr{x, size_t(M) * size_t(K) * 2};
   for (int i = 0; i < 3; ++i) {
@@ -857,7 +859,7 @@ int svdq_w4a4_quantize_operand(const void* x, int64_t M, int64_t K, const void* 
   }
   rc = check_device_arch();
   if (rc) return rc;
-  svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, lora_act_out, operand_out, row_scale_out, M, K,
+  svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, lora_act_out, operand_out, scale_out, M, K,
                         precision, rank};
   return launch_status(svdq::launch_quantize_act(qa, static_cast<hipStream_t>(stream)),
                        "quantize_act_lora_down launch");
@@ -922,9 +924,9 @@ int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up, cons
   // up layer: kernel 2 with the GELU + nvfp4 epilogue writing the down
   // layer's operand and its column tiles' low-rank partials (the up layer's
   // bf16 output is not stored)
-  svdq::GemmArgs ga{cu.act_f16, cu.row_scale, cu.lora_act, up->packed_w, up->wscales, up->lora_up, up->bias,
+  svdq::GemmArgs ga{cu.act_op, cu.act_scale, cu.lora_act, up->packed_w, up->wscales, up->lora_up, up->bias,
                     nullptr, nullptr, up->wtscale, M, up->K, H, up->precision, up->rank,
-                    down->smooth, down->lora_down, cd.act_f16, part, down->rank};
+                    down->smooth, down->lora_down, cd.act_op, part, down->rank};
   rc = launch_status(svdq::launch_gemm_w4a4(ga, s), "gemm_w4a4_lora_up (GELU epilogue) launch");
   if (rc) return rc;
   // the down layer's low-rank activations: the tiles' partials added in order
@@ -964,7 +966,7 @@ int svdq_w4a4_qkv_rmsnorm_rope(const void* x, int64_t M, const svdq_w4a4_layer* 
   rc = launch_quantize(x, M, qkv->K, qkv->smooth, qkv->lora_down, qkv->precision, qkv->rank, workspace, s);
   if (rc) return rc;
   const Carve c = carve(workspace, M, qkv->K, qkv->precision);
-  svdq::GemmArgs ga{c.act_f16, c.row_scale, c.lora_act, qkv->packed_w, qkv->wscales, qkv->lora_up, qkv->bias,
+  svdq::GemmArgs ga{c.act_op, c.act_scale, c.lora_act, qkv->packed_w, qkv->wscales, qkv->lora_up, qkv->bias,
                     out, nullptr, qkv->wtscale, M, qkv->K, qkv->N, qkv->precision, qkv->rank};
   ga.q_norm = q_norm;
   ga.k_norm = k_norm;

@@ -23,6 +23,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 namespace svdq {
@@ -157,13 +158,6 @@ __device__ __forceinline__ uint32_t nvfp4_quant16(const float* x, uint32_t& cw0,
   cw0 = zero ? 0u : cw0;
   cw1 = zero ? 0u : cw1;
   return zero ? 0u : s8;
-}
-
-// Power-of-two exponent E of a positive normal float s such that s * 2^-E
-// lies in [2^12, 2^13): then |q| * s * 2^-E < 7 * 2^13 fits fp16 for |q| <= 7,
-// and every s' >= 2^-17 (within 2^29 of the largest) keeps all its bits.
-__device__ __forceinline__ int fp16_fit_exponent(float smax) {
-  return (int)((__float_as_uint(smax) >> 23) & 0xffu) - 127 - 12;
 }
 
 }  // namespace svdq

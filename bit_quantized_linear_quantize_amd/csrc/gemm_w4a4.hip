@@ -9,33 +9,36 @@
 //
 // gfx950 design
 // -------------
-// The group scales are folded into the operands instead of being applied to
-// every output once per group.  A code times its group scale needs at most
-// 3 + 8 significant bits (int4 |q| <= 7 times a bf16 scale) or 2 + 4 (E2M1
-// times E4M3), so both operands are exact fp16 values and one fp16 matrix
-// product with fp32 accumulation over all of K gives sum_g s_x s_w P_g with
-// exact products:
-//   A  the quantize kernel already writes q * s_x (nvfp4: e2m1 * dec(s8)) as
-//      fp16; int4 rows carry a power of two 2^-E[m] so that they fit fp16,
-//      undone here after the product (row_scale);
-//   W  converted while staging: codes via a v_perm table into fp16, times the
-//      group scale (int4: times 2^-F[n], one power of two per weight row chosen
-//      from its largest scale, undone at the end; nvfp4: dec(s8), with
-//      wtscale applied at the end).
-// A per-group fp32 epilogue (two VALU operations per output and group) would
-// outweigh the matrix work; with folded scales the main loop is matrix
-// instructions, LDS traffic and the staging of W.
-//
 // Workgroup tile 256 (M) x 192 (N) -- 256 workgroups for a 4096 x 3072
 // output, one per CU -- with 8 waves (4 x 2), each wave 64 x 96 = 2 x 3 blocks
-// of 32 x 32; 64 columns of K per stage, v_mfma_f32_32x32x16_f16.  A goes
-// from memory straight into a ring of three LDS stage buffers
+// of 32 x 32.  Tiles are visited in groups of 4 M-tiles, mapped so that the
+// workgroups on one XCD share A and W tiles in its L2.  Two datapaths:
+//
+// int4 -- fp8 operands, scales on the vector ALU.  Every code |q| <= 7 is an
+// exact fp8 E4M3 value, so one v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 block
+// and group (K = 64) gives the group's exact integer sums P, and the bf16
+// group scales (which the instruction's power-of-two block scales cannot
+// express) are applied as acc += P * fl32(s_x s_w) (the scale product is
+// exact).  The quantize kernel writes A as E4M3 bytes with fp32 group scales;
+// a stage is 128 values of K (two groups).  This route needs two VALU
+// operations per output and group, but its matrix work is half that of the
+// fp16 route below, and it runs at a lower power: the fp16 route on int4
+// data is held back by the clock the chip sustains under full matrix load.
+//
+// nvfp4 -- scales folded into exact fp16 operands.  An E2M1 code times its
+// E4M3 block scale needs at most 2 + 4 significant bits, an exact fp16, so
+// one fp16 matrix product with fp32 accumulation over all of K gives
+// sum_g s_x s_w P_g (the per-16 scales fit no wider instruction): A arrives
+// from the quantize kernel as e2m1 * dec(s8) in fp16; W is converted while
+// staging (codes via cvt_scalef32_pk_f16_fp4, times dec(s8)); wtscale is
+// applied at the end.  64 values of K per stage, v_mfma_f32_32x32x16_f16.
+//
+// Both: A goes from memory straight into a ring of three LDS stage buffers
 // (buffer_load ... lds, rows of 128 bytes with XOR-swizzled 16-byte chunks:
-// conflict-free operand reads), issued three stages ahead.  W codes and
-// scales are loaded two stages ahead into registers, converted, and written
-// to one of two padded LDS stage buffers among the matrix instructions of the
-// previous stage.  Tiles are visited in groups of 4 M-tiles, mapped so that
-// the workgroups on one XCD share A and W tiles in its L2.
+// conflict-free operand reads), issued three stages ahead (int4: its group
+// scales likewise).  W codes and scales are loaded two stages ahead into
+// registers, converted, and written to one of two padded LDS stage buffers
+// among the matrix instructions of the previous stage.
 // Low-rank up: lora_act (fp32) split into bf16 hi + lo, times lora_up, with
 // bf16 matrix instructions accumulating into the same registers.
 //
@@ -114,8 +117,34 @@ struct RawStage {
   // the scale of each W piece, kept in its loaded width (a widening right
   // after the load would make the wave wait for the load there)
   uint8_t sw8[kWP];    // nvfp4: E4M3 byte
-  uint16_t sw16[kWP];  // int4: bf16 bits
   uint32_t a[kAP];     // parity export only
+};
+
+// int4 as fp8: sixteen sign-magnitude codes (nibble i = column i, low nibble
+// first) -> sixteen OCP fp8 E4M3 bytes in column order.  |q| <= 7 is exact in
+// E4M3: a table of the eight magnitude bytes (v_perm) plus the sign bit; the
+// code 0x8 (-0) gives 0x80, fp8 -0.
+__device__ __forceinline__ u32x4 int4x16_to_fp8(u32x2 w) {
+  constexpr uint32_t kT0 = 0x44403800u;  // E4M3 bytes of 0, 1, 2, 3
+  constexpr uint32_t kT1 = 0x4E4C4A48u;  // of 4, 5, 6, 7
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t v = w[k];
+    const uint32_t elo = __builtin_amdgcn_perm(kT1, kT0, v & 0x07070707u) | ((v << 4) & 0x80808080u);  // columns 0 2 4 6
+    const uint32_t ehi = __builtin_amdgcn_perm(kT1, kT0, (v >> 4) & 0x07070707u) | (v & 0x80808080u);  // 1 3 5 7
+    r[2 * k] = __builtin_amdgcn_perm(ehi, elo, 0x05010400u);      // columns 0 1 2 3
+    r[2 * k + 1] = __builtin_amdgcn_perm(ehi, elo, 0x07030602u);  // columns 4 5 6 7
+  }
+  return r;
+}
+
+// One stage of raw W data of the int4 fp8 path in registers: piece j = 8
+// bytes of codes (columns 16 c .. 16 c + 15 of the stage, c = tid % 8) of
+// tile row tid/8 + 64 j, and the bf16 scales of the stage's two groups.
+struct RawStage8 {
+  u32x2 w[kWP];
+  uint32_t sw[kWP];
 };
 
 // Logical tile of this workgroup: consecutive workgroups land on different
@@ -464,9 +493,12 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   __shared__ __attribute__((aligned(16))) uint8_t lds_a2[kBM * kARow];
   __shared__ __attribute__((aligned(16))) uint8_t lds_w0[kBN * kWRow];
   __shared__ __attribute__((aligned(16))) uint8_t lds_w1[kBN * kWRow];
-  __shared__ float wexp[kBN];   // int4: 2^F[n] of this tile's weight rows
-  __shared__ float wdown[kBN];  // int4: 2^-F[n]
   __shared__ float nmu[kBN];    // MLP fusion: 1 / smooth of the next layer for this tile's columns
+  // int4 (fp8 operands): the group scales of the stages in LDS, A per A
+  // buffer [group][row], W per W buffer [group][row]
+  constexpr bool kFp8 = PREC == kInt4 && !PARTIALS;
+  __shared__ __attribute__((aligned(16))) float asc[kFp8 ? kAStages * 2 * kBM : 1];
+  __shared__ __attribute__((aligned(16))) float wsc[kFp8 ? 2 * 2 * kBN : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -480,7 +512,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   // split K: this workgroup's stages [s0, s0 + nstages) (the loads below take
   // their stage offsets from descriptor bases moved to stage s0)
   constexpr bool kSplit = EPI == kEpiSplit;
-  int s0 = 0, nstages = K / kBK;
+  // (a stage is kBK values of K; the int4 fp8 path takes two groups, 128)
+  int s0 = 0, nstages = kFp8 ? K / 128 : K / kBK;
   if constexpr (kSplit) {
     const int per = (nstages + args.ksplit - 1) / args.ksplit;
     s0 = blockIdx.y * per;
@@ -500,8 +533,171 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       nmu[tid] = col < N ? __fdiv_rn(1.0f, bf16_bits_to_f32(((const uint16_t*)args.next_smooth)[col])) : 0.f;
     }
   }
-  constexpr bool kRowExp = PREC == kInt4 && !PARTIALS;
+  f32x16 acc[kIB][kJB];
+#pragma unroll
+  for (int i = 0; i < kIB; ++i)
+#pragma unroll
+    for (int j = 0; j < kJB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  if constexpr (kFp8) {
+    // ---- int4: fp8 operands, group scales on the vector ALU --------------------
+    // A stage s (128 values of K, two groups of 64) comes straight from
+    // memory to LDS as fp8 codes in the same swizzled 16-byte chunks as the
+    // fp16 operand of the other path (8 chunks per 128-byte row); its group
+    // scales (fp32 [M, K/64]) likewise, into asc.  W stage s is staged
+    // through registers: int4 nibbles -> fp8 bytes (rows of kWRow bytes),
+    // its bf16 group scales -> fp32 in wsc.  Per group, each 32 x 32 tile is
+    // one v_mfma_f32_32x32x64_f8f6f4 of exact integer sums P (|P| <= 64 * 49)
+    // and acc += P * (s_x * s_w) (the scale product is exact in fp32).
+    // Loads run three stages ahead for A and two for W, as in the other path.
+    const int G = K >> 6;
+    const __amdgpu_buffer_rsrc_t a_rs = make_rsrc((const uint8_t*)args.act + (size_t)m0 * K + s0 * 128,
+                                                  (size_t)(M - m0) * K - s0 * 128);
+    const __amdgpu_buffer_rsrc_t as_rs = make_rsrc((const uint8_t*)args.act_scale + ((size_t)m0 * G + 2 * s0) * 4,
+                                                   ((size_t)(M - m0) * G - 2 * s0) * 4);
+    const int w_base = kQk ? 0 : n0;
+    const __amdgpu_buffer_rsrc_t w_rs = make_rsrc((const uint8_t*)args.w_codes + (size_t)w_base * K2 + s0 * 64,
+                                                  (size_t)(N - w_base) * K2 - s0 * 64);
+    const __amdgpu_buffer_rsrc_t ws_rs = make_rsrc((const uint8_t*)args.w_scales + (size_t)w_base * G * 2 + s0 * 4,
+                                                   (size_t)(N - w_base) * G * 2 - s0 * 4);
+    const __amdgpu_buffer_rsrc_t zero_rs = make_rsrc(args.w_codes, 0);
+    const int lc = tid & 7, lr = tid >> 3;
+    int w_off[kWP], ws_off[kWP];
+#pragma unroll
+    for (int j = 0; j < kWP; ++j) {
+      const int wrow = kQk ? pcol(lr + kRP * j) : lr + kRP * j;  // row from the descriptor base
+      w_off[j] = wrow * K2 + lc * 8;
+      ws_off[j] = wrow * G * 2;
+    }
+    int dma_off[kADma];
+#pragma unroll
+    for (int d = 0; d < kADma; ++d) {
+      const int u = (wave * kADma + d) * 64 + lane;
+      const int row = u >> 3;
+      dma_off[d] = row * K + a_pos(row, u & 7) * 16;
+    }
+    // A scales: waves 0-3 load group 0 of the stage, waves 4-7 group 1, one
+    // row per lane
+    const int sc_row = (wave & 3) * 64 + lane, sc_g = wave >> 2;
+    const int sc_off = sc_row * G * 4 + sc_g * 4;
+
+    auto abuf = [&](auto c) -> uint8_t* {
+      constexpr int i = decltype(c)::value % kAStages;
+      if constexpr (i == 0) return lds_a0;
+      else if constexpr (i == 1) return lds_a1;
+      else return lds_a2;
+    };
+    auto wbuf = [&](auto c) -> uint8_t* {
+      if constexpr (decltype(c)::value % 2 == 0) return lds_w0;
+      else return lds_w1;
+    };
+    // loads of stage s: A and its scales into A buffer ab (direct to LDS),
+    // then W into r
+    auto group = [&](RawStage8& r, int s, auto ab) {
+      const bool live = s < nstages;
+      constexpr int b = decltype(ab)::value % kAStages;
+      uint8_t* dst = abuf(ab) + wave * (kADma * 64 * 16);
+#pragma unroll
+      for (int d = 0; d < kADma; ++d)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? a_rs : zero_rs,
+                                                 (__attribute__((address_space(3))) void*)(dst + d * 1024), 16,
+                                                 dma_off[d], s * 128, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          live ? as_rs : zero_rs,
+          (__attribute__((address_space(3))) void*)(asc + (b * 2 + sc_g) * kBM + (wave & 3) * 64), 4, sc_off, s * 8,
+          0, 0);
+      // the W loads of the stage stay behind its A loads: a wave that has
+      // waited for its W registers has also received its A stage
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kWP; ++j) {
+        r.w[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(live ? w_rs : zero_rs, w_off[j],
+                                                                                s * 64, 0));
+        r.sw[j] = __builtin_amdgcn_raw_buffer_load_b32(live ? ws_rs : zero_rs, ws_off[j], s * 4, 0);
+      }
+    };
+    // staging of W piece p of a raw stage into W buffer Tw (its scales into
+    // wsc half wb)
+    auto store_part = [&](uint8_t* Tw, int wb, const RawStage8& r, int p) {
+      const int wrow = lr + kRP * p;
+      *(u32x4*)(Tw + wrow * kWRow + lc * 16) = int4x16_to_fp8(r.w[p]);
+      // (the eight lanes of a row write the same values: no branch here,
+      // which would split the schedule of the products around it)
+      wsc[(wb * 2 + 0) * kBN + wrow] = bf16_lo(r.sw[p]);
+      wsc[(wb * 2 + 1) * kBN + wrow] = bf16_hi(r.sw[p]);
+    };
+    // one stage: per group, per 32 x 32 tile one product of 64 values of K
+    auto compute = [&](auto P, int s, RawStage8& r) {
+      constexpr int p = decltype(P)::value;
+      constexpr int ab = p % kAStages, wb = p % 2;
+      const uint8_t* Ta = abuf(IC<p>{});
+      const uint8_t* Tw = wbuf(IC<p>{});
+      uint8_t* Nw = wbuf(IC<p + 1>{});
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        i32x8 aop[kIB], bop[kJB];
+        float sw[kJB];
+#pragma unroll
+        for (int i = 0; i < kIB; ++i) {
+          const int row = wm * (kIB * 32) + i * 32 + l32;
+          const u32x4 lo = *(const u32x4*)(Ta + row * kARow + a_pos(row, 4 * gi + 2 * h) * 16);
+          const u32x4 hi = *(const u32x4*)(Ta + row * kARow + a_pos(row, 4 * gi + 2 * h + 1) * 16);
+          aop[i] = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+#pragma unroll
+        for (int j = 0; j < kJB; ++j) {
+          const int col = wn * (kJB * 32) + j * 32 + l32;
+          const uint8_t* src = Tw + col * kWRow + 64 * gi + 32 * h;
+          const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
+          bop[j] = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          sw[j] = wsc[(wb * 2 + gi) * kBN + col];
+        }
+#pragma unroll
+        for (int i = 0; i < kIB; ++i) {
+          // s_x of the lane's 16 rows of tile row i: rows 8 q + 4 h + 0..3
+          f32x4 sx[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            sx[q] = *(const f32x4*)(asc + (ab * 2 + gi) * kBM + wm * (kIB * 32) + i * 32 + q * 8 + h * 4);
+#pragma unroll
+          for (int j = 0; j < kJB; ++j) {
+            const f32x16 pr = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[i], bop[j], f32x16{}, 0, 0, 0, 0,
+                                                                            0, 0);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              acc[i][j][e] = __fmaf_rn(pr[e], __fmul_rn(sx[e >> 2][e & 3], sw[j]), acc[i][j][e]);
+          }
+          // stage a third of the next W stage among the products
+          if (gi * kIB + i < 3) store_part(Nw, (p + 1) % 2, r, gi * kIB + i);
+        }
+      }
+      stage_barrier();
+      group(r, s + 3, IC<p>{});
+    };
+
+    RawStage8 r0, r1;
+    group(r0, 0, IC<0>{});
+    group(r1, 1, IC<1>{});
+#pragma unroll
+    for (int q = 0; q < 3; ++q) store_part(lds_w0, 0, r0, q);
+    group(r0, 2, IC<2>{});
+    stage_barrier();  // (each wave has its stage-0 A loads: they precede the W loads it staged)
+    for (int s = 0; s < nstages; s += 6) {
+      compute(IC<0>{}, s, r1);
+      compute(IC<1>{}, s + 1, r0);
+      compute(IC<2>{}, s + 2, r1);
+      compute(IC<3>{}, s + 3, r0);
+      compute(IC<4>{}, s + 4, r1);
+      compute(IC<5>{}, s + 5, r0);
+    }
+    // the direct-to-LDS loads of the stages past the end are still in flight
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
   // ---- loaders ---------------------------------------------------------------
   // Buffer loads: one descriptor per operand based at this tile's first row,
   // 32-bit lane offsets, the stage offset in a scalar register.  Rows past
@@ -574,16 +770,12 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     for (int j = 0; j < kWP; ++j) {
       r.w[j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, w_off[j], s * 32, 0);
       if constexpr (PREC == kNvfp4 && !PARTIALS) r.sw8[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, ws_off[j], s * 4, 0);
-      if constexpr (PREC == kInt4 && !PARTIALS) r.sw16[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, ws_off[j], s * 2, 0);
     }
     if constexpr (PARTIALS) {
 #pragma unroll
       for (int i = 0; i < kAP; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b32(ars, pa_off[i], s * 32, 0);
     }
   };
-
-  const int G64 = K >> 6;
-  float wdn[kWP];  // int4: 2^-F[n] of this thread's weight rows (set after the prologue)
 
   // staging of one raw stage in three parts (part p: W piece p and, for the
   // parity export, A pieces of part p), so that it can be interleaved with
@@ -602,26 +794,10 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     }
     const int wrow = lr + kRP * p;
     _Float16 sc = (_Float16)(PREC == kInt4 ? 1.0f : 2.0f);
-    if constexpr (!PARTIALS) {
-      if constexpr (PREC == kInt4)
-        sc = (_Float16)(bf16_bits_to_f32(r.sw16[p]) * wdn[p]);  // exact: a power of two
-      else
-        sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw8[p], 0);
-    }
+    if constexpr (!PARTIALS) sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw8[p], 0);  // nvfp4
     *(f16x8*)(Tw + wrow * kWRow + lc * 16) =
         PREC == kInt4 ? int4x8_to_f16_scaled(r.w[p], sc) : e2m1x8_to_f16_scaled(r.w[p], sc);
   };
-
-  f32x16 acc[kIB][kJB];
-#pragma unroll
-  for (int i = 0; i < kIB; ++i)
-#pragma unroll
-    for (int j = 0; j < kJB; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  const int l32 = lane & 31;
-  const int h = lane >> 5;
 
   // exact integer partials of one group (fp32 holds them exactly)
   auto partial_store = [&](int g, int G) {
@@ -720,31 +896,6 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   RawStage r0, r1;
   group(r0, 0, IC<0>{});
   group(r1, 1, IC<1>{});
-  // int4: per weight row the power of two 2^-F that makes every q * s_w * 2^-F
-  // an exact fp16, from the row's largest group scale (its loads overlap the
-  // first two stages' loads)
-  if constexpr (kRowExp) {
-    if (tid < kBN) {
-      // the row's scales, two per load (G64 is even: rows are 4-byte aligned)
-      const uint16_t* srow = (const uint16_t*)args.w_scales + (size_t)(kQk ? pcol(tid) : min(n0 + tid, N - 1)) * G64;
-      float m = 0.f;
-      for (int g0 = 0; g0 < G64; g0 += 16) {
-        uint32_t v[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-          if (g0 + 2 * p < G64) v[p] = *(const uint32_t*)(srow + g0 + 2 * p);
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-          if (g0 + 2 * p < G64) m = fmaxf(m, fmaxf(bf16_lo(v[p]), bf16_hi(v[p])));
-      }
-      const int F = m > 0.f ? fp16_fit_exponent(m) : 0;
-      wexp[tid] = __builtin_ldexpf(1.0f, F);
-      wdown[tid] = __builtin_ldexpf(1.0f, -F);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kWP; ++j) wdn[j] = wdown[lr + kRP * j];
-  }
 #pragma unroll
   for (int p = 0; p < 3; ++p) store_part(lds_a0, lds_w0, r0, p);
   group(r0, 2, IC<2>{});
@@ -763,21 +914,11 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   }
   // the direct-to-LDS loads of the stages past the end are still in flight
   __builtin_amdgcn_s_waitcnt(0);
+  }
 
   if constexpr (!PARTIALS) {
-    // ---- undo the operand powers of two / apply the tensor scale -------------
-    if constexpr (PREC == kInt4) {
-#pragma unroll
-      for (int i = 0; i < kIB; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = min(m0 + wm * (kIB * 32) + i * 32 + (e >> 2) * 8 + h * 4 + (e & 3), M - 1);
-          const float ra = args.row_scale[row];
-#pragma unroll
-          for (int j = 0; j < kJB; ++j)
-            acc[i][j][e] = __fmul_rn(acc[i][j][e], __fmul_rn(ra, wexp[wn * (kJB * 32) + j * 32 + l32]));
-        }
-    } else {
+    // ---- nvfp4: the weight tensor scale (int4 applied its scales per group) --
+    if constexpr (PREC == kNvfp4) {
       const float t = args.wtscale;
 #pragma unroll
       for (int i = 0; i < kIB; ++i)

@@ -16,19 +16,20 @@ struct QuantActArgs {
   void* codes;            // parity export: u8 [M, K/2] nibbles; else null
   void* scales;           // parity export: bf16 [M, K/64] | u8 [M, K/16]; else null
   float* lora_act;        // f32 [M, rank]
-  void* act_f16;          // linear only: f16 [M, K] product operand q * s (see below), else null
-  float* row_scale;       // linear int4 only: f32 [M] power-of-two factor of each row of act_f16
+  void* act_op;           // linear only: the product operand [M, K] (see below), else null
+  float* act_scale;       // linear int4 only: f32 [M, K/64] group scales s
   int64_t M, K;
   int precision, rank;
 };
 
-// act_f16 holds the dequantized activations exactly: int4 q * s * 2^-E[m]
-// (E[m] chosen per row so every value fits fp16, row_scale[m] = 2^E[m]);
-// nvfp4 e2m1 * dec(s8), which always fits fp16.
+// The product operand of the linear.  int4: the codes q (|q| <= 7) as fp8
+// E4M3 bytes (every such integer is exact), with the group scales in
+// act_scale, applied after each group's product; nvfp4: e2m1 * dec(s8) as
+// fp16 (always exact).
 
 struct GemmArgs {
-  const void* act;          // linear: f16 [M, K] (act_f16 above); partials: nibbles [M, K/2]
-  const float* row_scale;   // linear int4: f32 [M]; else null
+  const void* act;          // linear: act_op above; partials: nibbles [M, K/2]
+  const float* act_scale;   // linear int4: f32 [M, K/64]; else null
   const float* lora_act;    // f32 [M, rank]
   const void* w_codes;      // u8 [N, K/2]
   const void* w_scales;     // bf16 [N, K/64] | u8 [N, K/16]

@@ -28,15 +28,9 @@
 //
 // Outputs.  The parity export writes packed nibbles (low nibble = even
 // column), the group scales and lora_act.  Inside svdq_w4a4_linear the kernel
-// instead writes the activations already dequantized, as the fp16 operand of
-// the product kernel: nvfp4 e2m1 * dec(s8) (always an exact fp16), int4
-// q * s * 2^-E[m] with one power of two per row (row_scale[m] = 2^E[m] is
-// undone after the product).  E = 0 whenever every group scale s of the row
-// lies in [2^-17, 2^13): then q * s is an exact fp16 (at most 11 significant
-// bits, a multiple of 2^-24, below 2^16), so the values are written in the
-// same pass.  A row with a scale outside that range (known once the
-// workgroup has seen the whole row) is quantized again from X and rewritten
-// with E chosen from its largest scale.
+// instead writes the operand the product kernel reads: int4 the codes q as
+// fp8 E4M3 bytes (exact: |q| <= 7) and the group scales as fp32, nvfp4 the
+// activations dequantized to e2m1 * dec(s8) in fp16 (always exact).
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -60,12 +54,7 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
   constexpr int kK1Waves = K1Shape<RB>::waves;
   constexpr int kK1Threads = 64 * kK1Waves;
   extern __shared__ float lds[];
-  // int4 linear: per wave and row, the largest group scale and the smallest
-  // nonzero one
-  __shared__ float rmax[kK1Waves][kK1Rows];
-  __shared__ float rmin[kK1Waves][kK1Rows];
   constexpr int PF = K1Shape<RB>::prefetch;
-  constexpr bool kRowExp = LINEAR && PREC == kInt4;
   constexpr int NB = RB > 0 ? RB : 1;
   const int M = (int)args.M, K = (int)args.K;
   const uint16_t* __restrict__ x = (const uint16_t*)args.x;
@@ -127,17 +116,17 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
     cw0 = sbits == 0u ? 0u : cw0;
     cw1 = sbits == 0u ? 0u : cw1;
   };
-  // int4, product operand with row exponent 0: q * s for 8 of the lane's
-  // values, q = rne(x / s) (|q| <= 7), formed directly: the fp32 product is
-  // exact, and so is its fp16 value whenever 2^-17 <= s < 2^13 (at most 11
-  // significant bits, a multiple of 2^-24, below 2^16)
-  auto int4_qs_f16x8 = [&](const float* xh, float inv, float sv) -> u32x4 {
+  // int4, product operand: the 16 codes q = rne(x / s) of the lane as fp8
+  // E4M3 bytes (every integer |q| <= 7 is exact; a negative value that rounds
+  // to 0 gives -0, as the sign-magnitude code does)
+  auto int4_q8 = [&](const float* xh, float inv) -> u32x4 {
     u32x4 r;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const float a = __fmul_rn(__builtin_rintf(__fmul_rn(xh[2 * p], inv)), sv);
-      const float b = __fmul_rn(__builtin_rintf(__fmul_rn(xh[2 * p + 1], inv)), sv);
-      r[p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+      const float q0 = __builtin_rintf(__fmul_rn(xh[4 * p], inv)), q1 = __builtin_rintf(__fmul_rn(xh[4 * p + 1], inv));
+      const float q2 = __builtin_rintf(__fmul_rn(xh[4 * p + 2], inv)), q3 = __builtin_rintf(__fmul_rn(xh[4 * p + 3], inv));
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+      r[p] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
     }
     return r;
   };
@@ -145,7 +134,6 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
   f32x4 acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float smax = 0.f, smin = __builtin_huge_valf();  // int4 linear: over the lane's groups
 
   u32x4 xbuf[PF][2];
   u32x4 lbuf[PF][NB][2];
@@ -190,15 +178,11 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
           const uint32_t sbits = int4_scale(xh, inv);
           const float sv = __uint_as_float(sbits << 16);
           if constexpr (LINEAR) {
-            // speculatively with row exponent 0: q * s is an exact fp16
-            // whenever 2^-17 <= s < 2^13; rows with a scale outside that
-            // range are rewritten below
-            smax = fmaxf(smax, sv);
-            if (sbits != 0u) smin = fminf(smin, sv);
             if (row_ok) {
-              _Float16* dst = (_Float16*)args.act_f16 + (size_t)row * K + k0;
-              *(u32x4*)dst = int4_qs_f16x8(xh, inv, sv);
-              *(u32x4*)(dst + 8) = int4_qs_f16x8(xh + 8, inv, sv);
+              // (a zero group gets codes 0, as in the packed export)
+              const u32x4 z = {0u, 0u, 0u, 0u};
+              *(u32x4*)((uint8_t*)args.act_op + (size_t)row * K + k0) = sbits == 0u ? z : int4_q8(xh, inv);
+              if (q == 0) args.act_scale[(size_t)row * (K >> 6) + c] = sv;
             }
           } else {
             int4_codes(xh, inv, sbits, cw0, cw1);
@@ -211,7 +195,7 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
             // the product operand e2m1 * dec(s8): an exact fp16 (|v| <= 2688, >= 2^-10)
             if (row_ok) {
               const _Float16 S16 = (_Float16)S;
-              _Float16* dst = (_Float16*)args.act_f16 + (size_t)row * K + k0;
+              _Float16* dst = (_Float16*)args.act_op + (size_t)row * K + k0;
               *(f16x8*)dst = e2m1x8_to_f16_scaled(cw0, S16);
               *(f16x8*)(dst + 8) = e2m1x8_to_f16_scaled(cw1, S16);
             }
@@ -246,44 +230,6 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
           }
         }
         issue(p, c + PF * kK1Waves);
-      }
-    }
-  }
-
-  // ---- int4 linear: the row's power of two; rows that do not fit exponent 0
-  // are quantized again from X and rewritten as q * s * 2^-E[row] ------------
-  if constexpr (kRowExp) {
-    if (q == 0) {  // the four lanes of a row hold the same groups' scales
-      rmax[wave][r] = smax;
-      rmin[wave][r] = smin;
-    }
-    __syncthreads();
-    float mx = rmax[0][r], mn = rmin[0][r];
-#pragma unroll
-    for (int w = 1; w < kK1Waves; ++w) {
-      mx = fmaxf(mx, rmax[w][r]);
-      mn = fminf(mn, rmin[w][r]);
-    }
-    const bool fits = mx < 8192.0f && mn >= 7.62939453125e-06f;  // [2^-17, 2^13)
-    const int E = fits || !(mx > 0.f) ? 0 : fp16_fit_exponent(mx);
-    if (row_ok && wave == 0 && q == 0) args.row_scale[row] = __builtin_ldexpf(1.0f, E);
-    if (!fits && row_ok) {  // uniform over the four lanes of the row
-      const float down = __builtin_ldexpf(1.0f, -E);
-      _Float16* dst = (_Float16*)args.act_f16 + (size_t)row * K;
-      for (int c = wave; c < nchunks; c += kK1Waves) {
-        const int k0 = c * 64 + q * 16;
-        u32x4 xb[2];
-        xb[0] = *(const u32x4*)(xr + k0);
-        xb[1] = *(const u32x4*)(xr + k0 + 8);
-        float xh[16];
-        smooth16(xb, k0, xh);
-        uint32_t cw0, cw1;
-        float inv;
-        const uint32_t sbits = int4_scale(xh, inv);
-        int4_codes(xh, inv, sbits, cw0, cw1);
-        const _Float16 s16 = (_Float16)(__uint_as_float(sbits << 16) * down);  // exact power-of-two scaling
-        *(f16x8*)(dst + k0) = int4x8_to_f16_scaled(cw0, s16);
-        *(f16x8*)(dst + k0 + 8) = int4x8_to_f16_scaled(cw1, s16);
       }
     }
   }
@@ -340,7 +286,7 @@ static hipError_t dispatch_rank(const QuantActArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream) {
-  const bool linear = a.act_f16 != nullptr;
+  const bool linear = a.act_op != nullptr;
   if (a.precision == kInt4)
     return linear ? dispatch_rank<kInt4, true>(a, stream) : dispatch_rank<kInt4, false>(a, stream);
   return linear ? dispatch_rank<kNvfp4, true>(a, stream) : dispatch_rank<kNvfp4, false>(a, stream);

@@ -53,9 +53,10 @@ enum svdq_status {
 };
 
 /* Bytes of scratch svdq_w4a4_linear needs, each part 256-byte aligned: the
- * dequantized activations as fp16 [M, K] (the operand of the product kernel:
- * code times group scale is exact in fp16); for int4 also one fp32
- * power-of-two row factor [M]; the low-rank activations fp32 [M, rank]; and,
+ * operand of the product kernel [M, K] (int4: the codes as fp8 E4M3 bytes,
+ * followed by the fp32 group scales [M, K/64]; nvfp4: the dequantized
+ * activations e2m1 * dec(s8) as fp16, which is exact); the low-rank
+ * activations fp32 [M, rank]; and,
  * when the 256 x 192 output tiles would fill less than half of the GPU, the
  * fp32 partial sums [ksplit, M, N] of the product split along K (ksplit <= 8,
  * a function of M, N and K; the splits are added in a fixed order).
@@ -170,9 +171,9 @@ typedef struct svdq_w4a4_layer {
   int precision, group_size, rank;
 } svdq_w4a4_layer;
 
-/* Bytes of scratch svdq_w4a4_mlp_gelu needs: the up layer's activations,
- * row factors and low-rank activations (as in svdq_w4a4_workspace_bytes, no
- * split partials) followed by the down layer's linear workspace (its fp16
+/* Bytes of scratch svdq_w4a4_mlp_gelu needs: the up layer's product operand
+ * and low-rank activations (as in svdq_w4a4_workspace_bytes, no split
+ * partials) followed by the down layer's linear workspace (its fp16
  * product operand [M, H], fp32 low-rank activations [M, down->rank] and, for
  * small M x N, its split-K partials), then fp32 partial sums of the down
  * layer's low-rank activations per 192-column tile of the up projection
@@ -348,21 +349,19 @@ int svdq_w4a4_quantize_act(const void* x, int64_t M, int64_t K, const void* smoo
 /* Parity export of the first svdq_w4a4 kernel exactly as svdq_w4a4_linear
  * launches it: the product operand the second kernel multiplies, written to
  * caller buffers instead of the workspace ("Supported quantization types":
- * the svdq_w4a4 activation formats, held dequantized).
- *   operand_out    IEEE binary16 [M, K]: nvfp4 e2m1 * dec(s8) (always exact);
- *                  int4 q * s * 2^-E[m], where E[m] = 0 when every group scale
- *                  s of row m lies in [2^-17, 2^13) (then each value is the
- *                  exact product), else E[m] = floor(log2 max_g s) - 12 and
- *                  each value is f16(q * f16(s * 2^-E[m])) (exact for groups
- *                  within 2^29 of the row's largest scale, rounded to nearest
- *                  even below that)
- *   row_scale_out  int4: fp32 [M], 2^E[m]; must be NULL for nvfp4
+ * the svdq_w4a4 activation formats).
+ *   operand_out    int4: uint8 [M, K], each code q (|q| <= 7) as an OCP fp8
+ *                  E4M3 byte, exact (a negative value that rounds to 0 gives
+ *                  0x80, -0); nvfp4: IEEE binary16 [M, K], e2m1 * dec(s8)
+ *                  (always exact)
+ *   scale_out      int4: fp32 [M, K/64], the group scales s (the bf16 values,
+ *                  0 for a zero group); must be NULL for nvfp4
  *   lora_act_out   fp32 [M, rank] (NULL iff rank == 0)
  * Other arguments and rules as for svdq_w4a4_quantize_act; no output may
  * overlap x or another output. */
 int svdq_w4a4_quantize_operand(const void* x, int64_t M, int64_t K, const void* smooth,
                                const void* lora_down, int precision, int group_size, int rank,
-                               void* operand_out, float* row_scale_out, float* lora_act_out,
+                               void* operand_out, float* scale_out, float* lora_act_out,
                                void* stream);
 
 /* Parity export of the 4-bit product of the second svdq_w4a4 kernel (same

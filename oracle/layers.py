@@ -38,7 +38,7 @@ W_deq = (q - z) * s, fp64 accumulation.
 import numpy as np
 
 from .formats import (F32, bf16_bits, bf16_bits_f64, bf16_to_f32, e4m3_decode,
-                      e2m1_decode, f16_round, pack_nibbles, nibble_to_int4)
+                      e2m1_decode, e4m3_encode, pack_nibbles, nibble_to_int4)
 from .quant import (quantize_int4, quantize_nvfp4_act, quantize_nvfp4_weight,
                     quantize_awq)
 
@@ -171,40 +171,33 @@ def svdq_quantize_act(x_bits, smooth_bits, lora_down_bits, precision):
 
 
 def product_operand_ref(codes, scales, precision):
-    """The dequantized activations as the product kernel receives them: each
-    value code * group scale held as an IEEE binary16, int4 rows rescaled by
-    one power of two 2^-E[m] so that they fit binary16.
+    """The activations as the product kernel receives them.
 
     Reading (the pages fix no operand format; this is the library's own
     encoding of the activation codes and group scales, defined here value by
     value):
-      nvfp4: value = e2m1 * dec(s8), always an exact binary16 (|v| <= 2688,
-             nonzero |v| >= 2^-10); no row factor (None is returned).
-      int4:  with s_max the row's largest group scale and s_min its smallest
-             nonzero one, E = 0 if s_max < 2^13 and s_min >= 2^-17 (then
-             every q * s is an exact binary16) or the row is all zero;
-             otherwise E = floor(log2 s_max) - 12.  value =
-             f16(q * f16(s * 2^-E)) -- exact for every group within 2^29 of
-             s_max, rounded (each step to nearest even) below that.  The row
-             factor 2^E is returned as float64 [R].
+      nvfp4: the dequantized value e2m1 * dec(s8), always an exact binary16
+             (|v| <= 2688, nonzero |v| >= 2^-10); no separate scales (None).
+      int4:  each code q (|q| <= 7, sign-magnitude) as an OCP fp8 E4M3 byte --
+             every such integer is an E4M3 value, and the code 0x8 ("-0")
+             keeps its sign (0x80) -- and the group scales s as float64
+             [R, K/64] (the bf16 values).  The product kernel forms each
+             group's exact integer sum P and adds P * (s_x * s_w).
 
     codes [R, K] nibbles; scales as returned by the quantizers ([R, K/G]).
-    Returns (values float64 [R, K], row factor float64 [R] or None).
+    Returns (nvfp4: values float64 [R, K], None; int4: E4M3 bytes uint8
+    [R, K], scales float64 [R, K/64]).
     """
     G = GROUP[precision]
-    q = _code_values(codes, precision)
-    s = _scale_values(scales, precision)
-    R, K = q.shape
     if precision == "nvfp4":
+        q = _code_values(codes, precision)
+        s = _scale_values(scales, precision)
+        R, K = q.shape
         return (q.reshape(R, K // G, G) * s[..., None]).reshape(R, K), None
-    smax = s.max(axis=1)
-    smin = np.where(s > 0, s, np.inf).min(axis=1)
-    fits = (smax < 2.0 ** 13) & (smin >= 2.0 ** -17)
-    _, e = np.frexp(np.where(smax > 0, smax, 1.0))  # smax in [2^(e-1), 2^e)
-    E = np.where(fits | (smax == 0), 0, (e - 1) - 12).astype(np.int64)
-    s16 = f16_round(np.ldexp(s, -E[:, None]))
-    vals = f16_round(q.reshape(R, K // G, G) * s16[..., None]).reshape(R, K)
-    return vals, np.ldexp(1.0, E)
+    n = np.asarray(codes, dtype=np.uint8)
+    mag = (n & 7).astype(np.float64)
+    signed = np.where((n & 8) != 0, -mag, mag)  # -0.0 for the code 0x8
+    return e4m3_encode(signed), _scale_values(scales, precision)
 
 
 def _code_values(codes, precision):

@@ -2,12 +2,12 @@
 the workspace layout it implies), restated for the tests."""
 
 
-def ksplit(M, N, K):
+def ksplit(M, N, K, precision="nvfp4"):
     """Split only when the 256 x 192 output tiles fill less than half of 256
-    compute units; up to 8 splits of at least 2 64-column stages, every split
-    non-empty."""
+    compute units; up to 8 splits of at least 2 stages (128 values of K for
+    int4, 64 for nvfp4), every split non-empty."""
     tiles = -(-M // 256) * -(-N // 192)
-    nst = K // 64
+    nst = K // (128 if precision in ("int4", 0) else 64)
     if tiles >= 128:
         return 1
     s = max(min(8, 256 // tiles, nst // 2), 1)
@@ -16,6 +16,6 @@ def ksplit(M, N, K):
     return s
 
 
-def split_bytes(M, N, K):
-    s = ksplit(M, N, K)
+def split_bytes(M, N, K, precision="nvfp4"):
+    s = ksplit(M, N, K, precision)
     return 0 if s == 1 else (s * M * N * 4 + 255) // 256 * 256

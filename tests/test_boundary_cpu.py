@@ -154,16 +154,22 @@ def test_split_rule():
     assert ksplit(300, 320, 512) == 4             # 4 tiles, 8 stages
     assert ksplit(64, 64, 128) == 1               # 2 stages
     assert ksplit(64, 64, 576) == 3               # 9 stages: 4 splits of 3 would leave one empty
+    # int4 stages are 128 values of K
+    assert ksplit(512, 3072, 3072, "int4") == 8   # 24 stages
+    assert ksplit(300, 320, 512, "int4") == 2     # 4 stages
+    assert ksplit(64, 64, 256, "int4") == 1       # 2 stages
+    assert ksplit(64, 64, 1152, "int4") == 3      # 9 stages
 
 
 def test_workspace_size(L):
     M, K, N = 300, 512, 320
     rnd = lambda v: (v + 255) // 256 * 256
-    # fp16 activations [M, K]; int4 adds a row factor [M]; then lora_act
-    # fp32 [M, 32]; then the split-K partials fp32 [ksplit, M, N]
-    want = {0: rnd(2 * M * K) + rnd(4 * M) + rnd(M * 32 * 4) + split_bytes(M, N, K),
+    # the product operand (int4: fp8 codes [M, K] and fp32 group scales
+    # [M, K/64]; nvfp4: fp16 [M, K]); then lora_act fp32 [M, 32]; then the
+    # split-K partials fp32 [ksplit, M, N]
+    want = {0: rnd(M * K) + rnd(4 * M * (K // 64)) + rnd(M * 32 * 4) + split_bytes(M, N, K, "int4"),
             1: rnd(2 * M * K) + rnd(M * 32 * 4) + split_bytes(M, N, K)}
-    assert split_bytes(M, N, K) > 0
+    assert split_bytes(M, N, K) > 0 and split_bytes(M, N, K, "int4") > 0
     assert L.svdq_w4a4_workspace_bytes(4096, 3072, 3072, 1, 16, 32) == rnd(2 * 4096 * 3072) + rnd(4096 * 32 * 4)
     for prec, g in ((0, 64), (1, 16)):
         need = L.svdq_w4a4_workspace_bytes(M, K, N, prec, g, 32)
@@ -248,10 +254,10 @@ def test_mlp_rules(L):
     B = ctypes.byref
     need = L.svdq_w4a4_mlp_workspace_bytes(M, B(up), B(down))
     rnd = lambda v: (v + 255) // 256 * 256
-    # the up layer's operand, row factors and lora_act, the down layer's linear
-    # workspace, then the down layer's low-rank partials per 192-column tile
-    # of the up projection
-    assert need == (rnd(2 * M * K) + rnd(4 * M) + rnd(4 * M * 32)) + (rnd(2 * M * H) + rnd(4 * M * 32) +
+    # the up layer's operand (int4: fp8 codes and fp32 group scales) and
+    # lora_act, the down layer's linear workspace, then the down layer's
+    # low-rank partials per 192-column tile of the up projection
+    assert need == (rnd(M * K) + rnd(4 * M * (K // 64)) + rnd(4 * M * 32)) + (rnd(2 * M * H) + rnd(4 * M * 32) +
                                                                       split_bytes(M, N, H)) + \
         rnd(4 * ((H + 191) // 192) * M * 32)
 
@@ -260,7 +266,10 @@ def test_mlp_rules(L):
         return L.svdq_w4a4_mlp_gelu_check(p(x), M, B(up) if up is not None else None,
                                           B(down) if down is not None else None, p(out), p(ws), wsb, arch)
     assert call() == OK
-    assert call(up=_layer(0x1_0000_0000, K, H, precision=1)) == OK
+    up_n = _layer(0x1_0000_0000, K, H, precision=1)  # an nvfp4 up layer keeps an fp16 operand
+    need_n = L.svdq_w4a4_mlp_workspace_bytes(M, B(up_n), B(down))
+    assert need_n == need + rnd(2 * M * K) - rnd(M * K) - rnd(4 * M * (K // 64))
+    assert call(up=up_n, wsb=need_n) == OK and call(up=up_n) == EWS
     assert call(down=_layer(0x2_0000_0000, H, N, precision=0)) == EUNSUP  # int4 hidden activations
     assert L.svdq_w4a4_mlp_workspace_bytes(M, B(up), B(_layer(0x2_0000_0000, H, N, precision=0))) == 0
     assert call(down=_layer(0x2_0000_0000, H + 64, N)) == EINVAL     # up->N != down->K

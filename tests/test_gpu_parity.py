@@ -119,21 +119,29 @@ def check_quantize_act(x_bits, lay, label):
 
 def check_operand(x_bits, lay, label):
     """The first kernel as the linear launches it (svdq_w4a4_quantize_operand)
-    against the oracle: the binary16 product operand value for value (exact
-    equality, so +0 and -0 agree), the int4 row factors bit for bit, the
-    low-rank activations to 1e-4 of their largest magnitude."""
+    against the oracle: int4 the E4M3 code bytes and the fp32 group scales bit
+    for bit; nvfp4 the binary16 operand value for value (exact equality, so +0
+    and -0 agree); the low-rank activations to 1e-4 of their largest
+    magnitude."""
     p = lay["precision"]
     ref = L.svdq_quantize_act(x_bits, lay["smooth"], lay["lora_down"], p)
-    want, want_rs = L.product_operand_ref(ref["codes"], ref["scales"], p)
+    want, want_sc = L.product_operand_ref(ref["codes"], ref["scales"], p)
     ld = dev_bf16(lay["lora_down"]) if lay["rank"] else None
-    op, rs, lora = bq.svdq_w4a4_quantize_operand(dev_bf16(x_bits), dev_bf16(lay["smooth"]), ld, p)
+    op, sc, lora = bq.svdq_w4a4_quantize_operand(dev_bf16(x_bits), dev_bf16(lay["smooth"]), ld, p)
     torch.cuda.synchronize()
-    got = op.cpu().numpy().astype(np.float64)
-    bad = np.argwhere(got != want)
-    assert bad.size == 0, (f"{label}: {len(bad)} operand values differ, first {bad[:4].tolist()}: "
-                           f"{[(got[tuple(b)], want[tuple(b)]) for b in bad[:4]]}")
     if p == "int4":
-        assert np.array_equal(rs.cpu().numpy().astype(np.float64), want_rs), f"{label}: row factors differ"
+        got = op.cpu().numpy()
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, (f"{label}: {len(bad)} E4M3 code bytes differ, first {bad[:4].tolist()}: "
+                               f"{[(hex(got[tuple(b)]), hex(want[tuple(b)])) for b in bad[:4]]}")
+        got_sc = sc.cpu().numpy()
+        assert got_sc.dtype == np.float32 and np.array_equal(got_sc.astype(np.float64), want_sc), \
+            f"{label}: group scales differ"
+    else:
+        got = op.cpu().numpy().astype(np.float64)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, (f"{label}: {len(bad)} operand values differ, first {bad[:4].tolist()}: "
+                               f"{[(got[tuple(b)], want[tuple(b)]) for b in bad[:4]]}")
     if lay["rank"]:
         la = lora.cpu().numpy().astype(np.float64)
         err = np.abs(la - ref["lora_act"]).max()
@@ -216,11 +224,12 @@ def test_quantize_act_rounding_ties(family):
     check_k1(x, lay, f"k1 ties {family} ({len(cases)} groups)")
 
 
-def row_exponent_inputs():
-    """int4 rows of every row-exponent class of the product operand: E = 0
-    (all scales in [2^-17, 2^13)), scales far above or below, a row spread
-    over 2^-33 .. 2^-1 (beyond the exact 2^29 window), rows on both sides of
-    both bounds, zero rows, a row with one nonzero group."""
+def scale_range_inputs():
+    """int4 rows whose group scales span the bf16 range the quantizer makes:
+    ordinary rows, scales far above 2^13 or below 2^-17, a row spread over
+    2^-33 .. 2^-1, rows with one outlier group, zero rows, a row with one
+    nonzero group (the product operand keeps every scale as fp32, so each
+    class is exact)."""
     rng = np.random.default_rng(23)
     M, K = 100, 512
     xf = rng.standard_normal((M, K)).astype(np.float32)
@@ -228,20 +237,20 @@ def row_exponent_inputs():
     xf[32:48] *= 1e-7                     # scales below 2^-17
     xf[48:64, 256:] *= 1e-9               # one row, scales 2^-33 .. 2^-1
     xf[64:80] = np.clip(xf[64:80], -3, 3)  # other groups: s ~ 0.4
-    xf[64, 5] = 57088.0                   # s = bf16(57088 / 7) = 8160: fits
-    xf[65, 70] = 57344.0                  # s = 8192: rewritten
+    xf[64, 5] = 57088.0                   # s = bf16(57088 / 7) = 8160
+    xf[65, 70] = 57344.0                  # s = 8192
     xf[66, 128:192] *= 1e-9
-    xf[66, 130] = 7 * 2.0 ** -17          # smallest s = 2^-17: fits
+    xf[66, 130] = 7 * 2.0 ** -17          # smallest s = 2^-17
     xf[67, 128:192] *= 1e-9
-    xf[67, 130] = 1.734375 * 2.0 ** -15   # smallest s just below 2^-17: rewritten
+    xf[67, 130] = 1.734375 * 2.0 ** -15   # smallest s just below 2^-17
     xf[80:84] = 0.0                       # zero rows
     xf[84, 64:] = 0.0                     # one nonzero group
     return S.to_bf16_bits(xf), rng
 
 
-def test_quantize_operand_int4_row_exponents():
-    x, rng = row_exponent_inputs()
-    check_k1(x, act_layer(ones_smooth(x.shape[1]), 32, "int4", rng), "k1 int4 row exponents")
+def test_quantize_operand_int4_scale_range():
+    x, rng = scale_range_inputs()
+    check_k1(x, act_layer(ones_smooth(x.shape[1]), 32, "int4", rng), "k1 int4 scale range")
 
 
 # ------------------------------------------------------------------ kernel 2 partials
@@ -348,13 +357,12 @@ def test_linear_split_k(precision, M, K, N, rank):
     assert_output(y[rows], L.svdq_linear_ref(x[rows], lay), f"split-K {precision} M={M} K={K} N={N} r{rank}")
 
 
-def test_linear_int4_row_exponents():
-    # int4 activations enter the product as fp16 q * s * 2^-E[row]; E = 0 when
-    # every group scale s of the row is in [2^-17, 2^13), else the row is
-    # rewritten with E from its largest scale (the operand itself is checked
-    # bit for bit in test_quantize_operand_int4_row_exponents).  Rows of each
-    # kind, and rows on both sides of both bounds, each class checked on its own.
-    x, rng = row_exponent_inputs()
+def test_linear_int4_scale_range():
+    # int4 activations enter the product as fp8 codes with fp32 group scales
+    # applied to each group's exact integer sum (the operand itself is checked
+    # bit for bit in test_quantize_operand_int4_scale_range).  Rows of each
+    # scale class, each class checked on its own.
+    x, rng = scale_range_inputs()
     N, K = 192, x.shape[1]
     w = S.weight(N, K, 0.02, rng, spike_rank=4)
     b = S.bias(N, rng)
@@ -371,7 +379,7 @@ def test_linear_int4_row_exponents():
         for rr in rows if name == "bounds" else [rows]:
             sel = [rr] if name == "bounds" else rr
             _, excess, mre = L.output_errors(yf[sel], ref[sel])
-            print(f"[int4 row exponent {name} {sel if name == 'bounds' else ''}] excess {excess:.3e} MRE {mre:.3e}",
+            print(f"[int4 scale class {name} {sel if name == 'bounds' else ''}] excess {excess:.3e} MRE {mre:.3e}",
                   flush=True)
             assert excess <= 1e-2 and mre <= 2e-3, (name, sel)
 
@@ -689,7 +697,7 @@ def check_qkv(x, lay, heads, qn, kn, cos, sin, eps, label, rows=None):
     ref = L.qkv_norm_rope_ref(x[rows], lay, heads, qn, kn, eps, cos[rows], sin[rows])
     qk = 2 * heads * D
     yb = host_bits(y)[rows]
-    if ksplit(x.shape[0], 3 * heads * D, x.shape[1]) == 1:
+    if ksplit(x.shape[0], 3 * heads * D, x.shape[1], lay["precision"]) == 1:
         # the plain linear sums in the same order
         assert np.array_equal(yb[:, qk:], host_bits(plain)[rows][:, qk:]), label
     assert_output(torch.from_numpy(yb[:, qk:].view(np.int16).copy()).view(torch.bfloat16), ref[:, qk:], label + " v")

@@ -69,60 +69,41 @@ def test_operand_nvfp4_is_the_exact_dequantization():
     assert f16_exact(vals)
 
 
-def brute_exponent(scales_row):
-    """E by search: 0 if every nonzero scale lies in [2^-17, 2^13), else the
-    E with max(scale) * 2^-E in [2^12, 2^13)."""
-    nz = scales_row[scales_row > 0]
-    if nz.size == 0 or (nz.max() < 2.0 ** 13 and nz.min() >= 2.0 ** -17):
-        return 0
-    for E in range(-300, 300):
-        if 2.0 ** 12 <= nz.max() * 2.0 ** -E < 2.0 ** 13:
-            return E
-    raise AssertionError
+def test_operand_int4_codes_as_e4m3():
+    # every nibble: the E4M3 byte torch's float8_e4m3fn cast gives for the
+    # signed integer (the code 0x8 is -0, byte 0x80), and the byte decodes back
+    # to the integer
+    torch = pytest.importorskip("torch")
+    nib = np.tile(np.arange(16, dtype=np.uint8), 4)[None, :]  # [1, 64]: one int4 group
+    q8, sc = L.product_operand_ref(nib, F.bf16_bits(np.array([[0.5]], np.float32)), "int4")
+    mag = (nib & 7).astype(np.float32)
+    signed = np.where(nib & 8, -mag, mag)
+    want = torch.from_numpy(signed).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert q8.dtype == np.uint8 and np.array_equal(q8, want)
+    assert np.array_equal(q8[0, :16], [0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E,
+                                       0x80, 0xB8, 0xC0, 0xC4, 0xC8, 0xCA, 0xCC, 0xCE])
+    assert np.array_equal(F.e4m3_decode(q8).astype(np.float64), signed.astype(np.float64))
+    assert np.array_equal(np.signbit(F.e4m3_decode(q8)), np.signbit(signed))
+    assert sc.shape == (1, 1) and sc[0, 0] == 0.5
 
 
-def int4_rows():
+def test_operand_int4_reassembles_the_dequantization():
+    # codes times group scales give back dequant() for rows of every scale
+    # magnitude (no window: the scales stay separate)
     rng = np.random.default_rng(3)
-    K = 512
-    x = rng.standard_normal((12, K)).astype(np.float32)
-    x[1] *= 3e5                                   # all scales above 2^13
-    x[2] *= 1e-7                                  # all below 2^-17
-    x[3, 256:] *= 1e-9                            # spread 2^-33 .. 2^-1: beyond 2^29, rounded
-    x[4] = np.clip(x[4], -3, 3)
-    x[4, 5] = 57088.0                             # s = 8160: fits
-    x[5] = np.clip(x[5], -3, 3)
-    x[5, 70] = 57344.0                            # s = 8192: rewritten
-    x[6, 128:192] *= 1e-9
-    x[6, 130] = 7 * 2.0 ** -17                    # smallest s = 2^-17: fits
-    x[7, 128:192] *= 1e-9
-    x[7, 130] = 1.734375 * 2.0 ** -15             # just below 2^-17: rewritten
-    x[8] = 0.0                                    # zero row
-    x[9, 64:] = 0.0
-    x[10, :64] *= 1e20                            # one huge group, the rest far below 2^29 of it
-    x = F.bf16_round(x)
-    return quantize_int4(x, 64)
-
-
-def test_operand_int4_row_exponents_by_search():
-    nib, s, q = int4_rows()
-    vals, rs = L.product_operand_ref(nib, F.bf16_bits(s), "int4")
+    x = rng.standard_normal((12, 512)).astype(np.float32)
+    x[1] *= 3e5
+    x[2] *= 1e-7
+    x[3, 256:] *= 1e-9
+    x[4] = 0.0
+    x[5, 64:] = 0.0
+    x[6, :64] *= 1e20
+    nib, s, q = quantize_int4(F.bf16_round(x), 64)
+    q8, sc = L.product_operand_ref(nib, F.bf16_bits(s), "int4")
     deq = L.dequant(nib, F.bf16_bits(s), "int4")
-    for m in range(nib.shape[0]):
-        E = brute_exponent(s[m].astype(np.float64))
-        assert rs[m] == 2.0 ** E, m
-        assert f16_exact(vals[m])
-        sm = s[m].astype(np.float64)
-        near = np.repeat(sm >= sm.max() * 2.0 ** -29, 64)
-        # groups within 2^29 of the largest scale: exact (values * 2^E is the dequantization)
-        assert np.array_equal(vals[m][near] * 2.0 ** E, deq[m][near]), m
-        # below that: two roundings to binary16 (the scale, then the product),
-        # each at most half a binary16 subnormal quantum 2^-25 (relative 2^-11 above it)
-        far = ~near
-        if far.any():
-            err = np.abs(vals[m][far] * 2.0 ** E - deq[m][far])
-            bound = (7 * 2.0 ** -25 + 2.0 ** -25 + 2.0 ** -11 * np.abs(deq[m][far]) * 2.0 ** -E) * 2.0 ** E
-            assert np.all(err <= bound), m
-    assert [brute_exponent(s[m].astype(np.float64)) != 0 for m in (4, 5, 6, 7)] == [False, True, False, True]
+    vals = F.e4m3_decode(q8).astype(np.float64).reshape(12, 8, 64) * sc[..., None]
+    assert np.array_equal(vals.reshape(12, 512), deq)
+    assert np.array_equal(sc, s.astype(np.float64))
 
 
 # ------------------------------------------------------------------ bf16_half_ulp
