@@ -361,13 +361,15 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
 //     place; v columns keep h;
 //  4. the wave stores the tile with consecutive lanes on consecutive 16-byte
 //     pieces of a row.
-// Pieces of 8 columns never cross a head edge (D is a multiple of 8).
+// Pieces of 8 columns never cross a head edge (D is a multiple of 8).  NH =
+// 128 / D heads per tile, a compile-time constant.
+template <int NH>
 __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmArgs& args, f32x16 (&acc)[kIB][kJB], int m0, int nt,
                                                       int wave, int wm, int wn, int lane, int l32, int h,
                                                       uint8_t* tile_base, float* ssq) {
   const int M = (int)args.M, N = (int)args.N;
   const int heads = args.heads;
-  const int D = args.head_dim;
+  constexpr int D = kQkCols / NH;
   const int qk_cols = 2 * heads * D;
   uint8_t* gt = tile_base + (wave & 1) * (64 * kGeluRow);
   // every wave has left the main loop and every direct-to-LDS load has landed
@@ -394,7 +396,7 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmArgs& args, f32x
   // (the wave's own LDS writes and reads execute in order)
 
   // 2. RMSNorm factors of the lane's row, one per head of the tile
-  constexpr int kMaxHeads = kQkCols / 32;
+  constexpr int kMaxHeads = NH;
   uint8_t* rowp = gt + lane * kGeluRow;
   const int c0 = wn * (kJB * 32);                            // tile column of the wave's first column
   const int nqk = wn == 0 ? kJB * 32 : kQkCols - kJB * 32;  // q | k columns of this wave (96 | 32)
@@ -420,13 +422,13 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmArgs& args, f32x
     }
   }
   const int trow = wm * 64 + lane;  // row of the workgroup tile
-  const int nh = kQkCols / D;       // heads per tile
+  constexpr int nh = NH;
 #pragma unroll
   for (int hh = 0; hh < kMaxHeads; ++hh)
     if (hh < nh) ssq[(wn * kMaxHeads + hh) * kBM + trow] = ss[hh];
   lds_barrier();
   float rr[kMaxHeads];
-  const float invd = 1.0f / (float)D;  // exact: D is a power of two
+  constexpr float invd = 1.0f / (float)D;  // exact: D is a power of two
 #pragma unroll
   for (int hh = 0; hh < kMaxHeads; ++hh) {
     rr[hh] = 0.f;
@@ -979,8 +981,13 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       gelu_quant_epilogue(args, acc, m0, n0, wave, wm, wn, lane, l32, h, nmu,
                           wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, (float*)lds_w1);
     } else if constexpr (kQk) {
-      qk_norm_rope_epilogue(args, acc, m0, nt, wave, wm, wn, lane, l32, h,
-                            wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, (float*)lds_w1);
+      uint8_t* tb = wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0;
+      if (args.head_dim == 128)
+        qk_norm_rope_epilogue<1>(args, acc, m0, nt, wave, wm, wn, lane, l32, h, tb, (float*)lds_w1);
+      else if (args.head_dim == 64)
+        qk_norm_rope_epilogue<2>(args, acc, m0, nt, wave, wm, wn, lane, l32, h, tb, (float*)lds_w1);
+      else
+        qk_norm_rope_epilogue<4>(args, acc, m0, nt, wave, wm, wn, lane, l32, h, tb, (float*)lds_w1);
     } else if constexpr (kSplit) {
       // ---- fp32 partials of this split (no bias) ------------------------------
       float* part = args.partial + (size_t)blockIdx.y * M * N;
