@@ -198,9 +198,9 @@ size_t svdq_w4a4_mlp_workspace_bytes(int64_t M, const svdq_w4a4_layer* up,
  *
  * x      bf16 [M, up->K]; H = up->N must equal down->K
  * up     any svdq_w4a4 layer (int4 or nvfp4)
- * down   an nvfp4 layer (group 16): int4 activations need one power of two
- *        per row over the whole row, which a tile of the up projection does
- *        not see, so int4 returns SVDQ_EUNSUPPORTED
+ * down   an nvfp4 layer (group 16): the epilogue writes the nvfp4 operand
+ *        only (an int4 group of 64 would straddle the two waves that hold a
+ *        tile's 192 columns), so int4 returns SVDQ_EUNSUPPORTED
  * out    bf16 [M, down->N]; must not overlap x, the weights or the workspace
  * workspace  at least svdq_w4a4_mlp_workspace_bytes(M, up, down) bytes
  * Other rules (shapes, ranks, alignment, errors) as for svdq_w4a4_linear,
