@@ -72,6 +72,13 @@ size_t svdq_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision,
  *   Y = sum_g (q_x . q_w)_g * s_x * s_w * wtscale
  *       + (X_hat lora_down^T) lora_up^T + bias     -> bf16
  *
+ * nvfp4 activation range: the activations carry no tensor scale, so a group
+ * with amax <= 6 * 2^-10 (about 5.9e-3) gets scale 0 and zero codes (its
+ * residual product is dropped; the low-rank branch keeps it), and a group
+ * with amax above 6 * 448 = 2688 saturates.  The smoothing factors set where
+ * X_hat falls: a static per-tensor activation scale a is the same as smooth
+ * * a, with the weights prepared for that smoothing.
+ *
  * x         bf16 [M, K]
  * packed_w  uint8 [N, K/2] weight codes (residual after the low-rank split)
  * wscales   int4: bf16 [N, K/64]; nvfp4: uint8 E4M3 [N, K/16]

@@ -394,3 +394,41 @@ def test_prepare_from_factors_reproduces_prepare():
         for key in ("packed_w", "wscales", "resid"):
             assert np.array_equal(a[key], b[key]), key
         assert a["wtscale"] == b["wtscale"]
+
+
+# ------------------------------------------- nvfp4 activation range (tensor scale 1)
+def test_nvfp4_activation_range_low_magnitude_rows():
+    # With tensor scale 1 an activation group's E4M3 scale is E4M3(amax / 6):
+    # it rounds to zero when amax / 6 <= 2^-10 (half the smallest subnormal
+    # 2^-9, ties to even), i.e. amax <= 6 * 2^-10.  Such a group gets scale 0
+    # and all-zero codes, so a row whose groups all lie below that bound keeps
+    # only its 16-bit low-rank branch and the bias.  Above the bound the row's
+    # relative error stays of the order it has at unit magnitude.
+    rng = np.random.default_rng(17)
+    K, N, r = 256, 64, 16
+    w = S.weight(N, K, 0.05, rng, spike_rank=2)
+    lay = L.prepare_svdq_layer(w, _ones_smooth(K), r, "nvfp4", bias_bits=S.bias(N, rng))
+    # unit row: every 16-value group has amax exactly 1
+    u = rng.uniform(-1.0, 1.0, (4, K)).astype(np.float32)
+    u[:, ::16] = np.where(rng.random((4, K // 16)) < 0.5, -1.0, 1.0)
+    up = F.bf16_to_f32(lay["lora_up"]).astype(np.float64)
+    bias = F.bf16_to_f32(lay["bias"]).astype(np.float64)
+    err = {}
+    for e in (0, 4, 7, 8, 12):
+        x_bits = F.bf16_bits(u * np.float32(2.0 ** -e))  # exact: power-of-two scaling of bf16 values
+        xf = F.bf16_to_f32(x_bits).astype(np.float64)
+        act = L.svdq_quantize_act(x_bits, lay["smooth"], lay["lora_down"], "nvfp4")
+        y = L.svdq_linear_ref(x_bits, lay, act)
+        exact = xf @ w.T
+        err[e] = np.linalg.norm(y - bias - exact) / np.linalg.norm(exact)
+        if 2.0 ** -e <= 6 * 2.0 ** -10:
+            # below the range: zero scales and codes, low rank + bias only
+            assert not act["scales"].any() and not act["codes"].any()
+            np.testing.assert_array_equal(y, act["lora_act"] @ up.T + bias[None, :])
+        else:
+            assert act["scales"].all()
+    print({k: f"{v:.3e}" for k, v in err.items()})
+    # inside the range (amax 2^-7 uses the subnormal scale 2^-9) the error is
+    # of the unit row's order; below it the residual branch is lost
+    assert err[4] <= 1.5 * err[0] and err[7] <= 3.0 * err[0]
+    assert err[8] > err[0] and err[12] > err[0]
