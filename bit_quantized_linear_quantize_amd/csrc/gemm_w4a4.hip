@@ -147,6 +147,14 @@ struct RawStage8 {
   uint32_t sw[kWP];
 };
 
+// The operands of one 16-wide rank slice of the low-rank up projection, as
+// loaded: lora_act (fp32) of the wave's two 32-row blocks, lora_up (bf16) of
+// its three 32-column blocks.
+struct LoraOps {
+  f32x4 a[kIB][2];
+  u32x4 b[kJB];
+};
+
 // Logical tile of this workgroup: consecutive workgroups land on different
 // XCDs, so first gather the ids that share an XCD, then walk groups of
 // kGroupM M-tiles column by column.
@@ -201,7 +209,8 @@ static_assert(2 * kWM * 16 * kXchRow * 4 <= kBN * kWRow, "the exchange fits the 
 // `xch` is LDS of 2 kWM 16 kXchRow floats, free during this epilogue.
 __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16 (&acc)[kIB][kJB], int m0, int n0,
                                                     int wave, int wm, int wn, int lane, int l32, int h,
-                                                    const float* nmu, uint8_t* tile_base, float* xch) {
+                                                    const float* nmu, uint8_t* tile_base, float* xch,
+                                                    bool add_bias) {
   const int M = (int)args.M, N = (int)args.N;
   uint8_t* gt = tile_base + (wave & 1) * (64 * kGeluRow);
   // every wave has left the main loop (its LDS reads are done) and every
@@ -216,7 +225,7 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
 #pragma unroll
   for (int j = 0; j < kJB; ++j) {
     const int col = n0 + wn * (kJB * 32) + j * 32 + l32;
-    const float bv = (bias && col < N) ? bf16_bits_to_f32(bias[col]) : 0.f;
+    const float bv = (add_bias && bias && col < N) ? bf16_bits_to_f32(bias[col]) : 0.f;
 #pragma unroll
     for (int i = 0; i < kIB; ++i)
 #pragma unroll
@@ -366,7 +375,7 @@ __device__ __forceinline__ void gelu_quant_epilogue(const GemmArgs& args, f32x16
 template <int NH>
 __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmArgs& args, f32x16 (&acc)[kIB][kJB], int m0, int nt,
                                                       int wave, int wm, int wn, int lane, int l32, int h,
-                                                      uint8_t* tile_base, float* ssq) {
+                                                      uint8_t* tile_base, float* ssq, bool add_bias) {
   const int M = (int)args.M, N = (int)args.N;
   const int heads = args.heads;
   constexpr int D = kQkCols / NH;
@@ -384,7 +393,7 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmArgs& args, f32x
 #pragma unroll
   for (int j = 0; j < kJB; ++j) {
     const int col = qk_col(nt, wn * (kJB * 32) + j * 32 + l32, qk_cols);
-    const float bv = bias ? bf16_bits_to_f32(bias[col]) : 0.f;
+    const float bv = (add_bias && bias) ? bf16_bits_to_f32(bias[col]) : 0.f;
 #pragma unroll
     for (int i = 0; i < kIB; ++i)
 #pragma unroll
@@ -546,6 +555,61 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
+  // ---- low-rank up: acc += (lora_act_hi + lora_act_lo) lora_up^T -------------
+  // (split K: in split 0 only).  The int4 path runs it first, while the
+  // loads of its first stages are in flight; nvfp4 runs it after the main
+  // loop, whose sum is first multiplied by the weight tensor scale.
+  const bool lora_here = !kSplit || blockIdx.y == 0;
+  auto lora_load = [&](int rs16, LoraOps& o) {
+    constexpr int rank = RB * 16;
+    const uint16_t* __restrict__ lu = (const uint16_t*)args.lora_up;
+#pragma unroll
+    for (int i = 0; i < kIB; ++i) {
+      const int row = min(m0 + wm * (kIB * 32) + i * 32 + l32, M - 1);
+      const float* la = args.lora_act + (size_t)row * rank + rs16 * 16 + h * 8;
+      o.a[i][0] = *(const f32x4*)la;
+      o.a[i][1] = *(const f32x4*)(la + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < kJB; ++j) {
+      const int tc = wn * (kJB * 32) + j * 32 + l32;
+      const int col = kQk ? pcol(tc) : min(n0 + tc, N - 1);
+      o.b[j] = *(const u32x4*)(lu + (size_t)col * rank + rs16 * 16 + h * 8);
+    }
+  };
+  auto lora_mma = [&](const LoraOps& o) {
+    bf16x8 ahi[kIB], alo[kIB];
+#pragma unroll
+    for (int i = 0; i < kIB; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = o.a[i][e >> 2][e & 3];
+        const __bf16 hb = (__bf16)v;
+        ahi[i][e] = hb;
+        alo[i][e] = (__bf16)(v - (float)hb);
+      }
+#pragma unroll
+    for (int i = 0; i < kIB; ++i)
+#pragma unroll
+      for (int j = 0; j < kJB; ++j) {
+        const bf16x8 bo = __builtin_bit_cast(bf16x8, o.b[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[i], bo, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[i], bo, acc[i][j], 0, 0, 0);
+      }
+  };
+  auto lowrank_up = [&]() {
+    if constexpr (RB > 0 && !PARTIALS) {
+      if (lora_here) {
+#pragma unroll
+        for (int rs16 = 0; rs16 < RB; ++rs16) {
+          LoraOps o;
+          lora_load(rs16, o);
+          lora_mma(o);
+        }
+      }
+    }
+  };
+
   if constexpr (kFp8) {
     // ---- int4: fp8 operands, group scales on the vector ALU --------------------
     // A stage s (128 values of K, two groups of 64) comes straight from
@@ -691,9 +755,48 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       group(r, s + 3, IC<p>{});
     };
 
+    // Prologue.  The bias (except for split-K partials) and, for ranks up to
+    // 32, the low-rank operands are requested before the first stages, so
+    // that the wait for them is not a wait for the stages; the sum starts
+    // from the bias, then adds the low rank, then the groups (the epilogues
+    // add no bias on this path).
+    constexpr bool kLoraFirst = RB > 0 && RB <= 2;
+    LoraOps lops[kLoraFirst ? RB : 1];
+    if constexpr (kLoraFirst) {
+      if (lora_here) {
+#pragma unroll
+        for (int rs16 = 0; rs16 < RB; ++rs16) lora_load(rs16, lops[rs16]);
+      }
+    }
+    float bv[kJB];
+    if constexpr (!kSplit) {
+      const uint16_t* bias = (const uint16_t*)args.bias;
+#pragma unroll
+      for (int j = 0; j < kJB; ++j) {
+        const int col = pcol(wn * (kJB * 32) + j * 32 + l32);
+        bv[j] = (bias && col < N) ? bf16_bits_to_f32(bias[col]) : 0.f;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     RawStage8 r0, r1;
     group(r0, 0, IC<0>{});
     group(r1, 1, IC<1>{});
+    if constexpr (!kSplit) {
+#pragma unroll
+      for (int i = 0; i < kIB; ++i)
+#pragma unroll
+        for (int j = 0; j < kJB; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = bv[j];
+    }
+    if constexpr (kLoraFirst) {
+      if (lora_here) {
+#pragma unroll
+        for (int rs16 = 0; rs16 < RB; ++rs16) lora_mma(lops[rs16]);
+      }
+    } else {
+      lowrank_up();
+    }
 #pragma unroll
     for (int q = 0; q < 3; ++q) store_part(lds_w0, 0, r0, q);
     group(r0, 2, IC<2>{});
@@ -913,7 +1016,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   stage_barrier();  // (each wave has its stage-0 A loads: they precede the W loads it staged)
   rd(lds_a0, lds_w0, 0, 0);
   // Six stages per iteration (the A ring of three times the two raw register
-  // stages), all straight-line code.  Stages past the last (up to four when
+  // stages), all straight-line code.  Stages past the last (up to five when
   // the stage count is not a multiple of six) load zeros and add nothing.
   for (int s = 0; s < nstages; s += 6) {
     compute(IC<0>{}, s, r1);
@@ -938,56 +1041,20 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmul_rn(acc[i][j][e], t);
     }
-    // ---- low-rank up: acc += (lora_act_hi + lora_act_lo) lora_up^T -----------
-    // (split K: in split 0 only)
-    if constexpr (RB > 0) {
-      if (!kSplit || blockIdx.y == 0) {
-        constexpr int rank = RB * 16;
-        const uint16_t* __restrict__ lu = (const uint16_t*)args.lora_up;
-#pragma unroll
-        for (int rs16 = 0; rs16 < RB; ++rs16) {
-          bf16x8 ahi[kIB], alo[kIB], bo[kJB];
-#pragma unroll
-          for (int i = 0; i < kIB; ++i) {
-            const int row = min(m0 + wm * (kIB * 32) + i * 32 + l32, M - 1);
-            const float* la = args.lora_act + (size_t)row * rank + rs16 * 16 + h * 8;
-            const f32x4 v0 = *(const f32x4*)la, v1 = *(const f32x4*)(la + 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float v = e < 4 ? v0[e] : v1[e - 4];
-              const __bf16 hb = (__bf16)v;
-              ahi[i][e] = hb;
-              alo[i][e] = (__bf16)(v - (float)hb);
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < kJB; ++j) {
-            const int tc = wn * (kJB * 32) + j * 32 + l32;
-            const int col = kQk ? pcol(tc) : min(n0 + tc, N - 1);
-            bo[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(lu + (size_t)col * rank + rs16 * 16 + h * 8));
-          }
-#pragma unroll
-          for (int i = 0; i < kIB; ++i)
-#pragma unroll
-            for (int j = 0; j < kJB; ++j) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[i], bo[j], acc[i][j], 0, 0, 0);
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[i], bo[j], acc[i][j], 0, 0, 0);
-            }
-        }
-      }
-    }
+    // ---- low-rank up (int4: done before the main loop) -----------------------
+    if constexpr (!kFp8) lowrank_up();
     if constexpr (EPI == kEpiGelu) {
       // tile of wave w: base (w < 2: a0, < 4: a1, < 6: a2, else w0) + (w & 1) 64 rows
       gelu_quant_epilogue(args, acc, m0, n0, wave, wm, wn, lane, l32, h, nmu,
-                          wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, (float*)lds_w1);
+                          wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0, (float*)lds_w1, !kFp8);
     } else if constexpr (kQk) {
       uint8_t* tb = wave < 2 ? lds_a0 : wave < 4 ? lds_a1 : wave < 6 ? lds_a2 : lds_w0;
       if (args.head_dim == 128)
-        qk_norm_rope_epilogue<1>(args, acc, m0, nt, wave, wm, wn, lane, l32, h, tb, (float*)lds_w1);
+        qk_norm_rope_epilogue<1>(args, acc, m0, nt, wave, wm, wn, lane, l32, h, tb, (float*)lds_w1, !kFp8);
       else if (args.head_dim == 64)
-        qk_norm_rope_epilogue<2>(args, acc, m0, nt, wave, wm, wn, lane, l32, h, tb, (float*)lds_w1);
+        qk_norm_rope_epilogue<2>(args, acc, m0, nt, wave, wm, wn, lane, l32, h, tb, (float*)lds_w1, !kFp8);
       else
-        qk_norm_rope_epilogue<4>(args, acc, m0, nt, wave, wm, wn, lane, l32, h, tb, (float*)lds_w1);
+        qk_norm_rope_epilogue<4>(args, acc, m0, nt, wave, wm, wn, lane, l32, h, tb, (float*)lds_w1, !kFp8);
     } else if constexpr (kSplit) {
       // ---- fp32 partials of this split (no bias) ------------------------------
       float* part = args.partial + (size_t)blockIdx.y * M * N;
@@ -1015,13 +1082,19 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
 #pragma unroll
       for (int j = 0; j < kJB; ++j) {
         const int col = n0 + wn * (kJB * 32) + j * 32 + l32;
-        const float bv = (bias && col < N) ? bf16_bits_to_f32(bias[col]) : 0.f;
+        // (int4: the sum started from the bias)
+        const float bv = (!kFp8 && bias && col < N) ? bf16_bits_to_f32(bias[col]) : 0.f;
 #pragma unroll
         for (int i = 0; i < kIB; ++i)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
+          for (int e = 0; e < 16; e += 2) {
+            // rows r and r + 1 of the lane's column, one packed RNE conversion
             const int r = i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-            *(uint16_t*)(gt + r * kGeluRow + (j * 32 + l32) * 2) = (uint16_t)f32_to_bf16_bits(acc[i][j][e] + bv);
+            const float v0 = kFp8 ? acc[i][j][e] : acc[i][j][e] + bv;
+            const float v1 = kFp8 ? acc[i][j][e + 1] : acc[i][j][e + 1] + bv;
+            const uint32_t pk = bf16x2_rne(v0, v1);
+            *(uint16_t*)(gt + r * kGeluRow + (j * 32 + l32) * 2) = (uint16_t)pk;
+            *(uint16_t*)(gt + (r + 1) * kGeluRow + (j * 32 + l32) * 2) = (uint16_t)(pk >> 16);
           }
       }
       const int c0 = n0 + wn * (kJB * 32);
