@@ -144,7 +144,7 @@ __device__ __forceinline__ u32x4 int4x16_to_fp8(u32x2 w) {
 // tile row tid/8 + 64 j, and the bf16 scales of the stage's two groups.
 struct RawStage8 {
   u32x2 w[kWP];
-  uint32_t sw[kWP];
+  uint32_t sw;  // the two bf16 group scales of W row srow (24 rows per wave)
 };
 
 // The operands of one 16-wide rank slice of the low-rank up projection, as
@@ -633,13 +633,16 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
                                                    (size_t)(N - w_base) * G * 2 - s0 * 4);
     const __amdgpu_buffer_rsrc_t zero_rs = make_rsrc(args.w_codes, 0);
     const int lc = tid & 7, lr = tid >> 3;
-    int w_off[kWP], ws_off[kWP];
+    int w_off[kWP];
 #pragma unroll
     for (int j = 0; j < kWP; ++j) {
       const int wrow = kQk ? pcol(lr + kRP * j) : lr + kRP * j;  // row from the descriptor base
       w_off[j] = wrow * K2 + lc * 8;
-      ws_off[j] = wrow * G * 2;
     }
+    // W scales: wave w loads those of tile rows 24 w .. 24 w + 23, one row
+    // per lane (lanes 24-63 repeat rows), one load per wave and stage
+    const int srow = wave * (kBN / kWaves) + lane % (kBN / kWaves);
+    const int ws_off = (kQk ? pcol(srow) : srow) * G * 2;
     int dma_off[kADma];
 #pragma unroll
     for (int d = 0; d < kADma; ++d) {
@@ -684,18 +687,19 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       for (int j = 0; j < kWP; ++j) {
         r.w[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(live ? w_rs : zero_rs, w_off[j],
                                                                                 s * 64, 0));
-        r.sw[j] = __builtin_amdgcn_raw_buffer_load_b32(live ? ws_rs : zero_rs, ws_off[j], s * 4, 0);
       }
+      r.sw = __builtin_amdgcn_raw_buffer_load_b32(live ? ws_rs : zero_rs, ws_off, s * 4, 0);
     };
-    // staging of W piece p of a raw stage into W buffer Tw (its scales into
-    // wsc half wb)
+    // staging of W piece p of a raw stage into W buffer Tw (with piece 0, the
+    // wave's W scales into wsc half wb)
     auto store_part = [&](uint8_t* Tw, int wb, const RawStage8& r, int p) {
       const int wrow = lr + kRP * p;
       *(u32x4*)(Tw + wrow * kWRow + lc * 16) = int4x16_to_fp8(r.w[p]);
-      // (the eight lanes of a row write the same values: no branch here,
-      // which would split the schedule of the products around it)
-      wsc[(wb * 2 + 0) * kBN + wrow] = bf16_lo(r.sw[p]);
-      wsc[(wb * 2 + 1) * kBN + wrow] = bf16_hi(r.sw[p]);
+      if (p == 0) {
+        // (lanes holding the same row write the same values)
+        wsc[(wb * 2 + 0) * kBN + srow] = bf16_lo(r.sw);
+        wsc[(wb * 2 + 1) * kBN + srow] = bf16_hi(r.sw);
+      }
     };
     // one stage: per group, per 32 x 32 tile one product of 64 values of K
     auto compute = [&](auto P, int s, RawStage8& r) {
