@@ -14,16 +14,17 @@
 // of 32 x 32.  Tiles are visited in groups of 4 M-tiles, mapped so that the
 // workgroups on one XCD share A and W tiles in its L2.  Two datapaths:
 //
-// int4 -- fp8 operands, scales on the vector ALU.  Every code |q| <= 7 is an
-// exact fp8 E4M3 value, so one v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 block
-// and group (K = 64) gives the group's exact integer sums P, and the bf16
+// int4 -- fp8 operands, group scales applied per group.  Every code |q| <= 7
+// is an exact fp8 E4M3 value, so one v_mfma_f32_32x32x64_f8f6f4 per 32 x 32
+// block and group (K = 64) gives the group's exact integer sums P.  The bf16
 // group scales (which the instruction's power-of-two block scales cannot
-// express) are applied as acc += P * fl32(s_x s_w) (the scale product is
-// exact).  The quantize kernel writes A as E4M3 bytes with fp32 group scales;
-// a stage is 128 values of K (two groups).  This route needs two VALU
-// operations per output and group, but its matrix work is half that of the
-// fp16 route below, and it runs at a lower power: the fp16 route on int4
-// data is held back by the clock the chip sustains under full matrix load.
+// express) are applied as acc += P * (s_x s_w), the 32 x 32 scale products
+// (exact in fp32) coming from one bf16 outer-product instruction
+// (v_mfma_f32_32x32x8_bf16) and the accumulation from one FMA per output.
+// The quantize kernel writes A as E4M3 bytes with fp32 group scales; a stage
+// is 128 values of K (two groups).  The matrix work is half that of the fp16
+// route below, and it runs at a lower power: the fp16 route on int4 data is
+// held back by the clock the chip sustains under full matrix load.
 //
 // nvfp4 -- scales folded into exact fp16 operands.  An E2M1 code times its
 // E4M3 block scale needs at most 2 + 4 significant bits, an exact fp16, so
@@ -508,8 +509,13 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   // int4 (fp8 operands): the group scales of the stages in LDS, A per A
   // buffer [group][row], W per W buffer [group][row]
   constexpr bool kFp8 = PREC == kInt4 && !PARTIALS;
-  __shared__ __attribute__((aligned(16))) float asc[kFp8 ? kAStages * 2 * kBM : 1];
-  __shared__ __attribute__((aligned(16))) float wsc[kFp8 ? 2 * 2 * kBN : 1];
+  // (one object per A buffer, like the A buffers themselves: a read of one
+  // does not wait for the direct-to-LDS loads still filling another)
+  __shared__ __attribute__((aligned(16))) float asc0[kFp8 ? 2 * kBM : 1];
+  __shared__ __attribute__((aligned(16))) float asc1[kFp8 ? 2 * kBM : 1];
+  __shared__ __attribute__((aligned(16))) float asc2[kFp8 ? 2 * kBM : 1];
+  // (W: bf16 bits of s_w / 2, the operand of the scale-product instruction)
+  __shared__ __attribute__((aligned(16))) uint16_t wsc[kFp8 ? 2 * 2 * kBN : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -611,15 +617,16 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   };
 
   if constexpr (kFp8) {
-    // ---- int4: fp8 operands, group scales on the vector ALU --------------------
+    // ---- int4: fp8 operands, group scales per group ----------------------------
     // A stage s (128 values of K, two groups of 64) comes straight from
     // memory to LDS as fp8 codes in the same swizzled 16-byte chunks as the
     // fp16 operand of the other path (8 chunks per 128-byte row); its group
-    // scales (fp32 [M, K/64]) likewise, into asc.  W stage s is staged
+    // scales (fp32 [M, K/64]) likewise, into asc0-2.  W stage s is staged
     // through registers: int4 nibbles -> fp8 bytes (rows of kWRow bytes),
-    // its bf16 group scales -> fp32 in wsc.  Per group, each 32 x 32 tile is
-    // one v_mfma_f32_32x32x64_f8f6f4 of exact integer sums P (|P| <= 64 * 49)
-    // and acc += P * (s_x * s_w) (the scale product is exact in fp32).
+    // its bf16 group scales halved -> wsc.  Per group, each 32 x 32 tile is
+    // one v_mfma_f32_32x32x64_f8f6f4 of exact integer sums P (|P| <= 64 * 49),
+    // one bf16 outer product of the scales, and acc += P * (s_x * s_w) (the
+    // scale product is exact in fp32).
     // Loads run three stages ahead for A and two for W, as in the other path.
     const int G = K >> 6;
     const __amdgpu_buffer_rsrc_t a_rs = make_rsrc((const uint8_t*)args.act + (size_t)m0 * K + s0 * 128,
@@ -665,11 +672,16 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       if constexpr (decltype(c)::value % 2 == 0) return lds_w0;
       else return lds_w1;
     };
+    auto ascbuf = [&](auto c) -> float* {
+      constexpr int i = decltype(c)::value % kAStages;
+      if constexpr (i == 0) return asc0;
+      else if constexpr (i == 1) return asc1;
+      else return asc2;
+    };
     // loads of stage s: A and its scales into A buffer ab (direct to LDS),
     // then W into r
     auto group = [&](RawStage8& r, int s, auto ab) {
       const bool live = s < nstages;
-      constexpr int b = decltype(ab)::value % kAStages;
       uint8_t* dst = abuf(ab) + wave * (kADma * 64 * 16);
 #pragma unroll
       for (int d = 0; d < kADma; ++d)
@@ -678,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
                                                  dma_off[d], s * 128, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           live ? as_rs : zero_rs,
-          (__attribute__((address_space(3))) void*)(asc + (b * 2 + sc_g) * kBM + (wave & 3) * 64), 4, sc_off, s * 8,
+          (__attribute__((address_space(3))) void*)(ascbuf(ab) + sc_g * kBM + (wave & 3) * 64), 4, sc_off, s * 8,
           0, 0);
       // the W loads of the stage stay behind its A loads: a wave that has
       // waited for its W registers has also received its A stage
@@ -696,9 +708,10 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       const int wrow = lr + kRP * p;
       *(u32x4*)(Tw + wrow * kWRow + lc * 16) = int4x16_to_fp8(r.w[p]);
       if (p == 0) {
-        // (lanes holding the same row write the same values)
-        wsc[(wb * 2 + 0) * kBN + srow] = bf16_lo(r.sw);
-        wsc[(wb * 2 + 1) * kBN + srow] = bf16_hi(r.sw);
+        // s_w / 2 as bf16 (exact: a power-of-two step of a normal value);
+        // lanes holding the same row write the same values
+        wsc[(wb * 2 + 0) * kBN + srow] = (uint16_t)(__float_as_uint(__fmul_rn(bf16_lo(r.sw), 0.5f)) >> 16);
+        wsc[(wb * 2 + 1) * kBN + srow] = (uint16_t)(__float_as_uint(__fmul_rn(bf16_hi(r.sw), 0.5f)) >> 16);
       }
     };
     // one stage: per group, per 32 x 32 tile one product of 64 values of K
@@ -711,13 +724,20 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
         i32x8 aop[kIB], bop[kJB];
-        float sw[kJB];
+        // the scale products s_x s_w of a 32 x 32 block come from one bf16
+        // instruction of K = 8 (an outer product): element 0 of each lane's
+        // four values of K is s_x (A, row l32 of block i) or s_w / 2 (B,
+        // column l32 of block j), the rest zero; lanes 32-63 (K = 4..7)
+        // repeat them, so D = 2 (s_x s_w / 2) = s_x s_w, exact in fp32
+        uint32_t as16[kIB], bs16[kJB];
 #pragma unroll
         for (int i = 0; i < kIB; ++i) {
           const int row = wm * (kIB * 32) + i * 32 + l32;
           const u32x4 lo = *(const u32x4*)(Ta + row * kARow + a_pos(row, 4 * gi + 2 * h) * 16);
           const u32x4 hi = *(const u32x4*)(Ta + row * kARow + a_pos(row, 4 * gi + 2 * h + 1) * 16);
           aop[i] = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          // the upper half of the fp32 scale: its bf16 bits (s_x is a bf16 value)
+          as16[i] = ((const uint16_t*)(ascbuf(IC<p>{}) + gi * kBM + row))[1];
         }
 #pragma unroll
         for (int j = 0; j < kJB; ++j) {
@@ -725,34 +745,30 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
           const uint8_t* src = Tw + col * kWRow + 64 * gi + 32 * h;
           const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
           bop[j] = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-          sw[j] = wsc[(wb * 2 + gi) * kBN + col];
+          bs16[j] = wsc[(wb * 2 + gi) * kBN + col];
         }
 #pragma unroll
         for (int i = 0; i < kIB; ++i) {
-          // s_x of the lane's 16 rows of tile row i: rows 8 q + 4 h + 0..3
-          f32x4 sx[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            sx[q] = *(const f32x4*)(asc + (ab * 2 + gi) * kBM + wm * (kIB * 32) + i * 32 + q * 8 + h * 4);
 #pragma unroll
           for (int j = 0; j < kJB; ++j) {
             const f32x16 pr = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[i], bop[j], f32x16{}, 0, 0, 0, 0,
                                                                             0, 0);
+            const f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(
+                __builtin_bit_cast(s16x4, u32x2{as16[i], 0u}), __builtin_bit_cast(s16x4, u32x2{bs16[j], 0u}), f32x16{},
+                0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              acc[i][j][e] = __fmaf_rn(pr[e], __fmul_rn(sx[e >> 2][e & 3], sw[j]), acc[i][j][e]);
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmaf_rn(pr[e], sc[e], acc[i][j][e]);
           }
           // stage a third of the next W stage among the products
           if (gi * kIB + i < 3) store_part(Nw, (p + 1) % 2, r, gi * kIB + i);
-          // order of the tile row's products and scalings: two products,
-          // the first tile's 32 scaling operations (its product has had the
-          // second's issue time to finish), the third product, the other 64
-          // (measured 71.3 -> 66.8 us at M=4096, K=N=3072 against the
-          // compiler's own order)
+          // order of a tile row's instructions: the products of two blocks,
+          // the scaling of the first, the third block's products, the rest
+          // (62.5 us against 63.5 us in the compiler's own order at M = 4096,
+          // K = N = 3072)
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
         }
       }
       stage_barrier();
