@@ -356,6 +356,23 @@ def bench_mfma_peak(torch, stream, iters=20000):
             run()
         out[key] = {"measured_TFLOPs": round(gflops / (time_events(run, 5, stream) * 1e-3) / 1e12, 1),
                     "instruction": "v_mfma_scale_f32_32x32x64_f8f6f4 + 2 VALU per output and group"}
+    # the int4 product kernel's inner loop as built: per tile and group one
+    # f8f6f4 product, one bf16 outer-product instruction for the scale
+    # products and one FMA per output, on the kernel's 64 x 96 wave tile
+    fn = lib.svdq_peak_outer_scaled
+    fn.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    oiters = iters // 2
+    oflops = blocks * 8 * oiters * 6 * 2.0 * 32 * 32 * 64
+    for key, fmt in (("int4_as_fp8_outer_scaled", 0), ("int4_as_fp6_outer_scaled", 2)):
+        def run():
+            if fn(fmt, oiters, blocks, sink.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("outer-scaled probe launch failed")
+        for _ in range(3):
+            run()
+        out[key] = {"measured_TFLOPs": round(oflops / (time_events(run, 5, stream) * 1e-3) / 1e12, 1),
+                    "instruction": "v_mfma_scale_f32_32x32x64_f8f6f4 + v_mfma_f32_32x32x8_bf16 (scale products) "
+                                   "+ 1 FMA per output and group"}
     return out
 
 
@@ -679,8 +696,8 @@ def main():
                 "peak": PEAK["fp8"], "unit": "TFLOP/s", "frac": round(k2_tops / PEAK["fp8"], 4),
                 "traffic": measured_traffic("gemm_w4a4_lora_up", "int4_4096x3072x3072_r32"),
                 "avg_launch_us": round(r4["k2_ms"] * 1e3, 2),
-                "instruction": "v_mfma_f32_32x32x64_f8f6f4 (int4 codes as fp8 E4M3) + 2 fp32 VALU per output "
-                               "and group (s_x s_w)",
+                "instruction": "v_mfma_f32_32x32x64_f8f6f4 (int4 codes as fp8 E4M3) + v_mfma_f32_32x32x8_bf16 "
+                               "(scale products s_x s_w) + 1 fp32 FMA per output and group",
                 "frac_of_f16_peak": round(k2_tops / PEAK["f16"], 4)}
 
     extra = {"int4": {"step_us": round(r4["ms"] * 1e3, 2),
@@ -751,7 +768,7 @@ def main():
         peak = bench_mfma_peak(torch, stream)
         if peak:
             extra["mfma_peak"] = peak
-            g8 = peak["int4_as_fp8_group_scaled"]["measured_TFLOPs"]
+            g8 = peak["int4_as_fp8_outer_scaled"]["measured_TFLOPs"]
             roofline["measured_inner_loop_peak"] = g8
             roofline["frac_of_measured_peak"] = round(k2_tops / g8, 4)
         extra["mlp_pair_nvfp4_3072_12288_3072"] = bench_mlp_pair(bq, S, torch, np, x, M, K, rank, stream)

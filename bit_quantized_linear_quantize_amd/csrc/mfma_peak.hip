@@ -1,5 +1,6 @@
-// Measured peak of the matrix instruction the product kernel uses
-// (v_mfma_f32_32x32x16_f16).
+// Measured peaks of the matrix instructions the product kernel uses
+// (v_mfma_f32_32x32x16_f16; the int4 inner loop of f8f6f4 products with
+// scale products from a bf16 instruction).
 //
 // One workgroup of 8 waves per CU (two waves per SIMD); every wave issues
 // `iters` rounds of 8 independent 32x32x16 f16 products (8 accumulators, so
@@ -143,7 +144,83 @@ __global__ __launch_bounds__(512) void group_scaled_probe_kernel(int64_t iters, 
   sink[t] = s;
 }
 
+// The int4 product kernel's inner loop as it is built: per 32 x 32 tile and
+// group one f8f6f4 product P (codes as fp8 or fp6), one bf16 outer-product
+// instruction of K = 8 for the scale products s_x s_w (element 0 of each
+// lane's four values the scale, the rest zero), and acc += P * (s_x s_w), 16
+// FMAs.  A wave computes a 64 x 96 block (2 x 3 tiles), the kernel's wave
+// tile; its operands are marked as changing every group.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT>
+__global__ __launch_bounds__(512) void outer_scaled_probe_kernel(int64_t iters, float* sink) {
+  const uint32_t t = blockIdx.x * 512u + threadIdx.x;
+  i32x8 a[2], b[3];
+  uint32_t as[2], bs[3];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t h0 = peak_hash(t * 97u + i), h1 = peak_hash(~(t * 89u + i));
+    a[0][i] = (int)(h0 & 0x2d3d2d3du);
+    a[1][i] = (int)(h1 & 0x3d2d3d2du);
+    b[0][i] = (int)((h0 >> 3) & 0x2d3d2d3du);
+    b[1][i] = (int)((h1 >> 3) & 0x3d2d3d2du);
+    b[2][i] = (int)((h0 >> 5) & 0x3d2d2d3du);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) as[i] = 0x3c00u + (peak_hash(t + 7u * i) & 0x7fu);  // bf16 bits of ~2^-7
+#pragma unroll
+  for (int j = 0; j < 3; ++j) bs[j] = 0x3c80u + (peak_hash(t + 11u * j) & 0x7fu);
+  f32x16 acc[2][3];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const f32x16 zero = {};
+  for (int64_t it = 0; it < iters; ++it) {
+    // (the compiler may not keep the operands from one group to the next)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(a[i]), "+v"(as[i]));
+#pragma unroll
+    for (int j = 0; j < 3; ++j) asm volatile("" : "+v"(b[j]), "+v"(bs[j]));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], zero, FMT, FMT, 0, 0x7f, 0, 0x7f);
+        const f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, u32x2{as[i], 0u}),
+                                                                   __builtin_bit_cast(s16x4, u32x2{bs[j], 0u}), zero,
+                                                                   0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(p[e], sc[e], acc[i][j][e]);
+      }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) s += acc[i][j][0] + acc[i][j][15];
+  sink[t] = s;
+}
+
 extern "C" {
+
+// The product kernel's inner loop above: `iters` groups per wave (6
+// products of 32 x 32 x 64, 131072 flops each).  fmt 0: fp8 operands, 2:
+// fp6.  Returns 0, -5 on a launch error, -1 on another fmt.
+int svdq_peak_outer_scaled(int fmt, int64_t iters, int blocks, void* sink, void* stream) {
+  if (fmt == 0)
+    hipLaunchKernelGGL(outer_scaled_probe_kernel<0>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters,
+                       (float*)sink);
+  else if (fmt == 2)
+    hipLaunchKernelGGL(outer_scaled_probe_kernel<2>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters,
+                       (float*)sink);
+  else
+    return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // The group-scaled int4 product loop above: `iters` rounds of two groups per
 // wave (8 products of 32 x 32 x 64, 131072 flops each).  fmt 0: fp8
