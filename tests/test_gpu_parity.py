@@ -333,10 +333,13 @@ def test_linear_full_size(cfg1_layers, which):
 
 
 @pytest.mark.parametrize("precision", ["int4", "nvfp4"])
-@pytest.mark.parametrize("M,K,N,rank", [(33, 16384, 320, 32), (70, 128, 64, 16), (5, 128, 448, 0)])
+@pytest.mark.parametrize("M,K,N,rank", [(33, 16384, 320, 32), (70, 128, 64, 16), (5, 128, 448, 0),
+                                        (300, 384, 320, 32)])
 def test_linear_k_extremes(precision, M, K, N, rank):
     # K = 16384 (the largest accepted: 256 stages, not a multiple of the
-    # loop's six) and K = 128 (two stages); N with a partial 192-column tile
+    # loop's six), K = 128 (two stages) and K = 384 (an odd number of int4
+    # stages, unsplit: the weight scales of two stages are loaded together);
+    # N with a partial 192-column tile
     rng = np.random.default_rng(K + N + M)
     x = S.activations(M, K, 3, rng)
     lay = prepared(x, S.weight(N, K, 0.02, rng, spike_rank=2), S.bias(N, rng), precision, rank, smooth="calibrated")
