@@ -690,8 +690,8 @@ def main():
     value = ops / (r4["ms"] * 1e-3) / 1e12
     k2_tops = ops / (r4["k2_ms"] * 1e-3) / 1e12
     # the int4 product runs on fp8 matrix instructions (the codes are exact
-    # E4M3 values, one group of 64 per instruction) with the bf16 group scales
-    # applied on the vector ALU, so its peak is the dense fp8 one
+    # E4M3 values, one group of 64 per instruction), with the bf16 group
+    # scales applied per group, so its peak is the dense fp8 one
     roofline = {"kernel": "gemm_w4a4_lora_up<int4>", "bound": "mfma", "achieved": round(k2_tops, 2),
                 "peak": PEAK["fp8"], "unit": "TFLOP/s", "frac": round(k2_tops / PEAK["fp8"], 4),
                 "traffic": measured_traffic("gemm_w4a4_lora_up", "int4_4096x3072x3072_r32"),

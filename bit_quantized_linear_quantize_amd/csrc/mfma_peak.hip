@@ -80,7 +80,7 @@ __global__ __launch_bounds__(512) void mfma_f16_peak_switching_kernel(int64_t it
   sink[t] = s;
 }
 
-// The inner loop of the other datapath for int4 x int4 group products: the
+// An earlier form of the int4 x int4 group products' inner loop: the
 // codes (|q| <= 7) are exact fp8 E4M3 or fp6 E2M3 operands, one
 // 32x32x64 f8f6f4 product gives a group's integer sum P (64 = the group
 // size), and the bf16 group scales, which these instructions cannot take
