@@ -138,15 +138,18 @@ size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
 
 // Split K for the plain linear: when the 256 x 192 tiles would occupy less
 // than half of the 256 compute units, each tile's stages (128 values of K for
-// int4, 64 for nvfp4) are shared by up to 8 workgroups (at least 2 stages
-// each where there are enough) that write fp32 partials, summed in a fixed
-// order by a second kernel.
+// int4, 64 for nvfp4) are shared by up to 8 workgroups that write fp32
+// partials, summed in a fixed order by a second kernel.  A split takes about
+// five stages or more (at least 2 splits where there are 4 stages): fewer
+// stages per workgroup leave its fixed cost and the partials' traffic
+// unamortized (measured at M = 128..512, K = 1152..6144, N = 3072).
 int choose_ksplit(int64_t M, int64_t N, int64_t K, int precision) {
   const int64_t tiles = ((M + 255) / 256) * ((N + 191) / 192);
   const int nst = int(K / (precision == SVDQ_INT4 ? 128 : 64));
   if (tiles >= 128) return 1;
   int s = int(std::min<int64_t>(8, 256 / tiles));
   s = std::min(s, nst / 2);
+  s = std::min(s, std::max(2, nst / 5));
   s = std::max(s, 1);
   while (s > 1 && ((nst + s - 1) / s) * (s - 1) >= nst) --s;  // every split gets stages
   return s;

@@ -129,7 +129,7 @@ int svdq_w4a4_gemm(const void* workspace, size_t workspace_bytes, int64_t M, int
  *     exceeds SVDQ_NOALLOC_SCRATCH_BYTES returns SVDQ_EWORKSPACE and writes
  *     nothing; with K = 3072 that is M up to about 10400 tokens for int4
  *     rank 32 (M = 4096 needs 25.7 MB; M = 512, whose product is split along
- *     K, 53.5 MB).
+ *     K, 26.9 MB).
  *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
  *     time on one GPU (different streams, or host threads) race and give
  *     undefined results; calls on one stream are ordered and safe.  No part

@@ -151,14 +151,17 @@ def test_split_rule():
     assert ksplit(4096, 3072, 3072) == 1          # 256 tiles
     assert ksplit(512, 3072, 3072) == 8           # 32 tiles
     assert ksplit(1024, 3072, 3072) == 4          # 64 tiles
-    assert ksplit(300, 320, 512) == 4             # 4 tiles, 8 stages
+    assert ksplit(300, 320, 512) == 2             # 4 tiles, 8 stages: at most max(2, 8 // 5) splits
     assert ksplit(64, 64, 128) == 1               # 2 stages
-    assert ksplit(64, 64, 576) == 3               # 9 stages: 4 splits of 3 would leave one empty
+    assert ksplit(64, 64, 576) == 2               # 9 stages
+    assert ksplit(64, 64, 1152) == 3              # 18 stages
+    assert ksplit(256, 3072, 960) == 3            # 15 stages: 15 // 5 = 3 splits of 5
     # int4 stages are 128 values of K
-    assert ksplit(512, 3072, 3072, "int4") == 8   # 24 stages
+    assert ksplit(512, 3072, 3072, "int4") == 4   # 24 stages: about five per split
+    assert ksplit(512, 3072, 6144, "int4") == 8   # 48 stages
     assert ksplit(300, 320, 512, "int4") == 2     # 4 stages
     assert ksplit(64, 64, 256, "int4") == 1       # 2 stages
-    assert ksplit(64, 64, 1152, "int4") == 3      # 9 stages
+    assert ksplit(64, 64, 1152, "int4") == 2      # 9 stages
 
 
 def test_workspace_size(L):

@@ -28,7 +28,7 @@ def bits(t):
 
 def test_noalloc_matches_linear_on_consecutive_calls():
     # largest first: config 1 (25.7 MB of scratch), then one GPU's token
-    # share of it (M = 512: the product split along K, 53.5 MB), then a
+    # share of it (M = 512: the product split along K, 26.9 MB), then a
     # small ragged call; each must equal the workspace entry point bit for bit
     cases = [(4096, 3072, 3072, "int4", 32), (512, 3072, 3072, "int4", 32), (300, 512, 320, "nvfp4", 16),
              (37, 256, 192, "int4", 0)]
