@@ -136,8 +136,8 @@ size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
   return b + round_up(size_t(M) * size_t(rank) * 4);
 }
 
-// Split K for the plain linear: when the 256 x 192 tiles would occupy less
-// than half of the 256 compute units, each tile's stages (128 values of K for
+// Split K for the plain linear: when the 256 x 192 tiles would occupy at
+// most half of the 256 compute units, each tile's stages (128 values of K for
 // int4, 64 for nvfp4) are shared by up to 8 workgroups that write fp32
 // partials, summed in a fixed order by a second kernel.  A split takes about
 // five stages or more (at least 2 splits where there are 4 stages): fewer
@@ -146,7 +146,7 @@ size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
 int choose_ksplit(int64_t M, int64_t N, int64_t K, int precision) {
   const int64_t tiles = ((M + 255) / 256) * ((N + 191) / 192);
   const int nst = int(K / (precision == SVDQ_INT4 ? 128 : 64));
-  if (tiles >= 128) return 1;
+  if (tiles > 128) return 1;
   int s = int(std::min<int64_t>(8, 256 / tiles));
   s = std::min(s, nst / 2);
   s = std::min(s, std::max(2, nst / 5));

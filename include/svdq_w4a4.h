@@ -57,7 +57,7 @@ enum svdq_status {
  * followed by the fp32 group scales [M, K/64]; nvfp4: the dequantized
  * activations e2m1 * dec(s8) as fp16, which is exact); the low-rank
  * activations fp32 [M, rank]; and,
- * when the 256 x 192 output tiles would fill less than half of the GPU, the
+ * when the 256 x 192 output tiles would fill at most half of the GPU, the
  * fp32 partial sums [ksplit, M, N] of the product split along K (ksplit <= 8,
  * a function of M, N and K; the splits are added in a fixed order).
  * Returns 0 for arguments svdq_w4a4_linear would reject. */

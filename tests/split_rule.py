@@ -3,13 +3,13 @@ the workspace layout it implies), restated for the tests."""
 
 
 def ksplit(M, N, K, precision="nvfp4"):
-    """Split only when the 256 x 192 output tiles fill less than half of 256
+    """Split only when the 256 x 192 output tiles fill at most half of 256
     compute units; up to 8 splits of at least 2 stages (128 values of K for
     int4, 64 for nvfp4) and at most max(2, stages // 5) splits, every split
     non-empty."""
     tiles = -(-M // 256) * -(-N // 192)
     nst = K // (128 if precision in ("int4", 0) else 64)
-    if tiles >= 128:
+    if tiles > 128:
         return 1
     s = max(min(8, 256 // tiles, nst // 2, max(2, nst // 5)), 1)
     while s > 1 and -(-nst // s) * (s - 1) >= nst:

@@ -149,6 +149,8 @@ def test_wtscale_rules(L):
 
 def test_split_rule():
     assert ksplit(4096, 3072, 3072) == 1          # 256 tiles
+    assert ksplit(2048, 3072, 3072) == 2          # 128 tiles: half the compute units
+    assert ksplit(2048, 3264, 3072) == 1          # 136 tiles
     assert ksplit(512, 3072, 3072) == 8           # 32 tiles
     assert ksplit(1024, 3072, 3072) == 4          # 64 tiles
     assert ksplit(300, 320, 512) == 2             # 4 tiles, 8 stages: at most max(2, 8 // 5) splits
