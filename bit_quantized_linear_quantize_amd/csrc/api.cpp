@@ -125,15 +125,31 @@ size_t w_scale_bytes(int64_t N, int64_t K, int precision) {
   return precision == SVDQ_INT4 ? size_t(N) * size_t(K / 64) * 2 : size_t(N) * size_t(K / 16);
 }
 
+// Kernel 1 of the linear splits K over S workgroups per 16 rows (S = 1, 2,
+// 4 or 8, dividing the K/64 chunks) while the row blocks alone would leave
+// more than half of the 256 compute units idle; its low-rank sums are then
+// S fp32 partials, added in order by a second kernel.
+int k1_slices(int64_t M, int64_t K) {
+  const int64_t blocks = (M + 15) / 16;
+  const int64_t chunks = K / 64;
+  int s = 1;
+  while (s < 8 && blocks * s * 2 <= 256 && chunks % (s * 2) == 0) s *= 2;
+  return s;
+}
+
 // Base workspace of one layer (each part 256-byte aligned):
 //   act_op     the product operand [M, K]: int4 codes as fp8 E4M3 bytes,
 //              nvfp4 the dequantized values as fp16
 //   act_scale  int4 only: f32 [M, K/64], the group scales
 //   lora_act   f32 [M, rank]
+//   lora_part  f32 [S, M, rank] when kernel 1 splits K (S = k1_slices > 1)
 size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
   size_t b = round_up(size_t(M) * size_t(K) * (precision == SVDQ_INT4 ? 1 : 2));
   if (precision == SVDQ_INT4) b += round_up(size_t(M) * size_t(K / 64) * 4);
-  return b + round_up(size_t(M) * size_t(rank) * 4);
+  b += round_up(size_t(M) * size_t(rank) * 4);
+  const int S = k1_slices(M, K);
+  if (S > 1) b += round_up(size_t(S) * size_t(M) * size_t(rank) * 4);
+  return b;
 }
 
 // Split K for the plain linear: when the 256 x 192 tiles would occupy at
@@ -238,9 +254,10 @@ struct Carve {
   uint8_t* act_op;    // int4: E4M3 bytes [M, K]; nvfp4: f16 [M, K]
   float* act_scale;   // int4: f32 [M, K/64]; else null
   float* lora_act;    // f32 [M, rank]
+  float* lora_part;   // f32 [k1_slices, M, rank] (when kernel 1 splits K)
 };
 
-Carve carve(void* workspace, int64_t M, int64_t K, int precision) {
+Carve carve(void* workspace, int64_t M, int64_t K, int precision, int rank) {
   uint8_t* p = static_cast<uint8_t*>(workspace);
   Carve c{};
   c.act_op = p;
@@ -250,23 +267,30 @@ Carve carve(void* workspace, int64_t M, int64_t K, int precision) {
     p += round_up(size_t(M) * size_t(K / 64) * 4);
   }
   c.lora_act = reinterpret_cast<float*>(p);
+  c.lora_part = c.lora_act + round_up(size_t(M) * size_t(rank) * 4) / 4;
   return c;
 }
 
 // Kernel 1 into the workspace.
 int launch_quantize(const void* x, int64_t M, int64_t K, const void* smooth, const void* lora_down,
                     int precision, int rank, void* workspace, hipStream_t s) {
-  const Carve c = carve(workspace, M, K, precision);
+  const Carve c = carve(workspace, M, K, precision, rank);
   svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, c.lora_act, c.act_op, c.act_scale,
                         M, K, precision, rank};
-  return launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
+  qa.k_slices = k1_slices(M, K);
+  qa.lora_part = c.lora_part;
+  int rc = launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");
+  if (rc || qa.k_slices == 1 || rank == 0) return rc;
+  // the slices' low-rank partials, added in slice order
+  return launch_status(svdq::launch_tile_partial_sum(c.lora_part, qa.k_slices, M * rank, c.lora_act, s),
+                       "low-rank slice sum launch");
 }
 
 // Kernel 2 (plain store) from a linear workspace (linear_workspace_bytes).
 int launch_gemm(const void* workspace, int64_t M, int64_t K, int64_t N, const void* packed_w,
                 const void* wscales, float wtscale, const void* lora_up, const void* bias, int precision,
                 int rank, void* out, hipStream_t s) {
-  const Carve c = carve(const_cast<void*>(workspace), M, K, precision);
+  const Carve c = carve(const_cast<void*>(workspace), M, K, precision, rank);
   svdq::GemmArgs ga{c.act_op, c.act_scale, c.lora_act, packed_w, wscales, lora_up, bias, out, nullptr,
                     wtscale, M, K, N, precision, rank};
   ga.ksplit = choose_ksplit(M, N, K, precision);
@@ -916,9 +940,9 @@ int svdq_w4a4_mlp_gelu(const void* x, int64_t M, const svdq_w4a4_layer* up, cons
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t H = up->N;
-  const Carve cu = carve(workspace, M, up->K, up->precision);
+  const Carve cu = carve(workspace, M, up->K, up->precision, up->rank);
   void* ws_down = static_cast<uint8_t*>(workspace) + workspace_bytes(M, up->K, up->precision, up->rank);
-  const Carve cd = carve(ws_down, M, H, SVDQ_NVFP4);
+  const Carve cd = carve(ws_down, M, H, SVDQ_NVFP4, down->rank);
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws_down) +
                                         linear_workspace_bytes(M, H, down->N, SVDQ_NVFP4, down->rank));
   // up layer: kernel 1 into the first part of the workspace
@@ -968,7 +992,7 @@ int svdq_w4a4_qkv_rmsnorm_rope(const void* x, int64_t M, const svdq_w4a4_layer* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   rc = launch_quantize(x, M, qkv->K, qkv->smooth, qkv->lora_down, qkv->precision, qkv->rank, workspace, s);
   if (rc) return rc;
-  const Carve c = carve(workspace, M, qkv->K, qkv->precision);
+  const Carve c = carve(workspace, M, qkv->K, qkv->precision, qkv->rank);
   svdq::GemmArgs ga{c.act_op, c.act_scale, c.lora_act, qkv->packed_w, qkv->wscales, qkv->lora_up, qkv->bias,
                     out, nullptr, qkv->wtscale, M, qkv->K, qkv->N, qkv->precision, qkv->rank};
   ga.q_norm = q_norm;

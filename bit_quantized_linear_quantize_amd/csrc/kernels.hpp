@@ -20,6 +20,11 @@ struct QuantActArgs {
   float* act_scale;       // linear int4 only: f32 [M, K/64] group scales s
   int64_t M, K;
   int precision, rank;
+  // linear only: K slices (1: one workgroup per 16 rows and all of K; S > 1:
+  // S workgroups per 16 rows, each a K/S slice, the low-rank sums written as
+  // fp32 partials lora_part [S, M, rank] for a second kernel to add in order)
+  int k_slices = 1;
+  float* lora_part = nullptr;
 };
 
 // The product operand of the linear.  int4: the codes q (|q| <= 7) as fp8

@@ -49,10 +49,15 @@ struct K1Shape {
   static constexpr int prefetch = 2;
 };
 
+// K slices (the linear, few rows): workgroup b takes row block b / S and the
+// chunks [c0, c0 + C) of K slice b % S (C = K/64 / S), with one wave per
+// chunk up to the usual count; its low-rank sums are one fp32 partial
+// lora_part[slice, M, rank] (the slices are added in order afterwards).
+// With S = 1 it is the kernel above.  The wave count is the launch's.
 template <int PREC, int RB, bool LINEAR>
 __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_down_kernel(QuantActArgs args) {
-  constexpr int kK1Waves = K1Shape<RB>::waves;
-  constexpr int kK1Threads = 64 * kK1Waves;
+  const int kK1Waves = (int)(blockDim.x >> 6);
+  const int kK1Threads = (int)blockDim.x;
   extern __shared__ float lds[];
   constexpr int PF = K1Shape<RB>::prefetch;
   constexpr int NB = RB > 0 ? RB : 1;
@@ -67,14 +72,18 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
 
   const int r = lane & 15;
   const int q = lane >> 4;
-  const int row = blockIdx.x * kK1Rows + r;
+  const int S = LINEAR ? args.k_slices : 1;
+  const int slice = (int)blockIdx.x % S;
+  const int row = ((int)blockIdx.x / S) * kK1Rows + r;
   const bool row_ok = row < M;
   const uint16_t* xr = x + (size_t)(row_ok ? row : M - 1) * K;
-  const int nchunks = K >> 6;
+  const int nchunks = (K >> 6) / S;   // chunks of this slice
+  const int c0 = slice * nchunks;     // its first chunk
+  const int kb = c0 * 64;             // its first column
 
   // X_hat of the lane's 16 columns k0 .. k0+15
   auto smooth16 = [&](const u32x4* xb, int k0, float* xh) {
-    const f32x4* mu4 = (const f32x4*)(lds + k0);
+    const f32x4* mu4 = (const f32x4*)(lds + (k0 - kb));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
 
   auto issue = [&](int slot, int c) {
     if (c < nchunks) {
-      const int k0 = c * 64 + q * 16;
+      const int k0 = (c0 + c) * 64 + q * 16;
       xbuf[slot][0] = *(const u32x4*)(xr + k0);
       xbuf[slot][1] = *(const u32x4*)(xr + k0 + 8);
       if constexpr (RB > 0) {
@@ -157,16 +166,17 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, wave + p * kK1Waves);
 
-  // 1 / smooth for every input channel (IEEE division, one per channel),
-  // computed while the first chunks are in flight
-  for (int k = tid; k < K; k += kK1Threads) lds[k] = __fdiv_rn(1.0f, bf16_bits_to_f32(smooth[k]));
+  // 1 / smooth for every input channel of the slice (IEEE division, one per
+  // channel), computed while the first chunks are in flight
+  for (int k = tid; k < nchunks * 64; k += kK1Threads) lds[k] = __fdiv_rn(1.0f, bf16_bits_to_f32(smooth[kb + k]));
   __syncthreads();
 
   for (int base = wave; base < nchunks; base += PF * kK1Waves) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int c = base + p * kK1Waves;
-      if (c < nchunks) {
+      const int cl = base + p * kK1Waves;  // chunk of the slice
+      const int c = c0 + cl;               // chunk of K
+      if (cl < nchunks) {
         const int k0 = c * 64 + q * 16;
         float xh[16];
         smooth16(xbuf[p], k0, xh);
@@ -229,7 +239,7 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
             }
           }
         }
-        issue(p, c + PF * kK1Waves);
+        issue(p, cl + PF * kK1Waves);
       }
     }
   }
@@ -244,14 +254,15 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
 #pragma unroll
       for (int j = 0; j < 4; ++j) red[(wave * kK1Rows + q * 4 + j) * rank + b * 16 + r] = acc[b][j];
     __syncthreads();
+    // (one slice: lora_act itself; else this slice's partial)
+    float* out = S > 1 ? args.lora_part + (size_t)slice * M * rank : args.lora_act;
     for (int o = tid; o < kK1Rows * rank; o += kK1Threads) {
       const int rr = o / rank;
       const int cc = o - rr * rank;
       float s = 0.f;
-#pragma unroll
       for (int w = 0; w < kK1Waves; ++w) s += red[(w * kK1Rows + rr) * rank + cc];
-      const int grow = blockIdx.x * kK1Rows + rr;
-      if (grow < M) args.lora_act[(size_t)grow * rank + cc] = s;
+      const int grow = ((int)blockIdx.x / S) * kK1Rows + rr;
+      if (grow < M) out[(size_t)grow * rank + cc] = s;
     }
   }
 }
@@ -259,11 +270,13 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
 template <int PREC, int RB, bool LINEAR>
 static hipError_t launch_k1(const QuantActArgs& a, hipStream_t stream) {
   const int rank = RB * 16;
-  constexpr int waves = K1Shape<RB>::waves;
-  size_t lds = (size_t)a.K * sizeof(float);
+  const int S = LINEAR ? a.k_slices : 1;
+  const int chunks = (int)(a.K >> 6) / S;  // per slice
+  const int waves = chunks < K1Shape<RB>::waves ? chunks : K1Shape<RB>::waves;
+  size_t lds = (size_t)chunks * 64 * sizeof(float);
   const size_t red = (size_t)waves * kK1Rows * rank * sizeof(float);
   if (red > lds) lds = red;
-  const unsigned blocks = (unsigned)((a.M + kK1Rows - 1) / kK1Rows);
+  const unsigned blocks = (unsigned)((a.M + kK1Rows - 1) / kK1Rows) * (unsigned)S;
   hipLaunchKernelGGL((quantize_act_lora_down_kernel<PREC, RB, LINEAR>), dim3(blocks), dim3(64 * waves), lds,
                      stream, a);
   return hipGetLastError();
@@ -287,6 +300,8 @@ static hipError_t dispatch_rank(const QuantActArgs& a, hipStream_t s) {
 
 hipError_t launch_quantize_act(const QuantActArgs& a, hipStream_t stream) {
   const bool linear = a.act_op != nullptr;
+  if (a.k_slices < 1 || (a.K >> 6) % a.k_slices || (a.k_slices > 1 && (!linear || (a.rank > 0 && !a.lora_part))))
+    return hipErrorInvalidValue;
   if (a.precision == kInt4)
     return linear ? dispatch_rank<kInt4, true>(a, stream) : dispatch_rank<kInt4, false>(a, stream);
   return linear ? dispatch_rank<kNvfp4, true>(a, stream) : dispatch_rank<kNvfp4, false>(a, stream);

@@ -56,7 +56,9 @@ enum svdq_status {
  * operand of the product kernel [M, K] (int4: the codes as fp8 E4M3 bytes,
  * followed by the fp32 group scales [M, K/64]; nvfp4: the dequantized
  * activations e2m1 * dec(s8) as fp16, which is exact); the low-rank
- * activations fp32 [M, rank]; and,
+ * activations fp32 [M, rank]; when the 16-row blocks of x would fill at
+ * most half of the GPU, the first kernel's low-rank partials fp32 [S, M,
+ * rank] of S = 2, 4 or 8 slices of K (added in slice order); and,
  * when the 256 x 192 output tiles would fill at most half of the GPU, the
  * fp32 partial sums [ksplit, M, N] of the product split along K (ksplit <= 8,
  * a function of M, N and K; the splits are added in a fixed order).

@@ -20,3 +20,19 @@ def ksplit(M, N, K, precision="nvfp4"):
 def split_bytes(M, N, K, precision="nvfp4"):
     s = ksplit(M, N, K, precision)
     return 0 if s == 1 else (s * M * N * 4 + 255) // 256 * 256
+
+
+def k1_slices(M, K):
+    """Kernel 1 of the linear splits K over S workgroups per 16 rows (1, 2, 4
+    or 8, dividing the K/64 chunks) while the row blocks alone would leave
+    more than half of 256 compute units idle."""
+    blocks, chunks, s = -(-M // 16), K // 64, 1
+    while s < 8 and blocks * s * 2 <= 256 and chunks % (s * 2) == 0:
+        s *= 2
+    return s
+
+
+def lora_part_bytes(M, K, rank):
+    """The workspace part holding kernel 1's low-rank slice partials."""
+    s = k1_slices(M, K)
+    return 0 if s == 1 else (s * M * rank * 4 + 255) // 256 * 256

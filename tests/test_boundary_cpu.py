@@ -11,7 +11,7 @@ import re
 import pytest
 
 import bit_quantized_linear_quantize_amd as bq
-from split_rule import ksplit, split_bytes
+from split_rule import k1_slices, ksplit, lora_part_bytes, split_bytes
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "svdq_w4a4.h")
@@ -170,10 +170,14 @@ def test_workspace_size(L):
     M, K, N = 300, 512, 320
     rnd = lambda v: (v + 255) // 256 * 256
     # the product operand (int4: fp8 codes [M, K] and fp32 group scales
-    # [M, K/64]; nvfp4: fp16 [M, K]); then lora_act fp32 [M, 32]; then the
-    # split-K partials fp32 [ksplit, M, N]
-    want = {0: rnd(M * K) + rnd(4 * M * (K // 64)) + rnd(M * 32 * 4) + split_bytes(M, N, K, "int4"),
-            1: rnd(2 * M * K) + rnd(M * 32 * 4) + split_bytes(M, N, K)}
+    # [M, K/64]; nvfp4: fp16 [M, K]); then lora_act fp32 [M, 32]; then, with
+    # kernel 1 split along K, its low-rank slice partials fp32 [S, M, 32];
+    # then the split-K partials fp32 [ksplit, M, N]
+    assert k1_slices(M, K) == 8 and k1_slices(4096, 3072) == 1 and k1_slices(2048, 3072) == 2
+    assert k1_slices(512, 3072) == 8 and k1_slices(64, 384) == 2 and k1_slices(1, 128) == 2
+    want = {0: rnd(M * K) + rnd(4 * M * (K // 64)) + rnd(M * 32 * 4) + lora_part_bytes(M, K, 32) +
+            split_bytes(M, N, K, "int4"),
+            1: rnd(2 * M * K) + rnd(M * 32 * 4) + lora_part_bytes(M, K, 32) + split_bytes(M, N, K)}
     assert split_bytes(M, N, K) > 0 and split_bytes(M, N, K, "int4") > 0
     assert L.svdq_w4a4_workspace_bytes(4096, 3072, 3072, 1, 16, 32) == rnd(2 * 4096 * 3072) + rnd(4096 * 32 * 4)
     for prec, g in ((0, 64), (1, 16)):
@@ -262,8 +266,8 @@ def test_mlp_rules(L):
     # the up layer's operand (int4: fp8 codes and fp32 group scales) and
     # lora_act, the down layer's linear workspace, then the down layer's
     # low-rank partials per 192-column tile of the up projection
-    assert need == (rnd(M * K) + rnd(4 * M * (K // 64)) + rnd(4 * M * 32)) + (rnd(2 * M * H) + rnd(4 * M * 32) +
-                                                                      split_bytes(M, N, H)) + \
+    assert need == (rnd(M * K) + rnd(4 * M * (K // 64)) + rnd(4 * M * 32) + lora_part_bytes(M, K, 32)) + \
+        (rnd(2 * M * H) + rnd(4 * M * 32) + lora_part_bytes(M, H, 32) + split_bytes(M, N, H)) + \
         rnd(4 * ((H + 191) // 192) * M * 32)
 
     def call(x=x, M=M, up=up, down=down, out=out, ws=ws, wsb=need, arch=GFX950):
@@ -294,8 +298,9 @@ def test_qkv_rules(L):
     qn, kn, cs, sn = 0x6_0000_0000, 0x6_0001_0000, 0x7_0000_0000, 0x8_0000_0000
     qkv = _layer(0x1_0000_0000, K, N, precision=1)
     B = ctypes.byref
-    # the linear's activations and lora_act (no split partials: the epilogue is not split)
-    need = (2 * M * K + 255) // 256 * 256 + (M * 32 * 4 + 255) // 256 * 256
+    # the linear's activations, lora_act and kernel 1's low-rank slice
+    # partials (no split partials: the epilogue is not split)
+    need = (2 * M * K + 255) // 256 * 256 + (M * 32 * 4 + 255) // 256 * 256 + lora_part_bytes(M, K, 32)
 
     def call(x=x, M=M, qkv=qkv, heads=H, hd=128, qn=qn, kn=kn, eps=1e-6, cs=cs, sn=sn, out=out, ws=ws,
              wsb=need, arch=GFX950):

@@ -414,6 +414,50 @@ def test_two_phase_entry_matches_linear(ragged, precision):
     assert np.array_equal(host_bits(y1), host_bits(y2))
 
 
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+@pytest.mark.parametrize("M,K,rank", [(300, 512, 32), (37, 3072, 16), (4096, 3072, 32), (64, 384, 32),
+                                      (70, 512, 48), (17, 16384, 32), (2048, 3072, 32), (5, 256, 0)])
+def test_linear_kernel1_workspace(precision, M, K, rank):
+    """Kernel 1 as the linear launches it (split along K for few rows: the
+    low-rank slice partials added in order by a second kernel) against the
+    operand export and the oracle: operand and group scales in the workspace
+    bit for bit equal to the export's, lora_act within 1e-4 of the oracle's
+    largest low-rank activation."""
+    rng = np.random.default_rng(M + K + rank)
+    x = S.activations(M, K, max(1, K // 100), rng)
+    lay = act_layer(L.smooth_factors(x, S.weight(64, K, 0.02, rng, spike_rank=0)), rank, precision, rng)
+    ref = L.svdq_quantize_act(x, lay["smooth"], lay["lora_down"], precision)
+    xd, smd = dev_bf16(x), dev_bf16(lay["smooth"])
+    ldd = dev_bf16(lay["lora_down"]) if rank else None
+    op, sc, _ = bq.svdq_w4a4_quantize_operand(xd, smd, ldd, precision)
+    G = 64 if precision == "int4" else 16
+    layer = bq.SVDQLinear(torch.zeros((64, K // 2), dtype=torch.uint8, device="cuda"),
+                          torch.zeros((64, K // G), dtype=torch.bfloat16 if precision == "int4" else torch.uint8,
+                                      device="cuda"),
+                          smd, ldd, torch.zeros((64, rank), dtype=torch.bfloat16, device="cuda") if rank else None,
+                          None, precision, wtscale=1.0)
+    ws = torch.empty(layer.workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)
+    bq.svdq_w4a4_quantize(xd, layer, ws)
+    torch.cuda.synchronize()
+    rnd = lambda v: (v + 255) // 256 * 256
+    w = ws.cpu().numpy()
+    opb = M * K * (1 if precision == "int4" else 2)
+    assert np.array_equal(w[:opb], op.cpu().numpy().view(np.uint8).reshape(-1)), "operand differs from the export"
+    off = rnd(opb)
+    if precision == "int4":
+        scb = M * (K // 64) * 4
+        assert np.array_equal(w[off:off + scb], sc.cpu().numpy().view(np.uint8).reshape(-1)), "group scales differ"
+        off += rnd(scb)
+    if rank:
+        la = w[off:off + M * rank * 4].view(np.float32).reshape(M, rank).astype(np.float64)
+        err = np.abs(la - ref["lora_act"]).max()
+        tol = 1e-4 * np.abs(ref["lora_act"]).max() + 1e-6
+        print(f"[kernel 1 workspace {precision} M={M} K={K} r{rank}] lora_act max err {err:.3e} (tol {tol:.3e})",
+              flush=True)
+        assert err <= tol
+
+
 # ------------------------------------------------------------------ AWQ
 def run_awq(x_bits, lay):
     layer = bq.AWQLinear.from_numpy(lay)
