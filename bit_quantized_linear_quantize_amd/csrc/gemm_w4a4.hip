@@ -142,10 +142,12 @@ __device__ __forceinline__ u32x4 int4x16_to_fp8(u32x2 w) {
 
 // One stage of raw W data of the int4 fp8 path in registers: piece j = 8
 // bytes of codes (columns 16 c .. 16 c + 15 of the stage, c = tid % 8) of
-// tile row tid/8 + 64 j, and the bf16 scales of the stage's two groups.
+// tile row tid/8 + 64 j, and (even stages only) the bf16 scales of two
+// stages' groups.
 struct RawStage8 {
   u32x2 w[kWP];
   uint32_t sw;  // the two bf16 group scales of W row srow (24 rows per wave)
+                // of this stage (lanes 0-23, 48-63) or of the next (24-47)
 };
 
 // The operands of one 16-wide rank slice of the low-rank up projection, as
@@ -514,8 +516,9 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   __shared__ __attribute__((aligned(16))) float asc0[kFp8 ? 2 * kBM : 1];
   __shared__ __attribute__((aligned(16))) float asc1[kFp8 ? 2 * kBM : 1];
   __shared__ __attribute__((aligned(16))) float asc2[kFp8 ? 2 * kBM : 1];
-  // (W: bf16 bits of s_w / 2, the operand of the scale-product instruction)
-  __shared__ __attribute__((aligned(16))) uint16_t wsc[kFp8 ? 2 * 2 * kBN : 1];
+  // (W: bf16 bits of s_w / 2, the operand of the scale-product instruction,
+  // [stage % 3][group][row])
+  __shared__ __attribute__((aligned(16))) uint16_t wsc[kFp8 ? 3 * 2 * kBN : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -647,9 +650,14 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       w_off[j] = wrow * K2 + lc * 8;
     }
     // W scales: wave w loads those of tile rows 24 w .. 24 w + 23, one row
-    // per lane (lanes 24-63 repeat rows), one load per wave and stage
+    // per lane, one load per wave and pair of stages (even s): lanes 0-23
+    // stage s, lanes 24-47 stage s + 1, lanes 48-63 repeat lanes 0-15.  (At
+    // an odd stage count the last pair's second half lies past the last
+    // stage: the next row's scales, never used, or beyond the descriptor,
+    // zero.)
     const int srow = wave * (kBN / kWaves) + lane % (kBN / kWaves);
-    const int ws_off = (kQk ? pcol(srow) : srow) * G * 2;
+    const int s_next = (lane >= kBN / kWaves && lane < 2 * (kBN / kWaves)) ? 1 : 0;
+    const int ws_off = (kQk ? pcol(srow) : srow) * G * 2 + s_next * 4;
     int dma_off[kADma];
 #pragma unroll
     for (int d = 0; d < kADma; ++d) {
@@ -679,8 +687,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       else return asc2;
     };
     // loads of stage s: A and its scales into A buffer ab (direct to LDS),
-    // then W into r
-    auto group = [&](RawStage8& r, int s, auto ab) {
+    // then W into r (the W scales of stages s and s + 1 if s is even, par 0)
+    auto group = [&](RawStage8& r, int s, auto ab, auto par) {
       const bool live = s < nstages;
       uint8_t* dst = abuf(ab) + wave * (kADma * 64 * 16);
 #pragma unroll
@@ -700,24 +708,28 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
         r.w[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(live ? w_rs : zero_rs, w_off[j],
                                                                                 s * 64, 0));
       }
-      r.sw = __builtin_amdgcn_raw_buffer_load_b32(live ? ws_rs : zero_rs, ws_off, s * 4, 0);
+      if constexpr (decltype(par)::value == 0)
+        r.sw = __builtin_amdgcn_raw_buffer_load_b32(live ? ws_rs : zero_rs, ws_off, s * 4, 0);
     };
-    // staging of W piece p of a raw stage into W buffer Tw (with piece 0, the
-    // wave's W scales into wsc half wb)
-    auto store_part = [&](uint8_t* Tw, int wb, const RawStage8& r, int p) {
+    // staging of W piece p of raw stage st (mod 6) into W buffer Tw (with
+    // piece 0 of an even stage, the wave's W scales of stages st and st + 1
+    // into wsc slots st % 3 and (st + 1) % 3)
+    auto store_part = [&](uint8_t* Tw, auto st, const RawStage8& r, int p) {
+      constexpr int q = decltype(st)::value;
       const int wrow = lr + kRP * p;
       *(u32x4*)(Tw + wrow * kWRow + lc * 16) = int4x16_to_fp8(r.w[p]);
-      if (p == 0) {
+      if (q % 2 == 0 && p == 0) {
         // s_w / 2 as bf16 (exact: a power-of-two step of a normal value);
-        // lanes holding the same row write the same values
-        wsc[(wb * 2 + 0) * kBN + srow] = (uint16_t)(__float_as_uint(__fmul_rn(bf16_lo(r.sw), 0.5f)) >> 16);
-        wsc[(wb * 2 + 1) * kBN + srow] = (uint16_t)(__float_as_uint(__fmul_rn(bf16_hi(r.sw), 0.5f)) >> 16);
+        // lanes holding the same row and stage write the same values
+        uint16_t* d = wsc + (q % 3) * 2 * kBN + srow + (q % 3 == 2 ? -2 : 1) * (s_next * 2 * kBN);
+        d[0] = (uint16_t)(__float_as_uint(__fmul_rn(bf16_lo(r.sw), 0.5f)) >> 16);
+        d[kBN] = (uint16_t)(__float_as_uint(__fmul_rn(bf16_hi(r.sw), 0.5f)) >> 16);
       }
     };
     // one stage: per group, per 32 x 32 tile one product of 64 values of K
     auto compute = [&](auto P, int s, RawStage8& r) {
       constexpr int p = decltype(P)::value;
-      constexpr int ab = p % kAStages, wb = p % 2;
+      constexpr int ab = p % kAStages;
       const uint8_t* Ta = abuf(IC<p>{});
       const uint8_t* Tw = wbuf(IC<p>{});
       uint8_t* Nw = wbuf(IC<p + 1>{});
@@ -745,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
           const uint8_t* src = Tw + col * kWRow + 64 * gi + 32 * h;
           const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
           bop[j] = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-          bs16[j] = wsc[(wb * 2 + gi) * kBN + col];
+          bs16[j] = wsc[((p % 3) * 2 + gi) * kBN + col];
         }
 #pragma unroll
         for (int i = 0; i < kIB; ++i) {
@@ -760,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
             for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmaf_rn(pr[e], sc[e], acc[i][j][e]);
           }
           // stage a third of the next W stage among the products
-          if (gi * kIB + i < 3) store_part(Nw, (p + 1) % 2, r, gi * kIB + i);
+          if (gi * kIB + i < 3) store_part(Nw, IC<(p + 1) % 6>{}, r, gi * kIB + i);
           // order of a tile row's instructions: the products of two blocks,
           // the scaling of the first, the third block's products, the rest
           // (62.5 us against 63.5 us in the compiler's own order at M = 4096,
@@ -772,7 +784,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
         }
       }
       stage_barrier();
-      group(r, s + 3, IC<p>{});
+      group(r, s + 3, IC<p>{}, IC<(p + 3) % 2>{});
     };
 
     // Prologue.  The bias (except for split-K partials) and, for ranks up to
@@ -799,8 +811,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     }
     __builtin_amdgcn_sched_barrier(0);
     RawStage8 r0, r1;
-    group(r0, 0, IC<0>{});
-    group(r1, 1, IC<1>{});
+    group(r0, 0, IC<0>{}, IC<0>{});
+    group(r1, 1, IC<1>{}, IC<1>{});
     if constexpr (!kSplit) {
 #pragma unroll
       for (int i = 0; i < kIB; ++i)
@@ -818,8 +830,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       lowrank_up();
     }
 #pragma unroll
-    for (int q = 0; q < 3; ++q) store_part(lds_w0, 0, r0, q);
-    group(r0, 2, IC<2>{});
+    for (int q = 0; q < 3; ++q) store_part(lds_w0, IC<0>{}, r0, q);
+    group(r0, 2, IC<2>{}, IC<0>{});
     stage_barrier();  // (each wave has its stage-0 A loads: they precede the W loads it staged)
     for (int s = 0; s < nstages; s += 6) {
       compute(IC<0>{}, s, r1);
