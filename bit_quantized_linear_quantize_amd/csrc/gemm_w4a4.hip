@@ -112,7 +112,9 @@ __device__ __forceinline__ int a_pos(int row, int c) { return c ^ ((row >> 1) & 
 // One stage of raw W (and, for the parity export, A) data in registers.  Every
 // thread has the same role: W piece j = 4 bytes of codes for columns 8c ..
 // 8c+7 (c = tid % 8) of tile row tid/8 + 64 j, and its scale; A piece i
-// likewise for A row tid/8 + 64 i.
+// likewise for A row tid/8 + 64 i.  (nvfp4 linear: pieces 0 and 1 are instead
+// the two halves of one 8-byte load, columns 16c .. 16c+15 (c = tid % 4, one
+// scale block, scale in sw8[0]) of tile row tid/4.)
 struct RawStage {
   uint32_t w[kWP];
   // the scale of each W piece, kept in its loaded width (a widening right
@@ -140,12 +142,14 @@ __device__ __forceinline__ u32x4 int4x16_to_fp8(u32x2 w) {
   return r;
 }
 
-// One stage of raw W data of the int4 fp8 path in registers: piece j = 8
-// bytes of codes (columns 16 c .. 16 c + 15 of the stage, c = tid % 8) of
-// tile row tid/8 + 64 j, and (even stages only) the bf16 scales of two
-// stages' groups.
+// One stage of raw W data of the int4 fp8 path in registers (192 rows x 64
+// bytes in two loads per thread): wa = 16 bytes of codes (columns
+// 32 c .. 32 c + 31 of the stage, c = tid % 4) of tile row tid / 4, wb = 8
+// bytes (columns 16 c .. 16 c + 15, c = tid % 8) of tile row 128 + tid / 8;
+// and (even stages only) the bf16 scales of two stages' groups.
 struct RawStage8 {
-  u32x2 w[kWP];
+  u32x4 wa;
+  u32x2 wb;
   uint32_t sw;  // the two bf16 group scales of W row srow (24 rows per wave)
                 // of this stage (lanes 0-23, 48-63) or of the next (24-47)
 };
@@ -642,13 +646,11 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     const __amdgpu_buffer_rsrc_t ws_rs = make_rsrc((const uint8_t*)args.w_scales + (size_t)w_base * G * 2 + s0 * 4,
                                                    (size_t)(N - w_base) * G * 2 - s0 * 4);
     const __amdgpu_buffer_rsrc_t zero_rs = make_rsrc(args.w_codes, 0);
-    const int lc = tid & 7, lr = tid >> 3;
-    int w_off[kWP];
-#pragma unroll
-    for (int j = 0; j < kWP; ++j) {
-      const int wrow = kQk ? pcol(lr + kRP * j) : lr + kRP * j;  // row from the descriptor base
-      w_off[j] = wrow * K2 + lc * 8;
-    }
+    // W codes: rows 0-127 of the tile 16 bytes per thread, rows 128-191 8
+    // bytes (fewer load instructions per stage than three 8-byte pieces)
+    const int la_r = tid >> 2, la_c = tid & 3, lb_r = 2 * kRP + (tid >> 3), lb_c = tid & 7;
+    const int wa_off = (kQk ? pcol(la_r) : la_r) * K2 + la_c * 16;  // rows from the descriptor base
+    const int wb_off = (kQk ? pcol(lb_r) : lb_r) * K2 + lb_c * 8;
     // W scales: wave w loads those of tile rows 24 w .. 24 w + 23, one row
     // per lane, one load per wave and pair of stages (even s): lanes 0-23
     // stage s, lanes 24-47 stage s + 1, lanes 48-63 repeat lanes 0-15.  (At
@@ -703,21 +705,20 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       // the W loads of the stage stay behind its A loads: a wave that has
       // waited for its W registers has also received its A stage
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < kWP; ++j) {
-        r.w[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(live ? w_rs : zero_rs, w_off[j],
-                                                                                s * 64, 0));
-      }
+      r.wa = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(live ? w_rs : zero_rs, wa_off, s * 64, 0));
+      r.wb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(live ? w_rs : zero_rs, wb_off, s * 64, 0));
       if constexpr (decltype(par)::value == 0)
         r.sw = __builtin_amdgcn_raw_buffer_load_b32(live ? ws_rs : zero_rs, ws_off, s * 4, 0);
     };
-    // staging of W piece p of raw stage st (mod 6) into W buffer Tw (with
-    // piece 0 of an even stage, the wave's W scales of stages st and st + 1
-    // into wsc slots st % 3 and (st + 1) % 3)
+    // staging of third p of raw stage st (mod 6) into W buffer Tw (the two
+    // halves of wa, then wb; with part 0 of an even stage, the wave's W
+    // scales of stages st and st + 1 into wsc slots st % 3 and (st + 1) % 3)
     auto store_part = [&](uint8_t* Tw, auto st, const RawStage8& r, int p) {
       constexpr int q = decltype(st)::value;
-      const int wrow = lr + kRP * p;
-      *(u32x4*)(Tw + wrow * kWRow + lc * 16) = int4x16_to_fp8(r.w[p]);
+      if (p < 2)
+        *(u32x4*)(Tw + la_r * kWRow + la_c * 32 + p * 16) = int4x16_to_fp8(u32x2{r.wa[2 * p], r.wa[2 * p + 1]});
+      else
+        *(u32x4*)(Tw + lb_r * kWRow + lb_c * 16) = int4x16_to_fp8(r.wb);
       if (q % 2 == 0 && p == 0) {
         // s_w / 2 as bf16 (exact: a power-of-two step of a normal value);
         // lanes holding the same row and stage write the same values
@@ -872,6 +873,12 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     w_off[j] = wrow * K2 + lc * 4;
     ws_off[j] = wrow * (int)ws_row_bytes + (PREC == kNvfp4 ? (lc >> 1) : 0);
   }
+  // nvfp4 linear: tile rows 0-127 by one 8-byte load (one scale block) per
+  // thread and stage, rows 128-191 as piece 2 (fewer load instructions)
+  constexpr bool kW8 = PREC == kNvfp4 && !PARTIALS;
+  const int la_r = tid >> 2, la_c = tid & 3;
+  const int wa_row = kQk ? pcol(la_r) : la_r;
+  const int wa_off = wa_row * K2 + la_c * 8, wsa_off = wa_row * (int)ws_row_bytes + la_c;
 #pragma unroll
   for (int i = 0; i < kAP; ++i) pa_off[i] = (lr + kRP * i) * K2 + lc * 4;
   // A (fp16) goes straight from memory to LDS: load d of a wave fills the
@@ -912,10 +919,19 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       // waited for its W registers has also received its A stage
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (kW8) {
+      const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wrs, wa_off, s * 32, 0));
+      r.w[0] = v[0];
+      r.w[1] = v[1];
+      r.sw8[0] = __builtin_amdgcn_raw_buffer_load_b8(srs, wsa_off, s * 4, 0);
+      r.w[2] = __builtin_amdgcn_raw_buffer_load_b32(wrs, w_off[2], s * 32, 0);
+      r.sw8[2] = __builtin_amdgcn_raw_buffer_load_b8(srs, ws_off[2], s * 4, 0);
+    } else {
 #pragma unroll
-    for (int j = 0; j < kWP; ++j) {
-      r.w[j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, w_off[j], s * 32, 0);
-      if constexpr (PREC == kNvfp4 && !PARTIALS) r.sw8[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, ws_off[j], s * 4, 0);
+      for (int j = 0; j < kWP; ++j) {
+        r.w[j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, w_off[j], s * 32, 0);
+        if constexpr (PREC == kNvfp4 && !PARTIALS) r.sw8[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, ws_off[j], s * 4, 0);
+      }
     }
     if constexpr (PARTIALS) {
 #pragma unroll
@@ -938,11 +954,18 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
             PREC == kInt4 ? int4x8_to_f16_scaled(r.a[i], one) : e2m1x8_to_f16_scaled(r.a[i], one);
       }
     }
-    const int wrow = lr + kRP * p;
-    _Float16 sc = (_Float16)(PREC == kInt4 ? 1.0f : 2.0f);
-    if constexpr (!PARTIALS) sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw8[p], 0);  // nvfp4
-    *(f16x8*)(Tw + wrow * kWRow + lc * 16) =
-        PREC == kInt4 ? int4x8_to_f16_scaled(r.w[p], sc) : e2m1x8_to_f16_scaled(r.w[p], sc);
+    if constexpr (kW8) {
+      // pieces 0 and 1: columns 16c .. 16c+7 and 16c+8 .. 16c+15 of row tid/4
+      const _Float16 sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw8[p < 2 ? 0 : 2], 0);
+      uint8_t* dst = p < 2 ? Tw + la_r * kWRow + la_c * 32 + p * 16 : Tw + (lr + 2 * kRP) * kWRow + lc * 16;
+      *(f16x8*)dst = e2m1x8_to_f16_scaled(r.w[p], sc);
+    } else {
+      const int wrow = lr + kRP * p;
+      _Float16 sc = (_Float16)(PREC == kInt4 ? 1.0f : 2.0f);
+      if constexpr (!PARTIALS) sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw8[p], 0);  // nvfp4
+      *(f16x8*)(Tw + wrow * kWRow + lc * 16) =
+          PREC == kInt4 ? int4x8_to_f16_scaled(r.w[p], sc) : e2m1x8_to_f16_scaled(r.w[p], sc);
+    }
   };
 
   // exact integer partials of one group (fp32 holds them exactly)
