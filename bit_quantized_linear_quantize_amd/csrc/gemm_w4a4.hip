@@ -114,9 +114,12 @@ __device__ __forceinline__ int a_pos(int row, int c) { return c ^ ((row >> 1) & 
 // 8c+7 (c = tid % 8) of tile row tid/8 + 64 j, and its scale; A piece i
 // likewise for A row tid/8 + 64 i.  (nvfp4 linear: pieces 0 and 1 are instead
 // the two halves of one 8-byte load, columns 16c .. 16c+15 (c = tid % 4, one
-// scale block, scale in sw8[0]) of tile row tid/4.)
+// scale block) of tile row tid/4; the scales come at even stages only, the
+// four of the stage and the four of the next per row in spa (row tid/4) and
+// spb (row 128 + tid/8).)
 struct RawStage {
   uint32_t w[kWP];
+  u32x2 spa, spb;      // nvfp4 linear
   // the scale of each W piece, kept in its loaded width (a widening right
   // after the load would make the wave wait for the load there)
   uint8_t sw8[kWP];    // nvfp4: E4M3 byte
@@ -878,7 +881,14 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   constexpr bool kW8 = PREC == kNvfp4 && !PARTIALS;
   const int la_r = tid >> 2, la_c = tid & 3;
   const int wa_row = kQk ? pcol(la_r) : la_r;
-  const int wa_off = wa_row * K2 + la_c * 8, wsa_off = wa_row * (int)ws_row_bytes + la_c;
+  const int wa_off = wa_row * K2 + la_c * 8, wsa_off = wa_row * (int)ws_row_bytes;
+  const int wsb_off = (kQk ? pcol(lr + 2 * kRP) : lr + 2 * kRP) * (int)ws_row_bytes;
+  const int sp_b4 = s0 > 0 ? 4 : 0;
+  const __amdgpu_buffer_rsrc_t wsp_rs =
+      make_rsrc((const uint8_t*)args.w_scales + (size_t)w_base * ws_row_bytes + ws_s0 - sp_b4,
+                kW8 ? (size_t)(N - w_base) * ws_row_bytes - ws_s0 + sp_b4 : 0);
+  // (the scale bytes of the odd stage of a pair, taken out at the even one)
+  uint32_t nsc_a = 0, nsc_b = 0;
 #pragma unroll
   for (int i = 0; i < kAP; ++i) pa_off[i] = (lr + kRP * i) * K2 + lc * 4;
   // A (fp16) goes straight from memory to LDS: load d of a wave fills the
@@ -903,8 +913,9 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     else return lds_w1;
   };
 
-  // loads of stage s: A into A buffer ab (direct to LDS), W into r
-  auto group = [&](RawStage& r, int s, auto ab) {
+  // loads of stage s: A into A buffer ab (direct to LDS), W into r (par:
+  // s % 2)
+  auto group = [&](RawStage& r, int s, auto ab, auto par) {
     const bool live = s < nstages;
     const __amdgpu_buffer_rsrc_t ars = live ? a_rs : zero_rs;
     const __amdgpu_buffer_rsrc_t wrs = live ? w_rs : zero_rs;
@@ -923,9 +934,19 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wrs, wa_off, s * 32, 0));
       r.w[0] = v[0];
       r.w[1] = v[1];
-      r.sw8[0] = __builtin_amdgcn_raw_buffer_load_b8(srs, wsa_off, s * 4, 0);
-      r.w[2] = __builtin_amdgcn_raw_buffer_load_b32(wrs, w_off[2], s * 32, 0);
-      r.sw8[2] = __builtin_amdgcn_raw_buffer_load_b8(srs, ws_off[2], s * 4, 0);
+      if constexpr (decltype(par)::value == 0) {
+        // the scales of stages s and s + 1 (8 bytes of the row); when s is
+        // the last stage (an odd stage count, split K only: K / 64 is even),
+        // those of s - 1 and s, so that the load stays inside the row (the
+        // pair descriptor starts one stage before s0 when s0 > 0)
+        const int so = (s + 1 == nstages && (s > 0 || s0 > 0) ? s - 1 : s) * 4 + sp_b4;
+        const __amdgpu_buffer_rsrc_t prs = live ? wsp_rs : zero_rs;
+        r.spa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(prs, wsa_off, so, 0));
+        r.w[2] = __builtin_amdgcn_raw_buffer_load_b32(wrs, w_off[2], s * 32, 0);
+        r.spb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(prs, wsb_off, so, 0));
+      } else {
+        r.w[2] = __builtin_amdgcn_raw_buffer_load_b32(wrs, w_off[2], s * 32, 0);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < kWP; ++j) {
@@ -939,10 +960,10 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     }
   };
 
-  // staging of one raw stage in three parts (part p: W piece p and, for the
-  // parity export, A pieces of part p), so that it can be interleaved with
-  // the matrix instructions of the previous stage
-  auto store_part = [&](uint8_t* Ta, uint8_t* Tw, const RawStage& r, int p) {
+  // staging of one raw stage q (par: q % 2) in three parts (part p: W piece p
+  // and, for the parity export, A pieces of part p), so that it can be
+  // interleaved with the matrix instructions of the previous stage
+  auto store_part = [&](uint8_t* Ta, uint8_t* Tw, const RawStage& r, int p, auto par, int q) {
     if constexpr (PARTIALS) {
       // unit scales; nvfp4 doubles the E2M1 codes so that they are integers
       const _Float16 one = (_Float16)(PREC == kInt4 ? 1.0f : 2.0f);
@@ -956,7 +977,19 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     }
     if constexpr (kW8) {
       // pieces 0 and 1: columns 16c .. 16c+7 and 16c+8 .. 16c+15 of row tid/4
-      const _Float16 sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.sw8[p < 2 ? 0 : 2], 0);
+      // (scale byte c of the row's stage), piece 2 as the other paths
+      // (scale byte c / 2)
+      const int sh = 8 * (p < 2 ? la_c : (lc >> 1));
+      uint32_t sb;
+      if constexpr (decltype(par)::value == 0) {
+        const u32x2 sp = p < 2 ? r.spa : r.spb;
+        sb = ((q + 1 == nstages && (q > 0 || s0 > 0) ? sp[1] : sp[0]) >> sh) & 0xFFu;
+        if (p == 0) nsc_a = (sp[1] >> sh) & 0xFFu;
+        if (p == 2) nsc_b = (sp[1] >> sh) & 0xFFu;
+      } else {
+        sb = p < 2 ? nsc_a : nsc_b;
+      }
+      const _Float16 sc = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sb, 0);
       uint8_t* dst = p < 2 ? Tw + la_r * kWRow + la_c * 32 + p * 16 : Tw + (lr + 2 * kRP) * kWRow + lc * 16;
       *(f16x8*)dst = e2m1x8_to_f16_scaled(r.w[p], sc);
     } else {
@@ -1033,8 +1066,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
 #pragma unroll
         for (int j = 0; j < kJB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[ks & 1][i], bop[ks & 1][j], acc[i][j], 0, 0, 0);
-      if (ks < 3) store_part(Na, Nw, r, ks);
-      if (ks == 3) group(r, s + 3, IC<p>{});
+      if (ks < 3) store_part(Na, Nw, r, ks, IC<(p + 1) % 2>{}, s + 1);
+      if (ks == 3) group(r, s + 3, IC<p>{}, IC<(p + 1) % 2>{});
       if constexpr (!PARTIALS) {
         // order: LDS reads of the next operands, then the products
         // interleaved with the staging arithmetic, then the staging write
@@ -1063,11 +1096,11 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   // loop is unrolled by two so that every register array index is a
   // compile-time constant (a runtime index would move the array to scratch).
   RawStage r0, r1;
-  group(r0, 0, IC<0>{});
-  group(r1, 1, IC<1>{});
+  group(r0, 0, IC<0>{}, IC<0>{});
+  group(r1, 1, IC<1>{}, IC<1>{});
 #pragma unroll
-  for (int p = 0; p < 3; ++p) store_part(lds_a0, lds_w0, r0, p);
-  group(r0, 2, IC<2>{});
+  for (int p = 0; p < 3; ++p) store_part(lds_a0, lds_w0, r0, p, IC<0>{}, 0);
+  group(r0, 2, IC<2>{}, IC<0>{});
   stage_barrier();  // (each wave has its stage-0 A loads: they precede the W loads it staged)
   rd(lds_a0, lds_w0, 0, 0);
   // Six stages per iteration (the A ring of three times the two raw register

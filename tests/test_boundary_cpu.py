@@ -158,12 +158,14 @@ def test_split_rule():
     assert ksplit(64, 64, 576) == 2               # 9 stages
     assert ksplit(64, 64, 1152) == 3              # 18 stages
     assert ksplit(256, 3072, 960) == 3            # 15 stages: 15 // 5 = 3 splits of 5
+    assert ksplit(64, 128, 3200) == 8             # 50 stages: 7 splits of 7, the last of 1
     # int4 stages are 128 values of K
     assert ksplit(512, 3072, 3072, "int4") == 4   # 24 stages: about five per split
     assert ksplit(512, 3072, 6144, "int4") == 8   # 48 stages
     assert ksplit(300, 320, 512, "int4") == 2     # 4 stages
     assert ksplit(64, 64, 256, "int4") == 1       # 2 stages
     assert ksplit(64, 64, 1152, "int4") == 2      # 9 stages
+    assert ksplit(64, 128, 3200, "int4") == 5     # 25 stages: 5 splits of 5
 
 
 def test_workspace_size(L):

@@ -348,13 +348,15 @@ def test_linear_k_extremes(precision, M, K, N, rank):
 
 @pytest.mark.parametrize("precision", ["int4", "nvfp4"])
 @pytest.mark.parametrize("M,K,N,rank", [(512, 3072, 3072, 32), (64, 640, 128, 16), (200, 1152, 576, 128),
-                                        (256, 6144, 384, 32), (2048, 3072, 3072, 32)])
+                                        (256, 6144, 384, 32), (2048, 3072, 3072, 32), (64, 3200, 128, 16)])
 def test_linear_split_k(precision, M, K, N, rank):
     # few output tiles: the product is split along K (int4 / nvfp4: 4 / 8
     # splits of 6 stages; 2 splits of 3 + 2 / of 5; 2 splits of 5 + 4 / 3 of
-    # 6; 8 splits of 6 / 8 of 12; at 128 tiles 2 splits of 12 / 24) and the
-    # fp32 partials summed in order; the low-rank term enters in split 0, the
-    # bias in the sum
+    # 6; 8 splits of 6 / 8 of 12; at 128 tiles 2 splits of 12 / 24; 5 splits
+    # of 5 / 7 splits of 7 + 1) and the fp32 partials summed in order; the
+    # low-rank term enters in split 0, the bias in the sum.  Odd stage counts
+    # per split reach the loaders' last pair of stages, whose second stage
+    # does not exist (the W scales of two stages share a load)
     rng = np.random.default_rng(M + K + N)
     x = S.activations(M, K, round(0.01 * K), rng)
     lay = prepared(x, S.weight(N, K, 0.02, rng, spike_rank=4), S.bias(N, rng), precision, rank, smooth="calibrated")
