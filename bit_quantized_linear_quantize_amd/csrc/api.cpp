@@ -140,12 +140,12 @@ int k1_slices(int64_t M, int64_t K) {
 // Base workspace of one layer (each part 256-byte aligned):
 //   act_op     the product operand [M, K]: int4 codes as fp8 E4M3 bytes,
 //              nvfp4 the dequantized values as fp16
-//   act_scale  int4 only: f32 [M, K/64], the group scales
+//   act_scale  int4 only: bf16 [M, K/64], the group scales
 //   lora_act   f32 [M, rank]
 //   lora_part  f32 [S, M, rank] when kernel 1 splits K (S = k1_slices > 1)
 size_t workspace_bytes(int64_t M, int64_t K, int precision, int rank) {
   size_t b = round_up(size_t(M) * size_t(K) * (precision == SVDQ_INT4 ? 1 : 2));
-  if (precision == SVDQ_INT4) b += round_up(size_t(M) * size_t(K / 64) * 4);
+  if (precision == SVDQ_INT4) b += round_up(size_t(M) * size_t(K / 64) * 2);
   b += round_up(size_t(M) * size_t(rank) * 4);
   const int S = k1_slices(M, K);
   if (S > 1) b += round_up(size_t(S) * size_t(M) * size_t(rank) * 4);
@@ -252,7 +252,7 @@ int launch_status(hipError_t e, const char* what) {
 
 struct Carve {
   uint8_t* act_op;    // int4: E4M3 bytes [M, K]; nvfp4: f16 [M, K]
-  float* act_scale;   // int4: f32 [M, K/64]; else null
+  uint16_t* act_scale;  // int4: bf16 [M, K/64]; else null
   float* lora_act;    // f32 [M, rank]
   float* lora_part;   // f32 [k1_slices, M, rank] (when kernel 1 splits K)
 };
@@ -263,8 +263,8 @@ Carve carve(void* workspace, int64_t M, int64_t K, int precision, int rank) {
   c.act_op = p;
   p += round_up(size_t(M) * size_t(K) * (precision == SVDQ_INT4 ? 1 : 2));
   if (precision == SVDQ_INT4) {
-    c.act_scale = reinterpret_cast<float*>(p);
-    p += round_up(size_t(M) * size_t(K / 64) * 4);
+    c.act_scale = reinterpret_cast<uint16_t*>(p);
+    p += round_up(size_t(M) * size_t(K / 64) * 2);
   }
   c.lora_act = reinterpret_cast<float*>(p);
   c.lora_part = c.lora_act + round_up(size_t(M) * size_t(rank) * 4) / 4;
@@ -275,8 +275,9 @@ Carve carve(void* workspace, int64_t M, int64_t K, int precision, int rank) {
 int launch_quantize(const void* x, int64_t M, int64_t K, const void* smooth, const void* lora_down,
                     int precision, int rank, void* workspace, hipStream_t s) {
   const Carve c = carve(workspace, M, K, precision, rank);
-  svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, c.lora_act, c.act_op, c.act_scale,
-                        M, K, precision, rank};
+  svdq::QuantActArgs qa{x, smooth, lora_down, nullptr, nullptr, c.lora_act, c.act_op,
+                        reinterpret_cast<float*>(c.act_scale), M, K, precision, rank};
+  qa.scale_bf16 = true;
   qa.k_slices = k1_slices(M, K);
   qa.lora_part = c.lora_part;
   int rc = launch_status(svdq::launch_quantize_act(qa, s), "quantize_act_lora_down launch");

@@ -21,7 +21,7 @@
 // express) are applied as acc += P * (s_x s_w), the 32 x 32 scale products
 // (exact in fp32) coming from one bf16 outer-product instruction
 // (v_mfma_f32_32x32x8_bf16) and the accumulation from one FMA per output.
-// The quantize kernel writes A as E4M3 bytes with fp32 group scales; a stage
+// The quantize kernel writes A as E4M3 bytes with bf16 group scales; a stage
 // is 128 values of K (two groups).  The matrix work is half that of the fp16
 // route below, and it runs at a lower power: the fp16 route on int4 data is
 // held back by the clock the chip sustains under full matrix load.
@@ -515,14 +515,15 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
   __shared__ __attribute__((aligned(16))) uint8_t lds_w0[kBN * kWRow];
   __shared__ __attribute__((aligned(16))) uint8_t lds_w1[kBN * kWRow];
   __shared__ float nmu[kBN];    // MLP fusion: 1 / smooth of the next layer for this tile's columns
-  // int4 (fp8 operands): the group scales of the stages in LDS, A per A
-  // buffer [group][row], W per W buffer [group][row]
+  // int4 (fp8 operands): the group scales of the stages in LDS, A per pair
+  // of stages [stage of the pair][row] (the bf16 scales of the row's two
+  // groups in one word), W [stage % 3][group][row]
   constexpr bool kFp8 = PREC == kInt4 && !PARTIALS;
-  // (one object per A buffer, like the A buffers themselves: a read of one
-  // does not wait for the direct-to-LDS loads still filling another)
-  __shared__ __attribute__((aligned(16))) float asc0[kFp8 ? 2 * kBM : 1];
-  __shared__ __attribute__((aligned(16))) float asc1[kFp8 ? 2 * kBM : 1];
-  __shared__ __attribute__((aligned(16))) float asc2[kFp8 ? 2 * kBM : 1];
+  // (one object per pair of stages in flight, as for the A buffers: a read of
+  // one does not wait for the direct-to-LDS loads still filling another)
+  __shared__ __attribute__((aligned(16))) uint32_t asc0[kFp8 ? 2 * kBM : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t asc1[kFp8 ? 2 * kBM : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t asc2[kFp8 ? 2 * kBM : 1];
   // (W: bf16 bits of s_w / 2, the operand of the scale-product instruction,
   // [stage % 3][group][row])
   __shared__ __attribute__((aligned(16))) uint16_t wsc[kFp8 ? 3 * 2 * kBN : 1];
@@ -631,7 +632,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     // A stage s (128 values of K, two groups of 64) comes straight from
     // memory to LDS as fp8 codes in the same swizzled 16-byte chunks as the
     // fp16 operand of the other path (8 chunks per 128-byte row); its group
-    // scales (fp32 [M, K/64]) likewise, into asc0-2.  W stage s is staged
+    // scales (bf16 [M, K/64]) likewise, two stages per load, into asc0-2.
+    // W stage s is staged
     // through registers: int4 nibbles -> fp8 bytes (rows of kWRow bytes),
     // its bf16 group scales halved -> wsc.  Per group, each 32 x 32 tile is
     // one v_mfma_f32_32x32x64_f8f6f4 of exact integer sums P (|P| <= 64 * 49),
@@ -641,8 +643,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     const int G = K >> 6;
     const __amdgpu_buffer_rsrc_t a_rs = make_rsrc((const uint8_t*)args.act + (size_t)m0 * K + s0 * 128,
                                                   (size_t)(M - m0) * K - s0 * 128);
-    const __amdgpu_buffer_rsrc_t as_rs = make_rsrc((const uint8_t*)args.act_scale + ((size_t)m0 * G + 2 * s0) * 4,
-                                                   ((size_t)(M - m0) * G - 2 * s0) * 4);
+    const __amdgpu_buffer_rsrc_t as_rs = make_rsrc((const uint8_t*)args.act_scale + ((size_t)m0 * G + 2 * s0) * 2,
+                                                   ((size_t)(M - m0) * G - 2 * s0) * 2);
     const int w_base = kQk ? 0 : n0;
     const __amdgpu_buffer_rsrc_t w_rs = make_rsrc((const uint8_t*)args.w_codes + (size_t)w_base * K2 + s0 * 64,
                                                   (size_t)(N - w_base) * K2 - s0 * 64);
@@ -670,10 +672,12 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       const int row = u >> 3;
       dma_off[d] = row * K + a_pos(row, u & 7) * 16;
     }
-    // A scales: waves 0-3 load group 0 of the stage, waves 4-7 group 1, one
-    // row per lane
-    const int sc_row = (wave & 3) * 64 + lane, sc_g = wave >> 2;
-    const int sc_off = sc_row * G * 4 + sc_g * 4;
+    // A scales, one load per pair of stages (s even): waves 0-3 load the
+    // two groups of stage s, waves 4-7 those of stage s + 1, one row per lane
+    // (4 bytes).  (At an odd stage count the last pair's second stage is the
+    // next row's first, never used, or beyond the descriptor, zero.)
+    const int sc_row = (wave & 3) * 64 + lane, sc_st = wave >> 2;
+    const int sc_off = sc_row * G * 2 + sc_st * 4;
 
     auto abuf = [&](auto c) -> uint8_t* {
       constexpr int i = decltype(c)::value % kAStages;
@@ -685,32 +689,36 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
       if constexpr (decltype(c)::value % 2 == 0) return lds_w0;
       else return lds_w1;
     };
-    auto ascbuf = [&](auto c) -> float* {
-      constexpr int i = decltype(c)::value % kAStages;
+    // the A scale object of stage s (st = s % 6): pair st / 2
+    auto ascbuf = [&](auto st) -> uint32_t* {
+      constexpr int i = decltype(st)::value % 6 / 2;
       if constexpr (i == 0) return asc0;
       else if constexpr (i == 1) return asc1;
       else return asc2;
     };
-    // loads of stage s: A and its scales into A buffer ab (direct to LDS),
-    // then W into r (the W scales of stages s and s + 1 if s is even, par 0)
-    auto group = [&](RawStage8& r, int s, auto ab, auto par) {
+    // loads of stage s (st = s % 6): A into A buffer s % 3 (direct to LDS),
+    // with the A scales of stages s and s + 1 if s is even, then W into r
+    // (with the W scales of stages s and s + 1 if s is even)
+    auto group = [&](RawStage8& r, int s, auto st) {
+      constexpr int q = decltype(st)::value;
       const bool live = s < nstages;
-      uint8_t* dst = abuf(ab) + wave * (kADma * 64 * 16);
+      uint8_t* dst = abuf(st) + wave * (kADma * 64 * 16);
 #pragma unroll
       for (int d = 0; d < kADma; ++d)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? a_rs : zero_rs,
                                                  (__attribute__((address_space(3))) void*)(dst + d * 1024), 16,
                                                  dma_off[d], s * 128, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          live ? as_rs : zero_rs,
-          (__attribute__((address_space(3))) void*)(ascbuf(ab) + sc_g * kBM + (wave & 3) * 64), 4, sc_off, s * 8,
-          0, 0);
+      if constexpr (q % 2 == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            live ? as_rs : zero_rs,
+            (__attribute__((address_space(3))) void*)(ascbuf(st) + sc_st * kBM + (wave & 3) * 64), 4, sc_off,
+            s * 4, 0, 0);
       // the W loads of the stage stay behind its A loads: a wave that has
       // waited for its W registers has also received its A stage
       __builtin_amdgcn_sched_barrier(0);
       r.wa = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(live ? w_rs : zero_rs, wa_off, s * 64, 0));
       r.wb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(live ? w_rs : zero_rs, wb_off, s * 64, 0));
-      if constexpr (decltype(par)::value == 0)
+      if constexpr (q % 2 == 0)
         r.sw = __builtin_amdgcn_raw_buffer_load_b32(live ? ws_rs : zero_rs, ws_off, s * 4, 0);
     };
     // staging of third p of raw stage st (mod 6) into W buffer Tw (the two
@@ -752,8 +760,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
           const u32x4 lo = *(const u32x4*)(Ta + row * kARow + a_pos(row, 4 * gi + 2 * h) * 16);
           const u32x4 hi = *(const u32x4*)(Ta + row * kARow + a_pos(row, 4 * gi + 2 * h + 1) * 16);
           aop[i] = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-          // the upper half of the fp32 scale: its bf16 bits (s_x is a bf16 value)
-          as16[i] = ((const uint16_t*)(ascbuf(IC<p>{}) + gi * kBM + row))[1];
+          // the bf16 scale of group gi of the row
+          as16[i] = ((const uint16_t*)(ascbuf(IC<p>{}) + (p % 2) * kBM + row))[gi];
         }
 #pragma unroll
         for (int j = 0; j < kJB; ++j) {
@@ -788,7 +796,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
         }
       }
       stage_barrier();
-      group(r, s + 3, IC<p>{}, IC<(p + 3) % 2>{});
+      group(r, s + 3, IC<(p + 3) % 6>{});
     };
 
     // Prologue.  The bias (except for split-K partials) and, for ranks up to
@@ -815,8 +823,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     }
     __builtin_amdgcn_sched_barrier(0);
     RawStage8 r0, r1;
-    group(r0, 0, IC<0>{}, IC<0>{});
-    group(r1, 1, IC<1>{}, IC<1>{});
+    group(r0, 0, IC<0>{});
+    group(r1, 1, IC<1>{});
     if constexpr (!kSplit) {
 #pragma unroll
       for (int i = 0; i < kIB; ++i)
@@ -835,7 +843,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     }
 #pragma unroll
     for (int q = 0; q < 3; ++q) store_part(lds_w0, IC<0>{}, r0, q);
-    group(r0, 2, IC<2>{}, IC<0>{});
+    group(r0, 2, IC<2>{});
     stage_barrier();  // (each wave has its stage-0 A loads: they precede the W loads it staged)
     for (int s = 0; s < nstages; s += 6) {
       compute(IC<0>{}, s, r1);

@@ -17,7 +17,8 @@ struct QuantActArgs {
   void* scales;           // parity export: bf16 [M, K/64] | u8 [M, K/16]; else null
   float* lora_act;        // f32 [M, rank]
   void* act_op;           // linear only: the product operand [M, K] (see below), else null
-  float* act_scale;       // linear int4 only: f32 [M, K/64] group scales s
+  float* act_scale;       // linear int4 only: [M, K/64] group scales s, f32 (the
+                          // operand export) or bf16 bits (scale_bf16, the linear)
   int64_t M, K;
   int precision, rank;
   // linear only: K slices (1: one workgroup per 16 rows and all of K; S > 1:
@@ -25,16 +26,19 @@ struct QuantActArgs {
   // fp32 partials lora_part [S, M, rank] for a second kernel to add in order)
   int k_slices = 1;
   float* lora_part = nullptr;
+  // linear int4: write the group scales as their bf16 bits (they are bf16
+  // values), the form the product kernel loads
+  bool scale_bf16 = false;
 };
 
 // The product operand of the linear.  int4: the codes q (|q| <= 7) as fp8
 // E4M3 bytes (every such integer is exact), with the group scales in
-// act_scale, applied after each group's product; nvfp4: e2m1 * dec(s8) as
-// fp16 (always exact).
+// act_scale (bf16 bits), applied after each group's product; nvfp4:
+// e2m1 * dec(s8) as fp16 (always exact).
 
 struct GemmArgs {
   const void* act;          // linear: act_op above; partials: nibbles [M, K/2]
-  const float* act_scale;   // linear int4: f32 [M, K/64]; else null
+  const uint16_t* act_scale;  // linear int4: bf16 [M, K/64]; else null
   const float* lora_act;    // f32 [M, rank]
   const void* w_codes;      // u8 [N, K/2]
   const void* w_scales;     // bf16 [N, K/64] | u8 [N, K/16]

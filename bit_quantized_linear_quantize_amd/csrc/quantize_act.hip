@@ -192,7 +192,10 @@ __global__ __launch_bounds__(64 * K1Shape<RB>::waves) void quantize_act_lora_dow
               // (a zero group gets codes 0, as in the packed export)
               const u32x4 z = {0u, 0u, 0u, 0u};
               *(u32x4*)((uint8_t*)args.act_op + (size_t)row * K + k0) = sbits == 0u ? z : int4_q8(xh, inv);
-              if (q == 0) args.act_scale[(size_t)row * (K >> 6) + c] = sv;
+              if (q == 0) {
+                if (args.scale_bf16) ((uint16_t*)args.act_scale)[(size_t)row * (K >> 6) + c] = (uint16_t)sbits;
+                else args.act_scale[(size_t)row * (K >> 6) + c] = sv;
+              }
             }
           } else {
             int4_codes(xh, inv, sbits, cw0, cw1);

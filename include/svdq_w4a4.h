@@ -54,7 +54,7 @@ enum svdq_status {
 
 /* Bytes of scratch svdq_w4a4_linear needs, each part 256-byte aligned: the
  * operand of the product kernel [M, K] (int4: the codes as fp8 E4M3 bytes,
- * followed by the fp32 group scales [M, K/64]; nvfp4: the dequantized
+ * followed by the group scales [M, K/64] as bf16; nvfp4: the dequantized
  * activations e2m1 * dec(s8) as fp16, which is exact); the low-rank
  * activations fp32 [M, rank]; when the 16-row blocks of x would fill at
  * most half of the GPU, the first kernel's low-rank partials fp32 [S, M,
@@ -129,9 +129,10 @@ int svdq_w4a4_gemm(const void* workspace, size_t workspace_bytes, int64_t M, int
  * held until the process ends.  The call allocates and frees nothing.
  *   - A call whose scratch need (svdq_w4a4_workspace_bytes of its arguments)
  *     exceeds SVDQ_NOALLOC_SCRATCH_BYTES returns SVDQ_EWORKSPACE and writes
- *     nothing; with K = 3072 that is M up to about 10400 tokens for int4
- *     rank 32 (M = 4096 needs 25.7 MB; M = 512, whose product is split along
- *     K, 26.9 MB).
+ *     nothing; with K = N = 3072 and rank 32 that is M up to 20360 tokens
+ *     for int4 and 10699 for nvfp4 (M = 4096 needs 13.5 MB for int4 and
+ *     25.7 MB for nvfp4; M = 512 int4, whose product is split along K,
+ *     27.4 MB).
  *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
  *     time on one GPU (different streams, or host threads) race and give
  *     undefined results; calls on one stream are ordered and safe.  No part
@@ -364,7 +365,8 @@ int svdq_w4a4_quantize_act(const void* x, int64_t M, int64_t K, const void* smoo
  *                  0x80, -0); nvfp4: IEEE binary16 [M, K], e2m1 * dec(s8)
  *                  (always exact)
  *   scale_out      int4: fp32 [M, K/64], the group scales s (the bf16 values,
- *                  0 for a zero group); must be NULL for nvfp4
+ *                  0 for a zero group; the linear keeps their bf16 bits in
+ *                  its workspace); must be NULL for nvfp4
  *   lora_act_out   fp32 [M, rank] (NULL iff rank == 0)
  * Other arguments and rules as for svdq_w4a4_quantize_act; no output may
  * overlap x or another output. */

@@ -171,13 +171,13 @@ def test_split_rule():
 def test_workspace_size(L):
     M, K, N = 300, 512, 320
     rnd = lambda v: (v + 255) // 256 * 256
-    # the product operand (int4: fp8 codes [M, K] and fp32 group scales
+    # the product operand (int4: fp8 codes [M, K] and bf16 group scales
     # [M, K/64]; nvfp4: fp16 [M, K]); then lora_act fp32 [M, 32]; then, with
     # kernel 1 split along K, its low-rank slice partials fp32 [S, M, 32];
     # then the split-K partials fp32 [ksplit, M, N]
     assert k1_slices(M, K) == 8 and k1_slices(4096, 3072) == 1 and k1_slices(2048, 3072) == 2
     assert k1_slices(512, 3072) == 8 and k1_slices(64, 384) == 2 and k1_slices(1, 128) == 2
-    want = {0: rnd(M * K) + rnd(4 * M * (K // 64)) + rnd(M * 32 * 4) + lora_part_bytes(M, K, 32) +
+    want = {0: rnd(M * K) + rnd(2 * M * (K // 64)) + rnd(M * 32 * 4) + lora_part_bytes(M, K, 32) +
             split_bytes(M, N, K, "int4"),
             1: rnd(2 * M * K) + rnd(M * 32 * 4) + lora_part_bytes(M, K, 32) + split_bytes(M, N, K)}
     assert split_bytes(M, N, K) > 0 and split_bytes(M, N, K, "int4") > 0
@@ -265,10 +265,10 @@ def test_mlp_rules(L):
     B = ctypes.byref
     need = L.svdq_w4a4_mlp_workspace_bytes(M, B(up), B(down))
     rnd = lambda v: (v + 255) // 256 * 256
-    # the up layer's operand (int4: fp8 codes and fp32 group scales) and
+    # the up layer's operand (int4: fp8 codes and bf16 group scales) and
     # lora_act, the down layer's linear workspace, then the down layer's
     # low-rank partials per 192-column tile of the up projection
-    assert need == (rnd(M * K) + rnd(4 * M * (K // 64)) + rnd(4 * M * 32) + lora_part_bytes(M, K, 32)) + \
+    assert need == (rnd(M * K) + rnd(2 * M * (K // 64)) + rnd(4 * M * 32) + lora_part_bytes(M, K, 32)) + \
         (rnd(2 * M * H) + rnd(4 * M * 32) + lora_part_bytes(M, H, 32) + split_bytes(M, N, H)) + \
         rnd(4 * ((H + 191) // 192) * M * 32)
 
@@ -279,7 +279,7 @@ def test_mlp_rules(L):
     assert call() == OK
     up_n = _layer(0x1_0000_0000, K, H, precision=1)  # an nvfp4 up layer keeps an fp16 operand
     need_n = L.svdq_w4a4_mlp_workspace_bytes(M, B(up_n), B(down))
-    assert need_n == need + rnd(2 * M * K) - rnd(M * K) - rnd(4 * M * (K // 64))
+    assert need_n == need + rnd(2 * M * K) - rnd(M * K) - rnd(2 * M * (K // 64))
     assert call(up=up_n, wsb=need_n) == OK and call(up=up_n) == EWS
     assert call(down=_layer(0x2_0000_0000, H, N, precision=0)) == EUNSUP  # int4 hidden activations
     assert L.svdq_w4a4_mlp_workspace_bytes(M, B(up), B(_layer(0x2_0000_0000, H, N, precision=0))) == 0

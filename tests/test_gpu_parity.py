@@ -366,7 +366,7 @@ def test_linear_split_k(precision, M, K, N, rank):
 
 
 def test_linear_int4_scale_range():
-    # int4 activations enter the product as fp8 codes with fp32 group scales
+    # int4 activations enter the product as fp8 codes with bf16 group scales
     # applied to each group's exact integer sum (the operand itself is checked
     # bit for bit in test_quantize_operand_int4_scale_range).  Rows of each
     # scale class, each class checked on its own.
@@ -448,8 +448,11 @@ def test_linear_kernel1_workspace(precision, M, K, rank):
     assert np.array_equal(w[:opb], op.cpu().numpy().view(np.uint8).reshape(-1)), "operand differs from the export"
     off = rnd(opb)
     if precision == "int4":
-        scb = M * (K // 64) * 4
-        assert np.array_equal(w[off:off + scb], sc.cpu().numpy().view(np.uint8).reshape(-1)), "group scales differ"
+        # the workspace holds the bf16 bits of the export's fp32 scales (bf16 values)
+        scb = M * (K // 64) * 2
+        sc32 = sc.cpu().numpy().view(np.uint32).reshape(-1)
+        assert np.all(sc32 & 0xFFFF == 0), "export scales are not bf16 values"
+        assert np.array_equal(w[off:off + scb].view(np.uint16), (sc32 >> 16).astype(np.uint16)), "group scales differ"
         off += rnd(scb)
     if rank:
         la = w[off:off + M * rank * 4].view(np.float32).reshape(M, rank).astype(np.float64)

@@ -28,7 +28,7 @@ def bits(t):
 
 def test_noalloc_matches_linear_on_consecutive_calls():
     # largest first: config 1 (25.7 MB of scratch), then one GPU's token
-    # share of it (M = 512: the product split along K, 26.9 MB), then a
+    # share of it (M = 512: the product split along K, 27.4 MB), then a
     # small ragged call; each must equal the workspace entry point bit for bit
     cases = [(4096, 3072, 3072, "int4", 32), (512, 3072, 3072, "int4", 32), (300, 512, 320, "nvfp4", 16),
              (37, 256, 192, "int4", 0)]
@@ -45,7 +45,7 @@ def test_noalloc_matches_linear_on_consecutive_calls():
 
 
 def test_noalloc_rejects_oversize_without_writing():
-    # M = 16384, K = 3072: 100 MB of scratch, more than the static 64 MiB
+    # M = 16384, K = 3072, N = 64 (split K): 69.7 MB of scratch, more than the static 64 MiB
     M, K, N = 16384, 3072, 64
     layer, x = layer_and_x(M, K, N, "int4", 16, seed=7)
     assert layer.workspace_bytes(M) > bq.NOALLOC_SCRATCH_BYTES
