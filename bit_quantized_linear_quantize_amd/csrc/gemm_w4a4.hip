@@ -1246,30 +1246,43 @@ hipError_t launch_gelu_table_copy(uint16_t* out, hipStream_t stream) {
 }
 
 // Split K: out[m, n] = bf16(sum_j partial[j, m, n] + bias[n]), the splits
-// added in order (deterministic); 8 columns per thread (N % 64 == 0).
+// added in order (deterministic); 8 columns per thread (N % 64 == 0).  The
+// loads of all splits (at most kMaxSplit) are issued before the additions.
+constexpr int kMaxSplit = 8;
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t M,
                                                             int64_t N, const uint16_t* __restrict__ bias,
                                                             uint16_t* __restrict__ out) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;  // first element
   if (i >= M * N) return;
   const int64_t n = i % N;
+  f32x4 a[kMaxSplit], b[kMaxSplit];
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; ++j) {
+    if (j < ksplit) {
+      const f32x4* p = (const f32x4*)(partial + (size_t)j * M * N + i);
+      a[j] = __builtin_nontemporal_load(p);
+      b[j] = __builtin_nontemporal_load(p + 1);
+    }
+  }
+  const u32x4 bb = bias ? *(const u32x4*)(bias + n) : u32x4{0u, 0u, 0u, 0u};
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-  for (int j = 0; j < ksplit; ++j) {
-    const f32x4* p = (const f32x4*)(partial + (size_t)j * M * N + i);
-    const f32x4 a = p[0], b = p[1];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      acc[c] += a[c];
-      acc[4 + c] += b[c];
+  for (int j = 0; j < kMaxSplit; ++j) {
+    if (j < ksplit) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[c] += a[j][c];
+        acc[4 + c] += b[j][c];
+      }
     }
   }
   u32x4 o;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const float b0 = bias ? bf16_bits_to_f32(bias[n + 2 * c]) : 0.f;
-    const float b1 = bias ? bf16_bits_to_f32(bias[n + 2 * c + 1]) : 0.f;
+    const float b0 = bf16_bits_to_f32((uint16_t)(bb[c] & 0xFFFFu));
+    const float b1 = bf16_bits_to_f32((uint16_t)(bb[c] >> 16));
     o[c] = f32_to_bf16_bits(acc[2 * c] + b0) | (f32_to_bf16_bits(acc[2 * c + 1] + b1) << 16);
   }
   *(u32x4*)(out + i) = o;
@@ -1313,6 +1326,7 @@ hipError_t launch_tile_partial_sum(const float* part, int tiles, int64_t n, floa
 
 hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N, const void* bias, void* out,
                                 hipStream_t stream) {
+  if (ksplit < 1 || ksplit > kMaxSplit) return hipErrorInvalidValue;
   const int64_t threads = M * N / 8;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, partial,
                      ksplit, M, N, (const uint16_t*)bias, (uint16_t*)out);
