@@ -660,8 +660,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     // per lane, one load per wave and pair of stages (even s): lanes 0-23
     // stage s, lanes 24-47 stage s + 1, lanes 48-63 repeat lanes 0-15.  (At
     // an odd stage count the last pair's second half lies past the last
-    // stage: the next row's scales, never used, or beyond the descriptor,
-    // zero.)
+    // stage: the next split's or the next row's scales, never used, or
+    // beyond the descriptor, zero.)
     const int srow = wave * (kBN / kWaves) + lane % (kBN / kWaves);
     const int s_next = (lane >= kBN / kWaves && lane < 2 * (kBN / kWaves)) ? 1 : 0;
     const int ws_off = (kQk ? pcol(srow) : srow) * G * 2 + s_next * 4;
@@ -675,7 +675,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_lora_up_kernel(GemmArgs ar
     // A scales, one load per pair of stages (s even): waves 0-3 load the
     // two groups of stage s, waves 4-7 those of stage s + 1, one row per lane
     // (4 bytes).  (At an odd stage count the last pair's second stage is the
-    // next row's first, never used, or beyond the descriptor, zero.)
+    // next split's first or the next row's first, never used, or beyond the
+    // descriptor, zero.)
     const int sc_row = (wave & 3) * 64 + lane, sc_st = wave >> 2;
     const int sc_off = sc_row * G * 2 + sc_st * 4;
 
